@@ -1,0 +1,135 @@
+"""GPU parity of the W4A4 GEMM + epilogue against the oracle.
+
+Given identical codes and scales: the INT32 sums are bit-exact, and the
+outputs are bit-exact under the epilogue order fp32(acc) * s_a * s_w + bias
+(each operation rounded separately).  With a low-rank term the GPU sums the
+rank terms in fp32 while the oracle sums them in fp64, so the bound is one
+ulp of the output dtype plus the fp32 rounding of that short sum."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import bits, dev, host, need_gpu, ulp_distance
+
+pytestmark = pytest.mark.gpu
+
+import bit_quantized_linear_rotate_amd as w4  # noqa: E402
+
+
+def _operands(M, K, N, odt, sw_dt, group=0, bias=True, seed=0):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    scales = rng.uniform(0.01, 0.5, size=M).astype(np.float32)
+    wp = workloads.random_packed_weights(rng, N, K)
+    if group:
+        sw = workloads.f32_to_storage(rng.uniform(0.005, 0.02, size=(K // group, N)), sw_dt)
+    else:
+        sw = workloads.f32_to_storage(rng.uniform(0.005, 0.02, size=N), sw_dt)
+    b = workloads.f32_to_storage(rng.normal(0, 0.1, size=N), odt) if bias else None
+    return codes, scales, wp, sw, b
+
+
+SHAPES = [  # (M, K, N): tiles of 128 x 128 x 64 plus ragged tails
+    (1, 256, 256), (32, 3840, 384), (130, 640, 200), (257, 1024, 129), (64, 96, 64),
+    (200, 2048, 300), (5, 160, 17), (128, 64, 128),
+]
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+@pytest.mark.parametrize("odt", ["f32", "bf16", "f16"])
+def test_acc_and_output_bit_exact(M, K, N, odt):
+    need_gpu()
+    codes, sa, wp, sw, b = _operands(M, K, N, odt, odt, seed=M + K + N)
+    out, acc = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, odt), bias=dev(b, odt),
+                                       out_dtype={"f32": torch.float32, "f16": torch.float16,
+                                                  "bf16": torch.bfloat16}[odt], return_acc=True)
+    oacc = oracle.gemm(codes, oracle.unpack(wp, K))
+    assert np.array_equal(host(acc).astype(np.int64), oacc)
+    oout = oracle.epilogue(oacc, sa, sw, odt, odt, bias=b, bias_dtype=odt)
+    assert np.array_equal(bits(host(out)), bits(oout))
+
+
+@pytest.mark.parametrize("sw_dt", ["f32", "bf16", "f16"])
+def test_no_bias_and_mixed_dtypes(sw_dt):
+    need_gpu()
+    M, K, N = 70, 512, 96
+    codes, sa, wp, sw, _ = _operands(M, K, N, "bf16", sw_dt, bias=False, seed=3)
+    out = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, sw_dt),
+                                  out_dtype=torch.float32)
+    oout = oracle.epilogue(oracle.gemm(codes, oracle.unpack(wp, K)), sa, sw, sw_dt, "f32")
+    assert np.array_equal(bits(host(out)), bits(oout))
+
+
+@pytest.mark.parametrize("M,K,N", [(33, 1024, 130), (128, 4096, 256)])
+def test_forced_k_chunks_are_exact(M, K, N):
+    need_gpu()
+    codes, sa, wp, sw, b = _operands(M, K, N, "bf16", "bf16", seed=11)
+    ref, racc = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, "bf16"),
+                                        bias=dev(b, "bf16"), return_acc=True)
+    for kc in (64, 192, 1024):
+        out, acc = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, "bf16"),
+                                           bias=dev(b, "bf16"), return_acc=True, k_chunk=kc)
+        assert torch.equal(acc, racc)
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_extreme_codes_int32_range():
+    need_gpu()
+    M, N, K = 16, 16, 16384
+    codes = np.full((M, K), 7, dtype=np.int8)
+    codes[1::2] = -7
+    wq = np.full((N, K), -8, dtype=np.int8)
+    wq[::3] = 7
+    wp = oracle.pack(wq)
+    sa = np.ones(M, np.float32)
+    sw = np.ones(N, np.float32)
+    out, acc = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw),
+                                       out_dtype=torch.float32, return_acc=True)
+    oacc = oracle.gemm(codes, wq)
+    assert np.array_equal(host(acc).astype(np.int64), oacc)
+    assert np.abs(oacc).max() == 56 * K
+
+
+@pytest.mark.parametrize("M,K,N", [(40, 1024, 96), (129, 2048, 200)])
+def test_group_scales_and_lowrank(M, K, N):
+    need_gpu()
+    codes, sa, wp, sw, _ = _operands(M, K, N, "bf16", "bf16", group=64, bias=False, seed=5)
+    rng = np.random.default_rng(6)
+    R = 32
+    L = rng.standard_normal((M, R)).astype(np.float32)
+    up = workloads.f32_to_storage(rng.normal(0, 0.1, size=(N, R)), "bf16")
+    parts = oracle.gemm(codes, oracle.unpack(wp, K), group=64)
+    # without the low-rank term: bit-exact
+    out = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, "bf16"), w_scale_group=64,
+                                  out_dtype=torch.bfloat16)
+    oout = oracle.epilogue(parts, sa, sw, "bf16", "bf16", group=64)
+    assert np.array_equal(bits(host(out)), bits(oout))
+    # with it: within one bf16 ulp
+    out = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, "bf16"), w_scale_group=64,
+                                  lora_act=dev(L), proj_up=dev(up, "bf16"), out_dtype=torch.bfloat16)
+    oout = oracle.epilogue(parts, sa, sw, "bf16", "bf16", group=64, L=L, proj_up=up, up_dtype="bf16")
+    assert ulp_distance(host(out), oout, "bf16").max() <= 1
+
+
+def test_lowrank_down_matches_oracle():
+    need_gpu()
+    rng = np.random.default_rng(8)
+    for dt, M, K, R in [("bf16", 37, 2048, 32), ("f16", 16, 512, 16), ("f32", 5, 256, 8)]:
+        x = workloads.f32_to_storage(rng.standard_normal((M, K)), dt)
+        down = workloads.f32_to_storage(rng.standard_normal((K, R)) / np.sqrt(K), dt)
+        L = host(w4.w4a4_lowrank_down(dev(x, dt), dev(down, dt)))
+        Lo = oracle.lowrank_down(x, down, dt)
+        xa = np.abs(oracle.decode(dt, x)) @ np.abs(oracle.decode(dt, down))
+        # recursive fp32 summation bound: |err| <= (K + 2) u sum |x d|, u = 2^-24
+        assert (np.abs(L.astype(np.float64) - Lo) <= (K + 2) * 2.0 ** -24 * xa + 1e-30).all()
+
+
+def test_empty_shapes():
+    need_gpu()
+    z = torch.zeros((0, 64), dtype=torch.int8, device="cuda")
+    out = w4.w4a4_gemm_from_codes(z, torch.zeros(0, device="cuda"),
+                                  torch.zeros((8, 32), dtype=torch.uint8, device="cuda"),
+                                  torch.ones(8, device="cuda"), out_dtype=torch.float32)
+    assert out.shape == (0, 8)
