@@ -62,7 +62,7 @@ def test_no_bias_and_mixed_dtypes(sw_dt):
     assert np.array_equal(bits(host(out)), bits(oout))
 
 
-@pytest.mark.parametrize("M,K,N", [(33, 1024, 130), (128, 4096, 256)])
+@pytest.mark.parametrize("M,K,N", [(33, 1024, 130), (128, 4096, 256), (300, 2048, 260)])
 def test_forced_k_chunks_are_exact(M, K, N):
     need_gpu()
     codes, sa, wp, sw, b = _operands(M, K, N, "bf16", "bf16", seed=11)
@@ -133,3 +133,22 @@ def test_empty_shapes():
                                   torch.zeros((8, 32), dtype=torch.uint8, device="cuda"),
                                   torch.ones(8, device="cuda"), out_dtype=torch.float32)
     assert out.shape == (0, 8)
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 2048, 520), (513, 1024, 257), (256, 3840, 256),
+                                   (1000, 640, 1000)])
+@pytest.mark.parametrize("odt", ["f32", "bf16", "f16"])
+def test_output_bit_exact_without_acc_export(M, K, N, odt):
+    # the large-tile kernels run only when the INT32 sums are not exported
+    need_gpu()
+    codes, sa, wp, sw, b = _operands(M, K, N, odt, odt, seed=M * 3 + N)
+    out = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, odt), bias=dev(b, odt),
+                                  out_dtype={"f32": torch.float32, "f16": torch.float16,
+                                             "bf16": torch.bfloat16}[odt])
+    oacc = oracle.gemm(codes, oracle.unpack(wp, K))
+    oout = oracle.epilogue(oacc, sa, sw, odt, odt, bias=b, bias_dtype=odt)
+    assert np.array_equal(bits(host(out)), bits(oout))
+    # forced K-chunks through the same kernels give the same bits
+    out2 = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, odt), bias=dev(b, odt),
+                                   out_dtype=out.dtype, k_chunk=128)
+    assert np.array_equal(bits(host(out2)), bits(oout))
