@@ -23,13 +23,12 @@ __device__ __forceinline__ float bits_to_f32(uint32_t u) { return __uint_as_floa
 // bf16 -> f32 is exact: the 16 stored bits are the top half of the fp32 pattern.
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// f32 -> bf16, round to nearest even; NaN stays a quiet NaN, overflow gives Inf.
+// f32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32); NaN stays a
+// NaN, overflow gives Inf, bf16 denormals are kept.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
 }
 
 __device__ __forceinline__ float f16_to_f32(uint16_t b)

@@ -76,8 +76,22 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
     const int wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, q = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t n0 = (int64_t)blockIdx.x * BN;
-    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    // Workgroups are dealt round-robin over the 8 XCDs; give each XCD a
+    // contiguous range of tiles, M-grouped, so its L2 sees shared code rows and
+    // weight columns.
+    const int tiles_n = (int)gridDim.x, tiles_m = (int)gridDim.y;
+    const int ntiles = tiles_m * tiles_n;
+    const int bid = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+    const int q8 = ntiles >> 3, r8 = ntiles & 7;
+    const int xcd = bid & 7, loc = bid >> 3;
+    const int tile = xcd * q8 + min(xcd, r8) + loc;
+    constexpr int GROUP_M = 16;
+    const int per_group = GROUP_M * tiles_n;
+    const int first_m = (tile / per_group) * GROUP_M;
+    const int gsize = min(tiles_m - first_m, GROUP_M);
+    const int in_g = tile - (tile / per_group) * per_group;
+    const int64_t m0 = (int64_t)(first_m + in_g % gsize) * BM;
+    const int64_t n0 = (int64_t)(in_g / gsize) * BN;
     const int64_t K = a.K, M = a.M, N = a.N;
     const int64_t kbeg = (int64_t)blockIdx.z * kc;
     const int64_t kend = min(K, kbeg + kc);

@@ -46,6 +46,45 @@ __device__ __forceinline__ int quant_code(float y, float s, float rinv)
     return (int)r;
 }
 
+// Four codes packed into one dword (code r in byte r).  quant4_fast uses
+// y * (1/s) and raises `near` when any quotient lies within 2^-17 of a
+// half-integer, where only the correctly rounded quotient may be trusted;
+// quant4_exact divides.  For |y/s| <= 7 (1 + 2^-23) the fast product is within
+// 2^-19 of fl(y/s), so outside that band both give the same integer.
+__device__ __forceinline__ uint32_t pack_codes(const float (&r)[4])
+{
+    uint32_t out = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out |= ((uint32_t)((int)r[i] & 0xff)) << (8 * i);
+    return out;
+}
+
+__device__ __forceinline__ uint32_t quant4_fast(const float (&y)[4], float rinv, bool& near)
+{
+    float c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float q = y[i] * rinv;
+        const float r = rintf(q);
+        near |= fabsf(fabsf(q - r) - 0.5f) < 0x1p-17f;
+        const float cl = __builtin_amdgcn_fmed3f(r, -7.0f, 7.0f);
+        c[i] = (q == q) ? cl : 0.0f;
+    }
+    return pack_codes(c);
+}
+
+__device__ __forceinline__ uint32_t quant4_exact(const float (&y)[4], float s)
+{
+    float c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float q = y[i] / s;
+        const float cl = __builtin_amdgcn_fmed3f(rintf(q), -7.0f, 7.0f);
+        c[i] = (q == q) ? cl : 0.0f;
+    }
+    return pack_codes(c);
+}
+
 __device__ __forceinline__ float row_scale(uint32_t absmax_bits)
 {
     float a = __uint_as_float(absmax_bits);
@@ -266,6 +305,260 @@ __global__ __launch_bounds__(256) void rq_mfma_kernel(
 }
 
 // -------------------------------------------------------------------------
+// Register-resident path for 16-bit activations, group width 32 or 64,
+// contiguous rows.  Persistent workgroups (R loaded once per workgroup) walk
+// blocks of rows; a block's group-rows are dealt to the four waves as 16-row
+// MFMA tiles.  The MFMA is issued as R^T . x^T so that each lane receives four
+// consecutive outputs of one group-row: codes then leave as 4-byte stores
+// straight from registers, and rotated values never touch LDS.  Only the
+// per-row absmax crosses waves (an LDS integer max).
+//   TW = tiles per wave per block (1, 2 or 4).
+// -------------------------------------------------------------------------
+template <int DT, int GP, bool ROT, bool SMOOTH, int TW>
+__global__ __launch_bounds__(256) void rq_reg_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t sm,
+    const float* __restrict__ rot, int g, const uint16_t* __restrict__ smooth,
+    int8_t* __restrict__ codes, float* __restrict__ scales, uint16_t* __restrict__ yout,
+    int rows_per_blk)
+{
+    constexpr int NKS = GP / 32;     // 32-deep k-steps
+    constexpr int CT = GP / 16;      // 16-wide output column tiles
+    constexpr int LPL = GP / 4;      // elements per lane per group-row
+    constexpr int NV = ROT ? NKS : CT / 2;  // 16-byte vectors per lane per tile
+    __shared__ uint32_t rowmax[3][16];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int j = lane & 15, q = lane >> 4;
+    const int gpr = (int)(K / GP);
+    const int64_t nblk = (M + rows_per_blk - 1) / rows_per_blk;
+
+    // R^T fragments (A operand): lane (j, q) holds R[kk][ct*16 + j] for its k-slots
+    v8s rfr[ROT ? CT : 1][ROT ? NKS : 1];
+    if constexpr (ROT) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const int c = ct * 16 + j;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int kk = q * LPL + ks * 8 + e;
+                    float rv;
+                    if (GP == 32 && g == 16)
+                        rv = ((kk >> 4) == (c >> 4)) ? rot[(kk & 15) * 16 + (c & 15)] : 0.0f;
+                    else
+                        rv = rot[kk * GP + c];
+                    rfr[ct][ks][e] = (short)f32_to_h<DT>(rv);
+                }
+        }
+    }
+    if (tid < 48) rowmax[tid >> 4][tid & 15] = 0u;
+    __syncthreads();
+
+    // ---- loads for one block.  With a rotation, lane (j, q) of tile t reads
+    // group-row t*16 + j, slice q (the MFMA B layout).  Without one, it reads
+    // the entries ct*16 + 4q .. +3 of that group-row that it will quantize.
+    auto load_blk = [&](int64_t blk, v8s (*xf)[NV]) {
+        const int64_t m0 = blk * rows_per_blk;
+        const int nrows = (int)min((int64_t)rows_per_blk, M - m0);
+        const int ngr = nrows * gpr;
+#pragma unroll
+        for (int u = 0; u < TW; ++u) {
+            const int gr = (wave * TW + u) * 16 + j;
+            if (blk < nblk && gr < ngr) {
+                const int rl = gr / gpr, b = gr - rl * gpr;
+                const uint16_t* rowp = x + (m0 + rl) * sm + (int64_t)b * GP;
+                if constexpr (ROT) {
+                    const v4i* src = (const v4i*)(rowp + q * LPL);
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+                        xf[u][ks] = __builtin_bit_cast(v8s, __builtin_nontemporal_load(src + ks));
+                } else {
+#pragma unroll
+                    for (int c2 = 0; c2 < CT / 2; ++c2) {
+                        const uint2 lo = *(const uint2*)(rowp + (2 * c2) * 16 + 4 * q);
+                        const uint2 hi = *(const uint2*)(rowp + (2 * c2 + 1) * 16 + 4 * q);
+                        xf[u][c2] = __builtin_bit_cast(v8s, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) xf[u][v] = (v8s){0, 0, 0, 0, 0, 0, 0, 0};
+            }
+        }
+    };
+
+    auto process_blk = [&](int64_t blk, v8s (*xf)[NV], int buf) {
+        const int64_t m0 = blk * rows_per_blk;
+        const int nrows = (int)min((int64_t)rows_per_blk, M - m0);
+        const int ngr = nrows * gpr;
+        int grw[TW];
+        uint32_t yv[TW][CT][2];   // 4 values of T per (tile, ct), packed in pairs
+        uint32_t tmax[TW];
+#pragma unroll
+        for (int u = 0; u < TW; ++u) {
+            const int gr = (wave * TW + u) * 16 + j;
+            grw[u] = gr;
+            if constexpr (SMOOTH) {
+                if (gr < ngr) {
+                    const int rl = gr / gpr, b = gr - rl * gpr;
+                    const uint16_t* sp = smooth + (int64_t)b * GP;
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int el = ROT ? q * LPL + v * 8 + e
+                                               : (2 * v + (e >> 2)) * 16 + 4 * q + (e & 3);
+                            xf[u][v][e] = (short)f32_to_h<DT>(h_to_f32<DT>((uint16_t)xf[u][v][e]) /
+                                                              h_to_f32<DT>(sp[el]));
+                        }
+                    (void)rl;
+                }
+            }
+            tmax[u] = 0u;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                uint16_t h[4];
+                if constexpr (ROT) {
+                    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        if constexpr (DT == BF16)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(v8bf, rfr[ct][ks]), __builtin_bit_cast(v8bf, xf[u][ks]),
+                                acc, 0, 0, 0);
+                        else
+                            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                __builtin_bit_cast(v8h, rfr[ct][ks]), __builtin_bit_cast(v8h, xf[u][ks]),
+                                acc, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) h[r] = f32_to_h<DT>(acc[r]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) h[r] = (uint16_t)xf[u][ct >> 1][(ct & 1) * 4 + r];
+                }
+                yv[u][ct][0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                yv[u][ct][1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    tmax[u] = max(tmax[u], __float_as_uint(h_to_f32<DT>(h[r])) & 0x7fffffffu);
+            }
+            if (gr >= ngr) tmax[u] = 0u;
+        }
+
+        // per-row absmax over the rows this wave's tiles touch
+#pragma unroll
+        for (int u = 0; u < TW; ++u) {
+            const int t = wave * TW + u;
+            const int g_lo = t * 16, g_hi = min(t * 16 + 15, ngr - 1);
+            if (g_lo > g_hi) continue;
+            const int r_lo = g_lo / gpr, r_hi = g_hi / gpr;
+            const int my_r = grw[u] / gpr;
+            for (int r = r_lo; r <= r_hi; ++r) {
+                uint32_t v = (my_r == r) ? tmax[u] : 0u;
+                for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+                if (lane == 0) atomicMax(&rowmax[buf][r], v);
+            }
+        }
+        // block i accumulates into buffer i % 3 and, before its barrier, clears
+        // buffer (i + 1) % 3: every wave finished reading that buffer (block
+        // i - 2) before the previous barrier, and nobody writes it before this one.
+        if (tid < 16) rowmax[buf == 2 ? 0 : buf + 1][tid] = 0u;
+        __syncthreads();
+
+        // quantize from registers: 4 consecutive codes per (tile, ct); the
+        // division is redone only for tiles where some lane sits near a tie
+#pragma unroll
+        for (int u = 0; u < TW; ++u) {
+            const int gr = grw[u];
+            const bool live = gr < ngr;
+            const int rl = live ? gr / gpr : 0;
+            const int b = live ? gr - rl * gpr : 0;
+            const float s = row_scale(rowmax[buf][rl]);
+            const float ri = 1.0f / s;
+            uint32_t pk[CT];
+            bool near = false;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                float yy[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    yy[r] = h_to_f32<DT>((uint16_t)(yv[u][ct][r >> 1] >> (16 * (r & 1))));
+                pk[ct] = quant4_fast(yy, ri, near);
+            }
+            if (__any(near && live)) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    float yy[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        yy[r] = h_to_f32<DT>((uint16_t)(yv[u][ct][r >> 1] >> (16 * (r & 1))));
+                    pk[ct] = quant4_exact(yy, s);
+                }
+            }
+            // Lane (j, q) holds codes ct*16 + 4q .. +3 of group-row j for each
+            // ct; the four lanes of a group-row exchange dwords (4 rounds of
+            // ds_bpermute) so that each ends up with 16 consecutive codes and
+            // a wave stores whole 64-byte group-rows.
+            if constexpr (CT == 4) {
+                uint32_t o4[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int send = (q - t) & 3;
+                    uint32_t v = pk[0];
+                    v = send == 1 ? pk[1] : v;
+                    v = send == 2 ? pk[2] : v;
+                    v = send == 3 ? pk[3] : v;
+                    const uint32_t got = (uint32_t)__shfl((int)v, j + 16 * ((q + t) & 3));
+                    o4[(q + t) & 3] = got;   // dword from the lane with that q
+                }
+                // o4[d] now holds codes q*16 + 4d .. +3 (d = source lane's q)
+                uint32_t w0 = o4[0], w1 = o4[1], w2 = o4[2], w3 = o4[3];
+                if (live) {
+                    int8_t* crow = codes + (m0 + rl) * K + (int64_t)b * GP;
+                    *(uint4*)(crow + q * 16) = make_uint4(w0, w1, w2, w3);
+                }
+            } else {
+                if (live) {
+                    int8_t* crow = codes + (m0 + rl) * K + (int64_t)b * GP;
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) *(uint32_t*)(crow + ct * 16 + 4 * q) = pk[ct];
+                }
+            }
+            if (live && yout) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    uint2 yy = make_uint2(yv[u][ct][0], yv[u][ct][1]);
+                    *(uint2*)(yout + (m0 + rl) * K + (int64_t)b * GP + ct * 16 + 4 * q) = yy;
+                }
+            }
+        }
+        if (tid < nrows) scales[m0 + tid] = row_scale(rowmax[buf][tid]);
+    };
+
+    // two register sets alternate (the loop covers two blocks), so the next
+    // block's loads are in flight while the current one is processed
+    v8s xa[TW][NV], xb[TW][NV];
+    const int64_t stride = gridDim.x;
+    int64_t blk = blockIdx.x;
+    int buf = 0;
+    load_blk(blk, xa);
+    while (blk < nblk) {
+        load_blk(blk + stride, xb);
+        process_blk(blk, xa, buf);
+        buf = buf == 2 ? 0 : buf + 1;
+        blk += stride;
+        if (blk >= nblk) break;
+        load_blk(blk + stride, xa);
+        process_blk(blk, xb, buf);
+        buf = buf == 2 ? 0 : buf + 1;
+        blk += stride;
+    }
+}
+
+// -------------------------------------------------------------------------
 // Generic path (fp32 activations, or shapes the MFMA path does not take):
 // one workgroup per row, the (smoothed) row staged in LDS as fp32, the
 // rotation evaluated on VALU twice (absmax pass, then quantize pass) as an
@@ -430,7 +723,63 @@ static hipError_t launch_generic_dt(const RQArgs& a, hipStream_t st)
     return go(rq_generic_kernel<DT, false, false>);
 }
 
-// Chooses the kernel; returns the path taken in *path (0 generic, 1 MFMA).
+
+template <int DT, int GP, bool ROT, bool SMOOTH>
+static hipError_t launch_reg_t(const RQArgs& a, hipStream_t st)
+{
+    const int gpr = (int)(a.K / GP);
+    // rows per block: enough group-rows for one 16-row tile per wave
+    int rows = 64 / (gpr > 0 ? gpr : 1);
+    if (rows < 1) rows = 1;
+    if (rows > 16) rows = 16;
+    const int tiles = (rows * gpr + 15) / 16;
+    int tw = (tiles + 3) / 4;
+    if (tw > 4) return hipErrorNotSupported;
+    const int64_t nblk = (a.M + rows - 1) / rows;
+    auto go = [&](auto kern) {
+        // persistent grid: exactly the workgroups that can be resident
+        static int per_cu = 0, n_cu = 0;
+        if (per_cu == 0) {
+            int dev = 0;
+            hipDeviceProp_t p;
+            if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&p, dev) != hipSuccess ||
+                hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess ||
+                per_cu < 1) {
+                per_cu = 2;
+                n_cu = 256;
+            } else {
+                n_cu = p.multiProcessorCount;
+            }
+        }
+        int64_t grid = (int64_t)per_cu * n_cu;
+        if (grid > nblk) grid = nblk;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.x, a.M,
+                           a.K, a.sm, a.rot, a.g, (const uint16_t*)a.smooth, a.codes, a.scales,
+                           (uint16_t*)a.yout, rows);
+        return hipGetLastError();
+    };
+    if (tw == 1) return go(rq_reg_kernel<DT, GP, ROT, SMOOTH, 1>);
+    if (tw == 2) return go(rq_reg_kernel<DT, GP, ROT, SMOOTH, 2>);
+    return go(rq_reg_kernel<DT, GP, ROT, SMOOTH, 4>);
+}
+
+template <int DT>
+static hipError_t launch_reg_dt(const RQArgs& a, int GP, hipStream_t st)
+{
+    const bool rot = a.rot != nullptr, sm = a.smooth != nullptr;
+    if (GP == 32) {
+        if (rot && sm) return launch_reg_t<DT, 32, true, true>(a, st);
+        if (rot) return launch_reg_t<DT, 32, true, false>(a, st);
+        if (sm) return launch_reg_t<DT, 32, false, true>(a, st);
+        return launch_reg_t<DT, 32, false, false>(a, st);
+    }
+    if (rot && sm) return launch_reg_t<DT, 64, true, true>(a, st);
+    if (rot) return launch_reg_t<DT, 64, true, false>(a, st);
+    if (sm) return launch_reg_t<DT, 64, false, true>(a, st);
+    return launch_reg_t<DT, 64, false, false>(a, st);
+}
+
+// Chooses the kernel; returns the path taken in *path (0 generic, 1 MFMA LDS, 2 MFMA registers).
 hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path)
 {
     // MFMA path: 16-bit activations, group width 16..256, K a multiple of
@@ -445,6 +794,12 @@ hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path)
     if (a.rot && !(a.g == 16 || a.g == 32 || a.g == 64 || a.g == 128 || a.g == 256)) ok = false;
     if (ok && mfma_lds_bytes(GP, a.K, 1) > 160 * 1024) ok = false;
     const bool contig = a.sk == 1 && (a.sm % 8) == 0 && ((uintptr_t)a.x % 16) == 0;
+    if (ok && contig && GP <= 64 && a.K / GP <= 256 &&
+        (a.yout == nullptr || ((uintptr_t)a.yout % 8) == 0) &&
+        ((uintptr_t)a.codes % 4) == 0) {
+        if (path) *path = 2;
+        return a.dtype == BF16 ? launch_reg_dt<BF16>(a, GP, st) : launch_reg_dt<F16>(a, GP, st);
+    }
     if (ok) {
         if (path) *path = 1;
         return a.dtype == BF16 ? launch_mfma_dt<BF16>(a, GP, contig, st)
