@@ -85,12 +85,56 @@ __device__ __forceinline__ uint32_t quant4_exact(const float (&y)[4], float s)
     return pack_codes(c);
 }
 
+// Fast path for rows whose scale is finite (then every entry is finite).  The
+// clamped quotient plus 1.5 * 2^23 is rounded to the nearest even integer by
+// the addition itself, and that integer's low byte is the two's-complement
+// code; subtracting the constant again gives the rounded value exactly, so
+// the residual q - r shows whether q sat within 2^-17 of a half-integer.
+constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
+
+__device__ __forceinline__ uint32_t pack4_magic(float t0, float t1, float t2, float t3)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(t3), __float_as_uint(t2), 0x0c0c0400u);
+    return lo | (hi << 16);
+}
+
+__device__ __forceinline__ uint32_t quant4_finite(const float (&y)[4], float rinv, bool& near)
+{
+    float t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float qv = y[i] * rinv;
+        const float c = __builtin_amdgcn_fmed3f(qv, -7.0f, 7.0f);
+        t[i] = c + kRoundMagic;
+        const float r = t[i] - kRoundMagic;
+        near |= fabsf(qv - r) > 0.5f - 0x1p-17f;
+    }
+    return pack4_magic(t[0], t[1], t[2], t[3]);
+}
+
 __device__ __forceinline__ float row_scale(uint32_t absmax_bits)
 {
     float a = __uint_as_float(absmax_bits);
     float s = a / 7.0f;
     if (s < 0x1p-126f) s = 0x1p-126f;  // NaN compares false and stays NaN
     return s;
+}
+
+// Wave-wide unsigned max with DPP moves inside each row of 16 lanes (quad
+// swaps, then row rotations by 4 and 8) and four lane reads across rows; no
+// LDS round trips.
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));  // quad [1,0,3,2]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));  // quad [2,3,0,1]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false)); // row_ror:4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false)); // row_ror:8
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(r0, r1), max(r2, r3));
 }
 
 __device__ __forceinline__ uint32_t wave_max16(uint32_t v)
@@ -559,6 +603,266 @@ __global__ __launch_bounds__(256) void rq_reg_kernel(
 }
 
 // -------------------------------------------------------------------------
+// Wave-per-row-block path (16-bit activations, g <= 64, K/g <= 64): every
+// wave owns RPB whole rows (RPB * K/g <= 16 * TW group-rows, one tile of 16
+// group-rows per unit of TW), so the row absmax is a wave shuffle and waves
+// never wait for each other: no LDS, no barrier.  Loads for the wave's next
+// row-block are in flight while the current one is rotated and quantized.
+// -------------------------------------------------------------------------
+template <int DT, int GP, bool ROT, bool SMOOTH, int TW>
+__global__ __launch_bounds__(256, 3) void rq_wave_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t sm,
+    const float* __restrict__ rot, int g, const uint16_t* __restrict__ smooth,
+    int8_t* __restrict__ codes, float* __restrict__ scales, uint16_t* __restrict__ yout, int rpb)
+{
+    constexpr int NKS = GP / 32;
+    constexpr int CT = GP / 16;
+    constexpr int LPL = GP / 4;
+    constexpr int NV = ROT ? NKS : CT / 2;
+
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15, q = lane >> 4;
+    const int gpr = (int)(K / GP);
+    const int64_t nblk = (M + rpb - 1) / rpb;
+    const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+
+    v8s rfr[ROT ? CT : 1][ROT ? NKS : 1];
+    if constexpr (ROT) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const int c = ct * 16 + j;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int kk = q * LPL + ks * 8 + e;
+                    float rv;
+                    if (GP == 32 && g == 16)
+                        rv = ((kk >> 4) == (c >> 4)) ? rot[(kk & 15) * 16 + (c & 15)] : 0.0f;
+                    else
+                        rv = rot[kk * GP + c];
+                    rfr[ct][ks][e] = (short)f32_to_h<DT>(rv);
+                }
+        }
+    }
+
+    // A lane's place inside a row-block never changes: precompute, per tile,
+    // its row within the block and 32-bit offsets into x and the codes.
+    int t_row[TW], t_xoff[TW], t_coff[TW], t_b[TW];
+#pragma unroll
+    for (int u = 0; u < TW; ++u) {
+        const int gr = u * 16 + j;
+        const int rl = gr / gpr, b = gr - rl * gpr;
+        t_row[u] = rl;
+        t_b[u] = b;
+        t_xoff[u] = (int)(rl * sm + b * GP);
+        t_coff[u] = (int)(rl * K + b * GP);
+    }
+
+    auto load_blk = [&](int64_t blk, v8s (*xf)[NV]) {
+        const int64_t m0 = blk * rpb;
+        const int nrows = blk < nblk ? (int)min((int64_t)rpb, M - m0) : 0;
+        const uint16_t* xb = x + m0 * sm;
+#pragma unroll
+        for (int u = 0; u < TW; ++u) {
+            if (t_row[u] < nrows) {
+                const uint16_t* rowp = xb + t_xoff[u];
+                if constexpr (ROT) {
+                    const v4i* src = (const v4i*)(rowp + q * LPL);
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+                        xf[u][ks] = __builtin_bit_cast(v8s, __builtin_nontemporal_load(src + ks));
+                } else {
+#pragma unroll
+                    for (int c2 = 0; c2 < CT / 2; ++c2) {
+                        const uint2 lo = *(const uint2*)(rowp + (2 * c2) * 16 + 4 * q);
+                        const uint2 hi = *(const uint2*)(rowp + (2 * c2 + 1) * 16 + 4 * q);
+                        xf[u][c2] = __builtin_bit_cast(v8s, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) xf[u][v] = (v8s){0, 0, 0, 0, 0, 0, 0, 0};
+            }
+        }
+    };
+
+    // fp32 MFMA results of one (tile, ct): 4 consecutive entries of group-row j
+    auto rotate4f = [&](const v8s* xt, int ct, float (&f)[4]) {
+        if constexpr (ROT) {
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                if constexpr (DT == BF16)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(v8bf, rfr[ct][ks]), __builtin_bit_cast(v8bf, xt[ks]), acc, 0, 0, 0);
+                else
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(v8h, rfr[ct][ks]), __builtin_bit_cast(v8h, xt[ks]), acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) f[r] = acc[r];
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) f[r] = h_to_f32<DT>((uint16_t)xt[ct >> 1][(ct & 1) * 4 + r]);
+        }
+    };
+
+    // Two passes over the registers: absmax, then quantize.  The rotation is
+    // recomputed in the second pass (a few MFMAs per tile) instead of keeping
+    // the rotated values live, which keeps enough waves resident.
+    auto process_blk = [&](int64_t blk, v8s (*xf)[NV]) {
+        const int64_t m0 = blk * rpb;
+        const int nrows = (int)min((int64_t)rpb, M - m0);
+        uint32_t tmax[TW];
+#pragma unroll
+        for (int u = 0; u < TW; ++u) {
+            const bool live = t_row[u] < nrows;
+            if constexpr (SMOOTH) {
+                if (live) {
+                    const uint16_t* sp = smooth + t_b[u] * GP;
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int el = ROT ? q * LPL + v * 8 + e
+                                               : (2 * v + (e >> 2)) * 16 + 4 * q + (e & 3);
+                            xf[u][v][e] = (short)f32_to_h<DT>(h_to_f32<DT>((uint16_t)xf[u][v][e]) /
+                                                              h_to_f32<DT>(sp[el]));
+                        }
+                }
+            }
+            // max |.| of the fp32 results, rounded to T once: rounding is
+            // monotone, so this is the max of the rounded values (a NaN, whose
+            // bits exceed every finite pattern, still dominates)
+            uint32_t m = 0u;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                float f[4];
+                rotate4f(xf[u], ct, f);
+                m = max(m, max(max(__float_as_uint(f[0]) & 0x7fffffffu, __float_as_uint(f[1]) & 0x7fffffffu),
+                               max(__float_as_uint(f[2]) & 0x7fffffffu, __float_as_uint(f[3]) & 0x7fffffffu)));
+            }
+            m = __float_as_uint(h_to_f32<DT>(f32_to_h<DT>(__uint_as_float(m)))) & 0x7fffffffu;
+            tmax[u] = live ? m : 0u;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // row scales: one wave-wide max per row of the block
+        float srow[TW], rinv[TW];
+#pragma unroll
+        for (int u = 0; u < TW; ++u) { srow[u] = 1.0f; rinv[u] = 1.0f; }
+        for (int r = 0; r < nrows; ++r) {
+            uint32_t v = 0u;
+#pragma unroll
+            for (int u = 0; u < TW; ++u)
+                if (t_row[u] == r) v = max(v, tmax[u]);
+            v = wave_max_dpp(v);
+            const float sv = row_scale(v);
+            if (lane == 0) scales[m0 + r] = sv;
+            const float ri = 1.0f / sv;
+#pragma unroll
+            for (int u = 0; u < TW; ++u)
+                if (t_row[u] == r) { srow[u] = sv; rinv[u] = ri; }
+        }
+        int8_t* cb = codes + m0 * K;
+        uint16_t* yb = yout ? yout + m0 * K : nullptr;
+        // quantize; exact division only for tiles with a near-tie somewhere
+#pragma unroll
+        for (int u = 0; u < TW; ++u) {
+            const bool live = t_row[u] < nrows;
+            uint32_t pk[CT];
+            uint32_t yv[CT][2];
+            const float sv = srow[u], ri = rinv[u];
+            if (__any(live && !(fabsf(sv) < 3.0e38f))) {
+                // some row of this tile has a NaN or Inf scale: exact path
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    float f[4];
+                    rotate4f(xf[u], ct, f);
+                    uint16_t h[4];
+                    float yy[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        h[r] = f32_to_h<DT>(f[r]);
+                        yy[r] = h_to_f32<DT>(h[r]);
+                    }
+                    yv[ct][0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                    yv[ct][1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+                    pk[ct] = quant4_exact(yy, sv);
+                }
+            } else {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    float f[4];
+                    rotate4f(xf[u], ct, f);
+                    uint16_t h[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) h[r] = f32_to_h<DT>(f[r]);
+                    yv[ct][0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                    yv[ct][1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+                    float t[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float yy = h_to_f32<DT>(h[r]);
+                        const float qv = yy * ri;
+                        t[r] = __builtin_amdgcn_fmed3f(qv, -7.0f, 7.0f) + kRoundMagic;
+                        const bool nr = fabsf(qv - (t[r] - kRoundMagic)) > 0.5f - 0x1p-17f;
+                        // a value-slot where some lane sits near a tie is
+                        // redone with the correctly rounded quotient
+                        if (__any(nr)) t[r] = __builtin_amdgcn_fmed3f(yy / sv, -7.0f, 7.0f) + kRoundMagic;
+                    }
+                    pk[ct] = pack4_magic(t[0], t[1], t[2], t[3]);
+                }
+            }
+            if constexpr (CT == 4) {
+                uint32_t o4[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int send = (q - t) & 3;
+                    uint32_t v = pk[0];
+                    v = send == 1 ? pk[1] : v;
+                    v = send == 2 ? pk[2] : v;
+                    v = send == 3 ? pk[3] : v;
+                    o4[(q + t) & 3] = (uint32_t)__shfl((int)v, j + 16 * ((q + t) & 3));
+                }
+                if (live) *(uint4*)(cb + t_coff[u] + q * 16) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+            } else {
+                if (live) {
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) *(uint32_t*)(cb + t_coff[u] + ct * 16 + 4 * q) = pk[ct];
+                }
+            }
+            if (live && yb) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    *(uint2*)(yb + t_coff[u] + ct * 16 + 4 * q) = make_uint2(yv[ct][0], yv[ct][1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // With up to two tiles per wave the next row-block's loads are issued
+    // before the current one is processed (the register copy afterwards finds
+    // them arrived); with four, registers go to occupancy instead.
+    constexpr bool PF = TW <= 2;
+    v8s xa[TW][NV], xb[PF ? TW : 1][NV];
+    load_blk(wid, xa);
+    for (int64_t blk = wid; blk < nblk; blk += nwaves) {
+        if constexpr (PF) load_blk(blk + nwaves, xb);
+        process_blk(blk, xa);
+        if constexpr (PF) {
+#pragma unroll
+            for (int u = 0; u < TW; ++u)
+#pragma unroll
+                for (int v = 0; v < NV; ++v) xa[u][v] = xb[u][v];
+        } else {
+            load_blk(blk + nwaves, xa);
+        }
+    }
+}
+
+// -------------------------------------------------------------------------
 // Generic path (fp32 activations, or shapes the MFMA path does not take):
 // one workgroup per row, the (smoothed) row staged in LDS as fp32, the
 // rotation evaluated on VALU twice (absmax pass, then quantize pass) as an
@@ -779,6 +1083,60 @@ static hipError_t launch_reg_dt(const RQArgs& a, int GP, hipStream_t st)
     return launch_reg_t<DT, 64, false, false>(a, st);
 }
 
+
+template <int DT, int GP, bool ROT, bool SMOOTH>
+static hipError_t launch_wave_t(const RQArgs& a, hipStream_t st)
+{
+    const int gpr = (int)(a.K / GP);
+    int tw = (gpr + 15) / 16;
+    tw = tw <= 1 ? 1 : tw <= 2 ? 2 : 4;
+    if (gpr > 64) return hipErrorNotSupported;
+    int rpb = (16 * tw) / gpr;
+    if (rpb < 1) rpb = 1;
+    const int64_t nblk = (a.M + rpb - 1) / rpb;
+    auto go = [&](auto kern) {
+        static int per_cu = 0, n_cu = 0;
+        if (per_cu == 0) {
+            int dev = 0;
+            hipDeviceProp_t p;
+            if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&p, dev) != hipSuccess ||
+                hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess ||
+                per_cu < 1) {
+                per_cu = 2;
+                n_cu = 256;
+            } else {
+                n_cu = p.multiProcessorCount;
+            }
+        }
+        int64_t grid = (int64_t)per_cu * n_cu;
+        const int64_t need = (nblk + 3) / 4;          // four waves per workgroup
+        if (grid > need) grid = need;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.x, a.M,
+                           a.K, a.sm, a.rot, a.g, (const uint16_t*)a.smooth, a.codes, a.scales,
+                           (uint16_t*)a.yout, rpb);
+        return hipGetLastError();
+    };
+    if (tw == 1) return go(rq_wave_kernel<DT, GP, ROT, SMOOTH, 1>);
+    if (tw == 2) return go(rq_wave_kernel<DT, GP, ROT, SMOOTH, 2>);
+    return go(rq_wave_kernel<DT, GP, ROT, SMOOTH, 4>);
+}
+
+template <int DT>
+static hipError_t launch_wave_dt(const RQArgs& a, int GP, hipStream_t st)
+{
+    const bool rot = a.rot != nullptr, sm = a.smooth != nullptr;
+    if (GP == 32) {
+        if (rot && sm) return launch_wave_t<DT, 32, true, true>(a, st);
+        if (rot) return launch_wave_t<DT, 32, true, false>(a, st);
+        if (sm) return launch_wave_t<DT, 32, false, true>(a, st);
+        return launch_wave_t<DT, 32, false, false>(a, st);
+    }
+    if (rot && sm) return launch_wave_t<DT, 64, true, true>(a, st);
+    if (rot) return launch_wave_t<DT, 64, true, false>(a, st);
+    if (sm) return launch_wave_t<DT, 64, false, true>(a, st);
+    return launch_wave_t<DT, 64, false, false>(a, st);
+}
+
 // Chooses the kernel; returns the path taken in *path (0 generic, 1 MFMA LDS, 2 MFMA registers).
 hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path)
 {
@@ -794,6 +1152,11 @@ hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path)
     if (a.rot && !(a.g == 16 || a.g == 32 || a.g == 64 || a.g == 128 || a.g == 256)) ok = false;
     if (ok && mfma_lds_bytes(GP, a.K, 1) > 160 * 1024) ok = false;
     const bool contig = a.sk == 1 && (a.sm % 8) == 0 && ((uintptr_t)a.x % 16) == 0;
+    if (ok && contig && GP <= 64 && a.K / GP <= 64 &&
+        (a.yout == nullptr || ((uintptr_t)a.yout % 8) == 0) && ((uintptr_t)a.codes % 16) == 0) {
+        if (path) *path = 3;
+        return a.dtype == BF16 ? launch_wave_dt<BF16>(a, GP, st) : launch_wave_dt<F16>(a, GP, st);
+    }
     if (ok && contig && GP <= 64 && a.K / GP <= 256 &&
         (a.yout == nullptr || ((uintptr_t)a.yout % 8) == 0) &&
         ((uintptr_t)a.codes % 4) == 0) {
