@@ -12,19 +12,26 @@
 // with l[m,n] = sum_r L[m,r] * up[n,r]; every listed multiply and add is a
 // separately rounded fp32 operation.
 //
-// Design for CDNA4:
-//   * 128 x 128 output tile per 256-thread workgroup, 4 waves in 2 x 2, each
-//     wave a 64 x 64 block of 4 x 4 v_mfma_i32_16x16x64_i8 tiles; K advances
-//     64 per step with double-buffered LDS (one barrier per step) and the next
-//     step's global loads in flight during the MFMAs.
-//   * Packed weights are read as bytes (N, K/2) and unpacked once per tile
-//     into LDS as 16*w: the low nibble shifted into the high half of a byte
-//     and the high nibble masked in place are both already sign-correct int8
-//     values, so unpacking is shift/and/perm with no sign extension.  The
-//     integer result is divided by 16 (an exact arithmetic shift) before the
-//     epilogue.
-//   * LDS rows are padded to 80 bytes so the 16 lanes of a ds_read_b128
-//     phase hit distinct banks.
+// Design for CDNA4 (two kernels; launch_gemm picks one per call):
+//   * w4a4_gemm_ring3_kernel, for prefill-sized layers: 256 x 256 output tile
+//     per workgroup, one wave per SIMD, each wave a 128 x 128 block of 8 x 8
+//     v_mfma_i32_16x16x64_i8 tiles with its 256 INT32 accumulators in AGPRs.
+//     Codes and packed weights stream global -> LDS through buffer_load ... lds
+//     into a three-stage ring, so two K-steps are in flight while one is
+//     multiplied; the weights are unpacked in registers right before the MFMAs.
+//   * w4a4_gemm_kernel, for everything else (decode-sized M, per-64-group
+//     weight scales, the low-rank term, INT32 export, K-chunked runs): 128 x 128
+//     output tile, 4 waves in 2 x 2, each a 64 x 64 block of 4 x 4 MFMA tiles;
+//     K advances 64 per step with double-buffered LDS and the next step's
+//     global loads in flight during the MFMAs.
+//   * Packed weights are read as bytes (N, K/2) and unpacked as 16*w: the low
+//     nibble shifted into the high half of a byte and the high nibble masked
+//     in place are both already sign-correct int8 values, so unpacking is
+//     shift/and/perm with no sign extension.  The integer result is divided
+//     by 16 (an exact arithmetic shift) before the epilogue.
+//   * Workgroups are dealt round-robin over the 8 XCDs; tiles are renumbered
+//     so that each XCD works on a contiguous, M-grouped range and its L2 sees
+//     shared code rows and weight columns.
 //   * When K is too large for INT32 (16 * 7 * 8 * K > 2^31 - 1) or a chunk
 //     size is forced, each workgroup accumulates one K-chunk and adds it into
 //     an int64 workspace with 64-bit atomics (exact and order-independent);
@@ -35,15 +42,6 @@
 namespace w4a4 {
 
 constexpr int BM = 128, BN = 128, BK = 64, LDR = 80;
-#ifndef W4A4_GEMM_KERNEL
-#define W4A4_GEMM_KERNEL 1
-#endif
-// 5: four-wave 256x256 (AGPR accumulators); 8: eight-wave 256x256;
-// 4: first four-wave 256x256; 1: 128x128
-constexpr bool kUseFourWaveV2 = W4A4_GEMM_KERNEL == 5;
-constexpr bool kUseEightWave = W4A4_GEMM_KERNEL == 8;
-constexpr bool kUseBig = W4A4_GEMM_KERNEL >= 4;
-
 __device__ __forceinline__ void unpack16(uint32_t p, uint32_t& lo4, uint32_t& hi4)
 {
     // p holds 8 nibbles for k0..k7 (even k in the low nibble of each byte).
@@ -239,236 +237,11 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
 }
 
 
-// -------------------------------------------------------------------------
-// Large-tile kernel (per-channel scales, M > 128): 256 x 256 output tile per
-// workgroup, four waves in 2 x 2, each a 128 x 128 block of 8 x 8
-// v_mfma_i32_16x16x64_i8 tiles (256 INT32 accumulators per lane).  Only the
-// codes are staged through LDS (double-buffered, 80-byte padded rows); each
-// wave reads its packed weight fragments straight from global memory (8 bytes
-// = 16 nibbles per lane per tile) and unpacks them in registers, so weights
-// never touch LDS.  Tiles are numbered so that each XCD (workgroups are
-// dealt round-robin over 8) works on a contiguous, M-grouped range of tiles
-// and its L2 sees the same weight slices and code rows.
-// -------------------------------------------------------------------------
+
 constexpr int BBM = 256, BBN = 256;
+constexpr int W8_EPR = 132;  // epilogue strip row, words (128 + 4 pad)
 
-__device__ __forceinline__ v4i unpack_frag(uint2 p)
-{
-    v4i r;
-    uint32_t a, b, c, d;
-    unpack16(p.x, a, b);
-    unpack16(p.y, c, d);
-    r[0] = (int)a; r[1] = (int)b; r[2] = (int)c; r[3] = (int)d;
-    return r;
-}
-
-template <int ODT, bool SPLIT>
-__global__ __launch_bounds__(256) void w4a4_gemm_big_kernel(GemmArgs a, int64_t kc, int tiles_m,
-                                                            int tiles_n)
-{
-    // main loop: A tiles, double-buffered; epilogue: per-wave 16 x 128 int32
-    // strips with rows padded to 132 words (reuses the same LDS).
-    constexpr int EPR = 132;
-    constexpr int LDS_BYTES = (2 * BBM * LDR > 4 * 16 * EPR * 4) ? 2 * BBM * LDR : 4 * 16 * EPR * 4;
-    __shared__ __align__(16) int8_t smem[LDS_BYTES];
-    int8_t (*As)[BBM * LDR] = (int8_t (*)[BBM * LDR])smem;
-
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int j = lane & 15, q = lane >> 4;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    // XCD-contiguous tile ranges, then M-grouped order inside a range.
-    const int ntiles = tiles_m * tiles_n;
-    const int bid = blockIdx.x;
-    const int q8 = ntiles >> 3, r8 = ntiles & 7;
-    const int xcd = bid & 7, loc = bid >> 3;
-    const int tile = xcd * q8 + min(xcd, r8) + loc;
-    constexpr int GROUP_M = 8;
-    const int per_group = GROUP_M * tiles_n;
-    const int first_m = (tile / per_group) * GROUP_M;
-    const int gsize = min(tiles_m - first_m, GROUP_M);
-    const int in_g = tile - (tile / per_group) * per_group;
-    const int tm = first_m + in_g % gsize;
-    const int tn = in_g / gsize;
-
-    const int64_t m0 = (int64_t)tm * BBM, n0 = (int64_t)tn * BBN;
-    const int64_t K = a.K, M = a.M, N = a.N;
-    const int64_t kbeg = (int64_t)blockIdx.z * kc;
-    const int64_t kend = min(K, kbeg + kc);
-    const int nsteps = (int)((kend - kbeg + BK - 1) / BK);
-
-    uint4 ra[4];
-    auto aload = [&](int64_t k) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c >> 2, c16 = c & 3;
-            const int64_t gm = m0 + row, gk = k + c16 * 16;
-            ra[i] = (gm < M && gk < kend) ? *(const uint4*)(a.codes + gm * K + gk)
-                                          : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto astore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c >> 2, c16 = c & 3;
-            *(uint4*)(&As[buf][row * LDR + c16 * 16]) = ra[i];
-        }
-    };
-    // packed weight fragments: column n0 + wn*128 + nt*16 + j, k + q*16 .. +16
-    const uint8_t* wrow[8];
-    bool wok[8];
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-        const int64_t col = n0 + wn * 128 + nt * 16 + j;
-        wok[nt] = col < N;
-        wrow[nt] = a.wp + (wok[nt] ? col : 0) * (K >> 1) + q * 8;
-    }
-    uint2 bq[8];
-    auto bload = [&](int64_t k) {
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-            bq[nt] = (wok[nt] && k + q * 16 < kend) ? *(const uint2*)(wrow[nt] + (k >> 1))
-                                                    : make_uint2(0, 0);
-    };
-
-    v4i acc[8][8];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = (v4i){0, 0, 0, 0};
-
-    if (nsteps > 0) {
-        aload(kbeg);
-        astore(0);
-        bload(kbeg);
-    }
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-        const int buf = s & 1;
-        const bool more = s + 1 < nsteps;
-        const int64_t knext = kbeg + (int64_t)(s + 1) * BK;
-        if (more) aload(knext);
-        v4i bf[8];
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) bf[nt] = unpack_frag(bq[nt]);
-        if (more) bload(knext);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const v4i af = *(const v4i*)(&As[buf][(wm * 128 + mt * 16 + j) * LDR + q * 16]);
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[nt], acc[mt][nt], 0, 0, 0);
-        }
-        if (more) astore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue, one 16-row strip at a time per wave: lane (j, q) holds
-    // rows 4q..4q+3 / column j of each 16 x 16 tile; after the LDS transpose a
-    // lane owns 32 consecutive columns of one row.
-    int* strip = (int*)smem + wave * 16 * EPR;
-    const int er = lane >> 2;            // row within the strip
-    const int ec = (lane & 3) * 32;      // first of 32 columns (of 128)
-    const int64_t col0 = n0 + wn * 128 + ec;
-    float swv[32], bsv[32];
-#pragma unroll
-    for (int c = 0; c < 32; ++c) {
-        const int64_t col = col0 + c;
-        swv[c] = col < N ? load_any_f32(a.sw_dtype, a.sw, col) : 0.0f;
-        bsv[c] = (a.bias && col < N) ? load_any_f32(a.bias_dtype, a.bias, col) : 0.0f;
-    }
-    const bool has_bias = a.bias != nullptr;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) strip[(4 * q + r) * EPR + nt * 16 + j] = acc[mt][nt][r] >> 4;
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): strip writes of this wave done
-        __builtin_amdgcn_wave_barrier();
-        const int64_t row = m0 + wm * 128 + mt * 16 + er;
-        int iv[32];
-#pragma unroll
-        for (int c4 = 0; c4 < 8; ++c4) {
-            const int4 v = *(const int4*)(strip + er * EPR + ec + 4 * c4);
-            iv[4 * c4] = v.x; iv[4 * c4 + 1] = v.y; iv[4 * c4 + 2] = v.z; iv[4 * c4 + 3] = v.w;
-        }
-        __builtin_amdgcn_wave_barrier();
-        if (row < M) {
-            const bool full = col0 + 32 <= N;
-            if constexpr (SPLIT) {
-#pragma unroll
-                for (int c = 0; c < 32; ++c)
-                    if (col0 + c < N)
-                        atomicAdd((unsigned long long*)(a.acc64 + row * N + col0 + c),
-                                  (unsigned long long)(int64_t)iv[c]);
-            } else {
-                if (a.acc_out) {
-#pragma unroll
-                    for (int c = 0; c < 32; ++c)
-                        if (col0 + c < N) a.acc_out[row * N + col0 + c] = iv[c];
-                }
-                const float sa = a.sa[row];
-                float o[32];
-#pragma unroll
-                for (int c = 0; c < 32; ++c) {
-                    float t = mul_rn(mul_rn((float)iv[c], sa), swv[c]);
-                    if (has_bias) t = add_rn(t, bsv[c]);
-                    o[c] = t;
-                }
-                if constexpr (ODT == F32) {
-                    float* dst = (float*)a.out + row * N + col0;
-                    if (full && (N % 4) == 0) {
-#pragma unroll
-                        for (int c4 = 0; c4 < 8; ++c4)
-                            *(float4*)(dst + 4 * c4) = make_float4(o[4 * c4], o[4 * c4 + 1],
-                                                                   o[4 * c4 + 2], o[4 * c4 + 3]);
-                    } else {
-#pragma unroll
-                        for (int c = 0; c < 32; ++c)
-                            if (col0 + c < N) dst[c] = o[c];
-                    }
-                } else {
-                    uint16_t* dst = (uint16_t*)a.out + row * N + col0;
-                    uint32_t pk[16];
-#pragma unroll
-                    for (int c2 = 0; c2 < 16; ++c2)
-                        pk[c2] = (uint32_t)f32_to_h<ODT>(o[2 * c2]) |
-                                 ((uint32_t)f32_to_h<ODT>(o[2 * c2 + 1]) << 16);
-                    if (full && (N % 8) == 0) {
-#pragma unroll
-                        for (int c8 = 0; c8 < 4; ++c8)
-                            *(uint4*)(dst + 8 * c8) = make_uint4(pk[4 * c8], pk[4 * c8 + 1],
-                                                                 pk[4 * c8 + 2], pk[4 * c8 + 3]);
-                    } else {
-#pragma unroll
-                        for (int c = 0; c < 32; ++c)
-                            if (col0 + c < N) dst[c] = (uint16_t)(pk[c >> 1] >> (16 * (c & 1)));
-                    }
-                }
-            }
-        }
-    }
-}
-
-
-// -------------------------------------------------------------------------
-// Eight-wave kernel (per-channel scales, M > 128, K % 64 == 0): 256 x 256
-// tile per 512-thread workgroup, waves in 4 (M) x 2 (N), each a 64 x 128 block
-// of 4 x 8 v_mfma_i32_16x16x64_i8 tiles (128 INT32 accumulators per lane), two
-// waves per SIMD.  All global reads are buffer loads whose out-of-range lanes
-// return zero (no branches around loads).  Codes go through LDS; while they
-// are staged, each 16-byte chunk is reordered to (even k of the first 8,
-// odd k of the first 8, even k of the last 8, odd k of the last 8), which is
-// the order in which a packed weight dword unpacks with no byte permutes:
-// (p & 0x0f0f0f0f) << 4 gives 16*w of the even k, p & 0xf0f0f0f0 the odd k.
-// The MFMA contracts over k, so any order shared by both operands is exact.
-// -------------------------------------------------------------------------
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
-typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes)
 {
@@ -476,35 +249,47 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, 0x00020000);
 }
 
-__device__ __forceinline__ v4i unpack_frag_eo(v2u p)
+// -------------------------------------------------------------------------
+// Three-stage kernel (per-channel scales, M > 128, K % 128 == 0): 256 x 256
+// tile, four waves of 128 x 128 (INT32 accumulators in AGPRs), K advancing 128
+// per step.
+//   * Codes (32 KB per step) and packed weights (16 KB per step) go global ->
+//     LDS with buffer_load ... lds (no VGPR staging) into a ring of three
+//     stages (144 KB).  16-byte chunks are XOR-swizzled inside a row (codes:
+//     chunk c of row r at c ^ (r & 7), 128-byte rows; weights: chunk c of
+//     column n at c ^ ((n >> 1) & 3), 64-byte rows) so that the fragment reads
+//     spread over the banks.  The swizzle is applied on the fetch side: each
+//     lane writes a fixed LDS slot and fetches the logical chunk that belongs
+//     there.
+//   * Every byte offset, row and k included, travels in the per-lane voffset,
+//     so the buffer range check covers it: rows past M or N and k past K read
+//     as zero.
+//   * Every step waits only for its own stage (vmcnt leaves the next stage's
+//     loads in flight), meets the other waves at a bare s_barrier
+//     (__syncthreads would also wait for the loads still in flight) and then
+//     puts stage s+2 in flight before computing stage s.
+// Lane (j, q) covers k = q*32 .. q*32+31 of a step: k-substep t uses
+// k = q*32 + t*16 .. +15 for both operands (low / high half of the lane's 16
+// packed weight bytes).
+// -------------------------------------------------------------------------
+constexpr int R3_BK = 128;
+constexpr int R3_ASTAGE = BBM * R3_BK;       // 32 KB of codes
+constexpr int R3_WSTAGE = BBN * R3_BK / 2;   // 16 KB of packed weights
+constexpr int R3_LOADS = R3_ASTAGE / 4096 + R3_WSTAGE / 4096;  // per wave per stage
+
+__device__ __forceinline__ v4i r3_half(v4u p, int t)
 {
-    v4i r;
-    r[0] = (int)((p.x & 0x0f0f0f0fu) << 4);
-    r[1] = (int)(p.x & 0xf0f0f0f0u);
-    r[2] = (int)((p.y & 0x0f0f0f0fu) << 4);
-    r[3] = (int)(p.y & 0xf0f0f0f0u);
-    return r;
+    uint32_t a, b, c, d;
+    unpack16(t ? p.z : p.x, a, b);
+    unpack16(t ? p.w : p.y, c, d);
+    return (v4i){(int)a, (int)b, (int)c, (int)d};
 }
 
-__device__ __forceinline__ uint4 reorder_even_odd(v4u d)
+template <int ODT>
+__global__ __launch_bounds__(256) void w4a4_gemm_ring3_kernel(GemmArgs a, int tiles_m, int tiles_n)
 {
-    uint4 r;
-    r.x = __builtin_amdgcn_perm(d.y, d.x, 0x06040200u);  // k0 k2 k4 k6
-    r.y = __builtin_amdgcn_perm(d.y, d.x, 0x07050301u);  // k1 k3 k5 k7
-    r.z = __builtin_amdgcn_perm(d.w, d.z, 0x06040200u);  // k8 .. k14
-    r.w = __builtin_amdgcn_perm(d.w, d.z, 0x07050301u);  // k9 .. k15
-    return r;
-}
-
-constexpr int W8_EPR = 132;
-constexpr int W8_LDS = 8 * 16 * W8_EPR * 4;  // epilogue strips; >= 2 * 256 * LDR
-
-template <int ODT, bool SPLIT>
-__global__ __launch_bounds__(512) void w4a4_gemm_w8_kernel(GemmArgs a, int64_t kc, int tiles_m,
-                                                           int tiles_n)
-{
-    extern __shared__ __align__(16) int8_t smem[];
-    int8_t (*As)[BBM * LDR] = (int8_t (*)[BBM * LDR])smem;
+    __shared__ __align__(16) int8_t smem[3 * (R3_ASTAGE + R3_WSTAGE)];
+    static_assert(R3_LOADS == 12, "vmcnt immediates below assume 12 loads per stage");
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -521,240 +306,37 @@ __global__ __launch_bounds__(512) void w4a4_gemm_w8_kernel(GemmArgs a, int64_t k
     const int first_m = (tile / per_group) * GROUP_M;
     const int gsize = min(tiles_m - first_m, GROUP_M);
     const int in_g = tile - (tile / per_group) * per_group;
-    const int tm = first_m + in_g % gsize;
-    const int tn = in_g / gsize;
-
-    const int64_t m0 = (int64_t)tm * BBM, n0 = (int64_t)tn * BBN;
+    const int64_t m0 = (int64_t)(first_m + in_g % gsize) * BBM;
+    const int64_t n0 = (int64_t)(in_g / gsize) * BBN;
     const int64_t K = a.K, M = a.M, N = a.N;
-    const int64_t kbeg = (int64_t)blockIdx.z * kc;
-    const int64_t kend = min(K, kbeg + kc);
-    const int nsteps = (int)((kend - kbeg) / BK);
+    const int nsteps = (int)(K / R3_BK);
 
     const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(a.codes + m0 * K, (uint64_t)(M - m0) * K);
     const __amdgpu_buffer_rsrc_t rw_rsrc =
         make_rsrc(a.wp + n0 * (K >> 1), (uint64_t)(N - n0) * (K >> 1));
 
-    // code staging: two 16-byte chunks per thread (rows r and r + 128).  Only
-    // one lane-varying offset per operand lives in a VGPR; the row/column
-    // step between chunks and the K position go into the scalar offset.
-    const int arow = tid >> 2, ac16 = tid & 3;
-    const int aoff = (int)(arow * K + ac16 * 16);
-    const int a_step = (int)(128 * K);
-    const int lds_off = arow * LDR + ac16 * 16;
-    const int woff = (int)((wn * 128 + j) * (K >> 1) + q * 8);
-    const int w_step = (int)(16 * (K >> 1));
-
-    auto aload = [&](v4u* r, int64_t k) {
-        r[0] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, aoff, (int)k, 0);
-        r[1] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, aoff, (int)k + a_step, 0);
-    };
-    auto astore = [&](const v4u* r, int buf) {
-        *(uint4*)(&As[buf][lds_off]) = reorder_even_odd(r[0]);
-        *(uint4*)(&As[buf][lds_off + 128 * LDR]) = reorder_even_odd(r[1]);
-    };
-    auto bload = [&](v2u* dst, int64_t k) {
+    // codes: wave w fills tile rows w*64 .. w*64+63, eight rows per load; lane
+    // l writes LDS chunk (l & 7) of row (l >> 3).
+    const int a_vo = (int)((wave * 64 + (lane >> 3)) * K + (((lane & 7) ^ (lane >> 3)) * 16));
+    const int a_row8 = (int)(8 * K);
+    // weights: wave w fills tile columns w*64 .. w*64+63, sixteen per load;
+    // lane l writes chunk (l & 3) of column (l >> 2).
+    const int w_vo = (int)((wave * 64 + (lane >> 2)) * (K >> 1) + (((lane & 3) ^ ((lane >> 3) & 3)) * 16));
+    const int w_col16 = (int)(16 * (K >> 1));
+    auto issue = [&](int stage, int st) {
+        int8_t* as = smem + stage * R3_ASTAGE;
+        int8_t* ws = smem + 3 * R3_ASTAGE + stage * R3_WSTAGE;
+        const int ka = st * R3_BK, kw = st * (R3_BK / 2);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-            dst[nt] = __builtin_amdgcn_raw_buffer_load_b64(rw_rsrc, woff, (int)(k >> 1) + nt * w_step, 0);
-    };
-
-    v4i acc[4][8];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = (v4i){0, 0, 0, 0};
-
-    auto mma = [&](int buf, const v2u* w) {
-        v4i af[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            af[mt] = *(const v4i*)(&As[buf][(wm * 64 + mt * 16 + j) * LDR + q * 16]);
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            const v4i bf = unpack_frag_eo(w[nt]);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt], bf, acc[mt][nt], 0, 0, 0);
-        }
-    };
-
-    // Pipeline: codes for step s+2 are fetched during step s and written to
-    // LDS at the end of step s+1; weights for step s+1 are fetched during s.
-    // Two named register sets alternate, so no register copies (and no early
-    // waits on in-flight loads) are needed.
-    v4u ra0[2], ra1[2];
-    v2u w0[8], w1[8];
-    auto kat = [&](int st) { return kbeg + (int64_t)st * BK; };
-    if (nsteps > 0) {
-        aload(ra0, kat(0));
-        bload(w0, kat(0));
-        if (nsteps > 1) aload(ra1, kat(1));
-        astore(ra0, 0);
-    }
-    __syncthreads();
-    for (int s = 0; s < nsteps; s += 2) {
-        // even step s: A(s) in LDS buf 0, W(s) in w0, A(s+1) in ra1
-        if (s + 2 < nsteps) aload(ra0, kat(s + 2));
-        if (s + 1 < nsteps) bload(w1, kat(s + 1));
-        mma(0, w0);
-        if (s + 1 < nsteps) astore(ra1, 1);
-        __syncthreads();
-        if (s + 1 >= nsteps) break;
-        // odd step s+1: A(s+1) in LDS buf 1, W(s+1) in w1, A(s+2) in ra0
-        if (s + 3 < nsteps) aload(ra1, kat(s + 3));
-        if (s + 2 < nsteps) bload(w0, kat(s + 2));
-        mma(1, w1);
-        if (s + 2 < nsteps) astore(ra0, 0);
-        __syncthreads();
-    }
-
-    // ---- epilogue through per-wave 16 x 128 LDS strips (as in the 4-wave
-    // kernel); scales and bias are read per strip to keep registers free.
-    int* strip = (int*)smem + wave * 16 * W8_EPR;
-    const int er = lane >> 2;
-    const int ec = (lane & 3) * 32;
-    const int64_t col0 = n0 + wn * 128 + ec;
-    const bool has_bias = a.bias != nullptr;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) strip[(4 * q + r) * W8_EPR + nt * 16 + j] = acc[mt][nt][r] >> 4;
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-        const int64_t row = m0 + wm * 64 + mt * 16 + er;
-        int iv[32];
-#pragma unroll
-        for (int c4 = 0; c4 < 8; ++c4) {
-            const int4 v = *(const int4*)(strip + er * W8_EPR + ec + 4 * c4);
-            iv[4 * c4] = v.x; iv[4 * c4 + 1] = v.y; iv[4 * c4 + 2] = v.z; iv[4 * c4 + 3] = v.w;
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-        if (row >= M) continue;
-        const bool full = col0 + 32 <= N;
-        if constexpr (SPLIT) {
-#pragma unroll
-            for (int c = 0; c < 32; ++c)
-                if (col0 + c < N)
-                    atomicAdd((unsigned long long*)(a.acc64 + row * N + col0 + c),
-                              (unsigned long long)(int64_t)iv[c]);
-        } else {
-            if (a.acc_out) {
-#pragma unroll
-                for (int c = 0; c < 32; ++c)
-                    if (col0 + c < N) a.acc_out[row * N + col0 + c] = iv[c];
-            }
-            const float sa = a.sa[row];
-#pragma unroll
-            for (int c8 = 0; c8 < 4; ++c8) {
-                float o[8];
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const int64_t col = col0 + c8 * 8 + c;
-                    const int64_t cc = col < N ? col : N - 1;
-                    float t = mul_rn(mul_rn((float)iv[c8 * 8 + c], sa),
-                                     load_any_f32(a.sw_dtype, a.sw, cc));
-                    if (has_bias) t = add_rn(t, load_any_f32(a.bias_dtype, a.bias, cc));
-                    o[c] = t;
-                }
-                if constexpr (ODT == F32) {
-                    float* dst = (float*)a.out + row * N + col0 + c8 * 8;
-                    if (full && (N % 4) == 0) {
-                        *(float4*)dst = make_float4(o[0], o[1], o[2], o[3]);
-                        *(float4*)(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
-                    } else {
-#pragma unroll
-                        for (int c = 0; c < 8; ++c)
-                            if (col0 + c8 * 8 + c < N) dst[c] = o[c];
-                    }
-                } else {
-                    uint16_t* dst = (uint16_t*)a.out + row * N + col0 + c8 * 8;
-                    uint32_t pk[4];
-#pragma unroll
-                    for (int c2 = 0; c2 < 4; ++c2)
-                        pk[c2] = (uint32_t)f32_to_h<ODT>(o[2 * c2]) |
-                                 ((uint32_t)f32_to_h<ODT>(o[2 * c2 + 1]) << 16);
-                    if (full && (N % 8) == 0) {
-                        *(uint4*)dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-                    } else {
-#pragma unroll
-                        for (int c = 0; c < 8; ++c)
-                            if (col0 + c8 * 8 + c < N) dst[c] = (uint16_t)(pk[c >> 1] >> (16 * (c & 1)));
-                    }
-                }
-            }
-        }
-    }
-}
-
-// -------------------------------------------------------------------------
-// Four-wave 256 x 256 kernel, one wave per SIMD: each wave owns a 128 x 128
-// block of 8 x 8 v_mfma_i32_16x16x64_i8 tiles whose 256 INT32 accumulators
-// live in AGPRs, which halves LDS and weight traffic per MFMA compared with a
-// 64 x 128 block.  Loads are buffer loads (zero outside the operands),
-// addressed with one lane offset plus a scalar offset; codes are fetched two
-// K-steps ahead and weights one step ahead into alternating register sets
-// (the loop body covers two steps, so no register copies are needed).
-// -------------------------------------------------------------------------
-template <int ODT, bool SPLIT>
-__global__ __launch_bounds__(256) void w4a4_gemm_w4_kernel(GemmArgs a, int64_t kc, int tiles_m,
-                                                           int tiles_n)
-{
-    extern __shared__ __align__(16) int8_t smem[];
-    int8_t (*As)[BBM * LDR] = (int8_t (*)[BBM * LDR])smem;
-
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int j = lane & 15, q = lane >> 4;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    const int ntiles = tiles_m * tiles_n;
-    const int bid = blockIdx.x;
-    const int q8 = ntiles >> 3, r8 = ntiles & 7;
-    const int xcd = bid & 7, loc = bid >> 3;
-    const int tile = xcd * q8 + min(xcd, r8) + loc;
-    constexpr int GROUP_M = 8;
-    const int per_group = GROUP_M * tiles_n;
-    const int first_m = (tile / per_group) * GROUP_M;
-    const int gsize = min(tiles_m - first_m, GROUP_M);
-    const int in_g = tile - (tile / per_group) * per_group;
-    const int tm = first_m + in_g % gsize;
-    const int tn = in_g / gsize;
-
-    const int64_t m0 = (int64_t)tm * BBM, n0 = (int64_t)tn * BBN;
-    const int64_t K = a.K, M = a.M, N = a.N;
-    const int64_t kbeg = (int64_t)blockIdx.z * kc;
-    const int64_t kend = min(K, kbeg + kc);
-    const int nsteps = (int)((kend - kbeg) / BK);
-
-    const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(a.codes + m0 * K, (uint64_t)(M - m0) * K);
-    const __amdgpu_buffer_rsrc_t rw_rsrc =
-        make_rsrc(a.wp + n0 * (K >> 1), (uint64_t)(N - n0) * (K >> 1));
-
-    // codes: four 16-byte chunks per thread, rows r, r+64, r+128, r+192
-    const int arow = tid >> 2, ac16 = tid & 3;
-    const int aoff = (int)(arow * K + ac16 * 16);
-    const int a_step = (int)(64 * K);
-    const int lds_off = arow * LDR + ac16 * 16;
-    const int woff = (int)((wn * 128 + j) * (K >> 1) + q * 8);
-    const int w_step = (int)(16 * (K >> 1));
-
-    auto aload = [&](v4u* r, int64_t k) {
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra_rsrc, (__attribute__((address_space(3))) void*)(as + (wave * 64 + i * 8) * R3_BK), 16,
+                a_vo + i * a_row8 + ka, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            r[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, aoff, (int)k + i * a_step, 0);
-    };
-    auto astore = [&](const v4u* r, int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *(uint4*)(&As[buf][lds_off + i * 64 * LDR]) = reorder_even_odd(r[i]);
-    };
-    auto bload = [&](v2u* dst, int64_t k) {
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-            dst[nt] = __builtin_amdgcn_raw_buffer_load_b64(rw_rsrc, woff, (int)(k >> 1) + nt * w_step, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw_rsrc, (__attribute__((address_space(3))) void*)(ws + (wave * 64 + i * 16) * (R3_BK / 2)), 16,
+                w_vo + i * w_col16 + kw, 0, 0, 0);
     };
 
     v4i acc[8][8];
@@ -763,49 +345,58 @@ __global__ __launch_bounds__(256) void w4a4_gemm_w4_kernel(GemmArgs a, int64_t k
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = (v4i){0, 0, 0, 0};
 
-    auto mma = [&](int buf, const v2u* w) {
-        v4i bf[8];
+    // fragment offsets inside a stage
+    const int w_ro = (wn * 128 + j) * (R3_BK / 2) + ((q ^ ((j >> 1) & 3)) * 16);
+    const int a_ro = (wm * 128 + j) * R3_BK;
+    auto compute = [&](int stage) {
+        const int8_t* as = smem + stage * R3_ASTAGE;
+        const int8_t* ws = smem + 3 * R3_ASTAGE + stage * R3_WSTAGE;
+        v4u wp[8];
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) bf[nt] = unpack_frag_eo(w[nt]);
+        for (int nt = 0; nt < 8; ++nt) wp[nt] = *(const v4u*)(ws + w_ro + nt * 16 * (R3_BK / 2));
+        v4i an = *(const v4i*)(as + a_ro + (((q * 2) ^ (j & 7)) * 16));
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const v4i af = *(const v4i*)(&As[buf][(wm * 128 + mt * 16 + j) * LDR + q * 16]);
+        for (int t = 0; t < 2; ++t) {
+            v4i bf[8];
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[nt], acc[mt][nt], 0, 0, 0);
+            for (int nt = 0; nt < 8; ++nt) bf[nt] = r3_half(wp[nt], t);
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+                const v4i af = an;
+                const int b = t * 8 + mt + 1;
+                if (b < 16)
+                    an = *(const v4i*)(as + a_ro + (b & 7) * 16 * R3_BK + (((q * 2 + (b >> 3)) ^ (j & 7)) * 16));
+                
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[nt], acc[mt][nt], 0, 0, 0);
+            }
         }
     };
 
-    v4u ra0[4], ra1[4];
-    v2u w0[8], w1[8];
-    auto kat = [&](int st) { return kbeg + (int64_t)st * BK; };
-    if (nsteps > 0) {
-        aload(ra0, kat(0));
-        bload(w0, kat(0));
-        if (nsteps > 1) aload(ra1, kat(1));
-        astore(ra0, 0);
+    // Loads are issued unconditionally: stages past the end of K fall outside
+    // the buffer range (zeros) or land in a ring slot nobody reads, so the
+    // loop carries no control flow around them.
+    issue(0, 0);
+    issue(1, 1);
+    // One loop step per K step; the ring slot is picked at run time, so the
+    // accumulators stay in place across iterations.
+    int cur = 0, nxt2 = 2;
+    for (int s = 0; s < nsteps; ++s) {
+        __builtin_amdgcn_s_waitcnt(0x0f7c);  // vmcnt(12): stage s has landed
+        __builtin_amdgcn_s_barrier();
+        issue(nxt2, s + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(cur);
+        cur = cur == 2 ? 0 : cur + 1;
+        nxt2 = nxt2 == 2 ? 0 : nxt2 + 1;
     }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
-    // pairs of steps; an odd final step is peeled after the loop so the
-    // accumulators have a single loop-carried path
-    int s = 0;
-    for (; s + 1 < nsteps; s += 2) {
-        if (s + 2 < nsteps) aload(ra0, kat(s + 2));
-        bload(w1, kat(s + 1));
-        mma(0, w0);
-        astore(ra1, 1);
-        __syncthreads();
-        if (s + 3 < nsteps) aload(ra1, kat(s + 3));
-        if (s + 2 < nsteps) bload(w0, kat(s + 2));
-        mma(1, w1);
-        if (s + 2 < nsteps) astore(ra0, 0);
-        __syncthreads();
-    }
-    if (s < nsteps) mma(0, w0);
 
-    // ---- epilogue: the tile's weight scales and bias are widened to fp32 in
-    // LDS once; then per-wave 16 x 128 int32 strips go through LDS so that a
-    // lane owns 32 consecutive columns of one row (16-byte output stores).
+    // ---- epilogue: scales and bias widened in LDS; each wave writes its
+    // accumulators out as 16 x 128 strips through LDS so that every lane
+    // stores 32 consecutive outputs with 16-byte stores
     float* scol = (float*)(smem + 4 * 16 * W8_EPR * 4);
     float* bcol = scol + BBN;
     {
@@ -841,47 +432,39 @@ __global__ __launch_bounds__(256) void w4a4_gemm_w4_kernel(GemmArgs a, int64_t k
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
         if (row < M) {
-            if constexpr (SPLIT) {
+            const float sa = a.sa[row];
+            float o[32];
 #pragma unroll
-                for (int c = 0; c < 32; ++c)
-                    if (col0 + c < N)
-                        atomicAdd((unsigned long long*)(a.acc64 + row * N + col0 + c),
-                                  (unsigned long long)(int64_t)iv[c]);
-            } else {
-                const float sa = a.sa[row];
-                float o[32];
+            for (int c = 0; c < 32; ++c) {
+                float t = mul_rn(mul_rn((float)iv[c], sa), sc[c]);
+                o[c] = has_bias ? add_rn(t, bc[c]) : t;
+            }
+            if constexpr (ODT == F32) {
+                float* dst = (float*)a.out + row * N + col0;
+                if (vec_ok) {
 #pragma unroll
-                for (int c = 0; c < 32; ++c) {
-                    float t = mul_rn(mul_rn((float)iv[c], sa), sc[c]);
-                    o[c] = has_bias ? add_rn(t, bc[c]) : t;
-                }
-                if constexpr (ODT == F32) {
-                    float* dst = (float*)a.out + row * N + col0;
-                    if (vec_ok) {
-#pragma unroll
-                        for (int c4 = 0; c4 < 8; ++c4)
-                            *(float4*)(dst + 4 * c4) =
-                                make_float4(o[4 * c4], o[4 * c4 + 1], o[4 * c4 + 2], o[4 * c4 + 3]);
-                    } else {
-                        for (int c = 0; c < 32; ++c)
-                            if (col0 + c < N) dst[c] = o[c];
-                    }
+                    for (int c4 = 0; c4 < 8; ++c4)
+                        *(float4*)(dst + 4 * c4) =
+                            make_float4(o[4 * c4], o[4 * c4 + 1], o[4 * c4 + 2], o[4 * c4 + 3]);
                 } else {
-                    uint16_t* dst = (uint16_t*)a.out + row * N + col0;
-                    uint32_t pk[16];
+                    for (int c = 0; c < 32; ++c)
+                        if (col0 + c < N) dst[c] = o[c];
+                }
+            } else {
+                uint16_t* dst = (uint16_t*)a.out + row * N + col0;
+                uint32_t pk[16];
 #pragma unroll
-                    for (int c2 = 0; c2 < 16; ++c2)
-                        pk[c2] = (uint32_t)f32_to_h<ODT>(o[2 * c2]) |
-                                 ((uint32_t)f32_to_h<ODT>(o[2 * c2 + 1]) << 16);
-                    if (vec_ok) {
+                for (int c2 = 0; c2 < 16; ++c2)
+                    pk[c2] = (uint32_t)f32_to_h<ODT>(o[2 * c2]) |
+                             ((uint32_t)f32_to_h<ODT>(o[2 * c2 + 1]) << 16);
+                if (vec_ok) {
 #pragma unroll
-                        for (int c8 = 0; c8 < 4; ++c8)
-                            *(uint4*)(dst + 8 * c8) =
-                                make_uint4(pk[4 * c8], pk[4 * c8 + 1], pk[4 * c8 + 2], pk[4 * c8 + 3]);
-                    } else {
-                        for (int c = 0; c < 32; ++c)
-                            if (col0 + c < N) dst[c] = (uint16_t)(pk[c >> 1] >> (16 * (c & 1)));
-                    }
+                    for (int c8 = 0; c8 < 4; ++c8)
+                        *(uint4*)(dst + 8 * c8) =
+                            make_uint4(pk[4 * c8], pk[4 * c8 + 1], pk[4 * c8 + 2], pk[4 * c8 + 3]);
+                } else {
+                    for (int c = 0; c < 32; ++c)
+                        if (col0 + c < N) dst[c] = (uint16_t)(pk[c >> 1] >> (16 * (c & 1)));
                 }
             }
         }
@@ -910,80 +493,25 @@ __global__ void split_epilogue_kernel(GemmArgs a)
         store_any(a.out_dtype, a.out, i, t);
     }
 }
-
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
 {
     const bool aligned = (a.K % 32) == 0 && ((uintptr_t)a.codes % 16) == 0 &&
                          ((uintptr_t)a.wp % 16) == 0;
     const bool group = a.sw_group > 0;
-    const bool big = kUseBig && !group && a.lora == nullptr && a.acc_out == nullptr && a.M > 128 &&
-                     (a.K % 64) == 0 && aligned;
-    if (big && kUseFourWaveV2) {
+    // Prefill-sized layers take the 256 x 256 three-stage kernel; everything
+    // else (small M, group scales, low-rank term, INT32 export, K chunks,
+    // K not a multiple of 128, unaligned operands) the 128 x 128 kernel.
+    const bool ring3 = !group && a.lora == nullptr && a.acc_out == nullptr && a.k_chunk == 0 &&
+                       a.M > 128 && (a.K % R3_BK) == 0 && aligned;
+    if (ring3) {
         const int tm = (int)((a.M + BBM - 1) / BBM), tn = (int)((a.N + BBN - 1) / BBN);
         const unsigned nt = (unsigned)(tm * tn);
-        const int64_t kc = a.k_chunk > 0 ? a.k_chunk : a.K;
-        const unsigned gz = (unsigned)((a.K + kc - 1) / kc);
-        constexpr int epi = 4 * 16 * W8_EPR * 4 + 2 * BBN * 4;
-        constexpr int lds = epi > 2 * BBM * LDR ? epi : 2 * BBM * LDR;
-        auto go = [&](auto kern) -> hipError_t {
-            hipLaunchKernelGGL(kern, dim3(nt, 1, gz), dim3(256), lds, st, a, kc, tm, tn);
-            return hipGetLastError();
-        };
-        if (a.k_chunk > 0) {
-            hipLaunchKernelGGL(fill_zero_i64, dim3(1024), dim3(256), 0, st, a.acc64, a.M * a.N);
-            hipError_t e = go(w4a4_gemm_w4_kernel<F32, true>);
-            if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(split_epilogue_kernel, dim3(2048), dim3(256), 0, st, a);
-            return hipGetLastError();
-        }
-        if (a.out_dtype == F32) return go(w4a4_gemm_w4_kernel<F32, false>);
-        if (a.out_dtype == F16) return go(w4a4_gemm_w4_kernel<F16, false>);
-        return go(w4a4_gemm_w4_kernel<BF16, false>);
-    }
-    if (big && kUseEightWave) {
-        const int tm = (int)((a.M + BBM - 1) / BBM), tn = (int)((a.N + BBN - 1) / BBN);
-        const unsigned nt = (unsigned)(tm * tn);
-        const int64_t kc = a.k_chunk > 0 ? a.k_chunk : a.K;
-        const unsigned gz = (unsigned)((a.K + kc - 1) / kc);
-        auto go = [&](auto kern) -> hipError_t {
-            hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, W8_LDS);
-            if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(kern, dim3(nt, 1, gz), dim3(512), W8_LDS, st, a, kc, tm, tn);
-            return hipGetLastError();
-        };
-        hipError_t e;
-        if (a.k_chunk > 0) {
-            hipLaunchKernelGGL(fill_zero_i64, dim3(1024), dim3(256), 0, st, a.acc64, a.M * a.N);
-            e = go(w4a4_gemm_w8_kernel<F32, true>);
-            if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(split_epilogue_kernel, dim3(2048), dim3(256), 0, st, a);
-            return hipGetLastError();
-        }
-        if (a.out_dtype == F32) return go(w4a4_gemm_w8_kernel<F32, false>);
-        if (a.out_dtype == F16) return go(w4a4_gemm_w8_kernel<F16, false>);
-        return go(w4a4_gemm_w8_kernel<BF16, false>);
-    }
-    if (big) {
-        const int tm = (int)((a.M + BBM - 1) / BBM), tn = (int)((a.N + BBN - 1) / BBN);
-        const unsigned nt = (unsigned)(tm * tn);
-        if (a.k_chunk > 0) {
-            const int64_t kc = a.k_chunk;
-            const unsigned gz = (unsigned)((a.K + kc - 1) / kc);
-            hipLaunchKernelGGL(fill_zero_i64, dim3(1024), dim3(256), 0, st, a.acc64, a.M * a.N);
-            hipLaunchKernelGGL((w4a4_gemm_big_kernel<F32, true>), dim3(nt, 1, gz), dim3(256), 0, st,
-                               a, kc, tm, tn);
-            hipLaunchKernelGGL(split_epilogue_kernel, dim3(2048), dim3(256), 0, st, a);
-        } else if (a.out_dtype == F32) {
-            hipLaunchKernelGGL((w4a4_gemm_big_kernel<F32, false>), dim3(nt, 1, 1), dim3(256), 0, st,
-                               a, a.K, tm, tn);
-        } else if (a.out_dtype == F16) {
-            hipLaunchKernelGGL((w4a4_gemm_big_kernel<F16, false>), dim3(nt, 1, 1), dim3(256), 0, st,
-                               a, a.K, tm, tn);
-        } else {
-            hipLaunchKernelGGL((w4a4_gemm_big_kernel<BF16, false>), dim3(nt, 1, 1), dim3(256), 0, st,
-                               a, a.K, tm, tn);
-        }
+        if (a.out_dtype == F32)
+            hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<F32>, dim3(nt), dim3(256), 0, st, a, tm, tn);
+        else if (a.out_dtype == F16)
+            hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<F16>, dim3(nt), dim3(256), 0, st, a, tm, tn);
+        else
+            hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<BF16>, dim3(nt), dim3(256), 0, st, a, tm, tn);
         return hipGetLastError();
     }
     const unsigned gx = (unsigned)((a.N + BN - 1) / BN);

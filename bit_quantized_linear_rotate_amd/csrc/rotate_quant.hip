@@ -610,7 +610,7 @@ __global__ __launch_bounds__(256) void rq_reg_kernel(
 // row-block are in flight while the current one is rotated and quantized.
 // -------------------------------------------------------------------------
 template <int DT, int GP, bool ROT, bool SMOOTH, int TW>
-__global__ __launch_bounds__(256, 3) void rq_wave_kernel(
+__global__ __launch_bounds__(256, TW >= 4 ? 2 : 3) void rq_wave_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t sm,
     const float* __restrict__ rot, int g, const uint16_t* __restrict__ smooth,
     int8_t* __restrict__ codes, float* __restrict__ scales, uint16_t* __restrict__ yout, int rpb)
@@ -842,10 +842,9 @@ __global__ __launch_bounds__(256, 3) void rq_wave_kernel(
         }
     };
 
-    // With up to two tiles per wave the next row-block's loads are issued
-    // before the current one is processed (the register copy afterwards finds
-    // them arrived); with four, registers go to occupancy instead.
-    constexpr bool PF = TW <= 2;
+    // The next row-block's loads are issued before the current one is
+    // processed (the register copy afterwards finds them arrived).
+    constexpr bool PF = true;
     v8s xa[TW][NV], xb[PF ? TW : 1][NV];
     load_blk(wid, xa);
     for (int64_t blk = wid; blk < nblk; blk += nwaves) {
