@@ -251,8 +251,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // -------------------------------------------------------------------------
 // Three-stage kernel (per-channel scales, M > 128, K % 128 == 0): 256 x 256
-// tile, four waves of 128 x 128 (INT32 accumulators in AGPRs), K advancing 128
-// per step.
+// tile per 512-thread workgroup, eight waves in 4 (M) x 2 (N), two per SIMD,
+// each a 64 x 128 block of 4 x 8 v_mfma_i32_16x16x64_i8 tiles with its 128
+// INT32 accumulators in VGPRs; K advances 128 per step.
 //   * Codes (32 KB per step) and packed weights (16 KB per step) go global ->
 //     LDS with buffer_load ... lds (no VGPR staging) into a ring of three
 //     stages (144 KB).  16-byte chunks are XOR-swizzled inside a row (codes:
@@ -268,6 +269,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 //     loads in flight), meets the other waves at a bare s_barrier
 //     (__syncthreads would also wait for the loads still in flight) and then
 //     puts stage s+2 in flight before computing stage s.
+//   * Two waves per SIMD keep the matrix core busy while the other waits on
+//     LDS or the barrier; with at most 256 registers per lane the compiler
+//     keeps the accumulators in VGPRs, where every MFMA updates its
+//     accumulator in place.
 // Lane (j, q) covers k = q*32 .. q*32+31 of a step: k-substep t uses
 // k = q*32 + t*16 .. +15 for both operands (low / high half of the lane's 16
 // packed weight bytes).
@@ -275,7 +280,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 constexpr int R3_BK = 128;
 constexpr int R3_ASTAGE = BBM * R3_BK;       // 32 KB of codes
 constexpr int R3_WSTAGE = BBN * R3_BK / 2;   // 16 KB of packed weights
-constexpr int R3_LOADS = R3_ASTAGE / 4096 + R3_WSTAGE / 4096;  // per wave per stage
+constexpr int R3_WAVES = 8;
+constexpr int R3_ALOADS = R3_ASTAGE / 1024 / R3_WAVES;  // 1 KB per load: 4 per wave
+constexpr int R3_WLOADS = R3_WSTAGE / 1024 / R3_WAVES;  // 2 per wave
 
 __device__ __forceinline__ v4i r3_half(v4u p, int t)
 {
@@ -286,15 +293,15 @@ __device__ __forceinline__ v4i r3_half(v4u p, int t)
 }
 
 template <int ODT>
-__global__ __launch_bounds__(256) void w4a4_gemm_ring3_kernel(GemmArgs a, int tiles_m, int tiles_n)
+__global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int tiles_m, int tiles_n)
 {
     __shared__ __align__(16) int8_t smem[3 * (R3_ASTAGE + R3_WSTAGE)];
-    static_assert(R3_LOADS == 12, "vmcnt immediates below assume 12 loads per stage");
+    static_assert(R3_ALOADS + R3_WLOADS == 6, "vmcnt immediates below assume 6 loads per stage");
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, q = lane >> 4;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 1, wn = wave & 1;  // 64-row block wm, 128-column block wn
 
     const int ntiles = tiles_m * tiles_n;
     const int bid = blockIdx.x;
@@ -315,58 +322,62 @@ __global__ __launch_bounds__(256) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
     const __amdgpu_buffer_rsrc_t rw_rsrc =
         make_rsrc(a.wp + n0 * (K >> 1), (uint64_t)(N - n0) * (K >> 1));
 
-    // codes: wave w fills tile rows w*64 .. w*64+63, eight rows per load; lane
+    // codes: wave w fills tile rows w*32 .. w*32+31, eight rows per load; lane
     // l writes LDS chunk (l & 7) of row (l >> 3).
-    const int a_vo = (int)((wave * 64 + (lane >> 3)) * K + (((lane & 7) ^ (lane >> 3)) * 16));
+    const int a_vo = (int)((wave * 32 + (lane >> 3)) * K + (((lane & 7) ^ (lane >> 3)) * 16));
     const int a_row8 = (int)(8 * K);
-    // weights: wave w fills tile columns w*64 .. w*64+63, sixteen per load;
+    // weights: wave w fills tile columns w*32 .. w*32+31, sixteen per load;
     // lane l writes chunk (l & 3) of column (l >> 2).
-    const int w_vo = (int)((wave * 64 + (lane >> 2)) * (K >> 1) + (((lane & 3) ^ ((lane >> 3) & 3)) * 16));
+    const int w_vo = (int)((wave * 32 + (lane >> 2)) * (K >> 1) + (((lane & 3) ^ ((lane >> 3) & 3)) * 16));
     const int w_col16 = (int)(16 * (K >> 1));
     auto issue = [&](int stage, int st) {
         int8_t* as = smem + stage * R3_ASTAGE;
         int8_t* ws = smem + 3 * R3_ASTAGE + stage * R3_WSTAGE;
         const int ka = st * R3_BK, kw = st * (R3_BK / 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < R3_ALOADS; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra_rsrc, (__attribute__((address_space(3))) void*)(as + (wave * 64 + i * 8) * R3_BK), 16,
+                ra_rsrc, (__attribute__((address_space(3))) void*)(as + (wave * 32 + i * 8) * R3_BK), 16,
                 a_vo + i * a_row8 + ka, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < R3_WLOADS; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw_rsrc, (__attribute__((address_space(3))) void*)(ws + (wave * 64 + i * 16) * (R3_BK / 2)), 16,
+                rw_rsrc, (__attribute__((address_space(3))) void*)(ws + (wave * 32 + i * 16) * (R3_BK / 2)), 16,
                 w_vo + i * w_col16 + kw, 0, 0, 0);
     };
 
-    v4i acc[8][8];
+    v4i acc[4][8];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = (v4i){0, 0, 0, 0};
 
     // fragment offsets inside a stage
     const int w_ro = (wn * 128 + j) * (R3_BK / 2) + ((q ^ ((j >> 1) & 3)) * 16);
-    const int a_ro = (wm * 128 + j) * R3_BK;
+    const int a_ro = (wm * 64 + j) * R3_BK;
+    // One step: the weight fragments, then the code fragment of each
+    // (substep, row block) one block ahead of its eight MFMAs.
     auto compute = [&](int stage) {
-        const int8_t* as = smem + stage * R3_ASTAGE;
-        const int8_t* ws = smem + 3 * R3_ASTAGE + stage * R3_WSTAGE;
+        const int8_t* as = smem + stage * R3_ASTAGE + a_ro;
+        const int8_t* ws = smem + 3 * R3_ASTAGE + stage * R3_WSTAGE + w_ro;
+        auto afrag = [&](int b) {  // block b = t*4 + mt
+            const int t = b >> 2, mt = b & 3;
+            return *(const v4i*)(as + mt * 16 * R3_BK + (((q * 2 + t) ^ (j & 7)) * 16));
+        };
         v4u wp[8];
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) wp[nt] = *(const v4u*)(ws + w_ro + nt * 16 * (R3_BK / 2));
-        v4i an = *(const v4i*)(as + a_ro + (((q * 2) ^ (j & 7)) * 16));
+        for (int nt = 0; nt < 8; ++nt) wp[nt] = *(const v4u*)(ws + nt * 16 * (R3_BK / 2));
+        v4i an = afrag(0);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             v4i bf[8];
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) bf[nt] = r3_half(wp[nt], t);
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
+            for (int mt = 0; mt < 4; ++mt) {
                 const v4i af = an;
-                const int b = t * 8 + mt + 1;
-                if (b < 16)
-                    an = *(const v4i*)(as + a_ro + (b & 7) * 16 * R3_BK + (((q * 2 + (b >> 3)) ^ (j & 7)) * 16));
-                
+                const int b = t * 4 + mt + 1;
+                if (b < 8) an = afrag(b);
 #pragma unroll
                 for (int nt = 0; nt < 8; ++nt)
                     acc[mt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[nt], acc[mt][nt], 0, 0, 0);
@@ -383,7 +394,7 @@ __global__ __launch_bounds__(256) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
     // accumulators stay in place across iterations.
     int cur = 0, nxt2 = 2;
     for (int s = 0; s < nsteps; ++s) {
-        __builtin_amdgcn_s_waitcnt(0x0f7c);  // vmcnt(12): stage s has landed
+        __builtin_amdgcn_s_waitcnt(0x0f76);  // vmcnt(6): stage s has landed
         __builtin_amdgcn_s_barrier();
         issue(nxt2, s + 2);
         __builtin_amdgcn_sched_barrier(0);
@@ -397,13 +408,14 @@ __global__ __launch_bounds__(256) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
     // ---- epilogue: scales and bias widened in LDS; each wave writes its
     // accumulators out as 16 x 128 strips through LDS so that every lane
     // stores 32 consecutive outputs with 16-byte stores
-    float* scol = (float*)(smem + 4 * 16 * W8_EPR * 4);
+    float* scol = (float*)(smem + R3_WAVES * 16 * W8_EPR * 4);
     float* bcol = scol + BBN;
     {
-        const int64_t col = n0 + tid;
+        const int c = tid & (BBN - 1);
+        const int64_t col = n0 + c;
         const int64_t cc = col < N ? col : N - 1;
-        scol[tid] = load_any_f32(a.sw_dtype, a.sw, cc);
-        bcol[tid] = a.bias ? load_any_f32(a.bias_dtype, a.bias, cc) : 0.0f;
+        if (tid < BBN) scol[c] = load_any_f32(a.sw_dtype, a.sw, cc);
+        else bcol[c] = a.bias ? load_any_f32(a.bias_dtype, a.bias, cc) : 0.0f;
     }
     __syncthreads();
     int* strip = (int*)smem + wave * 16 * W8_EPR;
@@ -415,14 +427,14 @@ __global__ __launch_bounds__(256) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
     const bool has_bias = a.bias != nullptr;
     const bool vec_ok = (col0 + 32 <= N) && (N % 8) == 0;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
+    for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) strip[(4 * q + r) * W8_EPR + nt * 16 + j] = acc[mt][nt][r] >> 4;
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
-        const int64_t row = m0 + wm * 128 + mt * 16 + er;
+        const int64_t row = m0 + wm * 64 + mt * 16 + er;
         int iv[32];
 #pragma unroll
         for (int c4 = 0; c4 < 8; ++c4) {
@@ -507,11 +519,11 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
         const int tm = (int)((a.M + BBM - 1) / BBM), tn = (int)((a.N + BBN - 1) / BBN);
         const unsigned nt = (unsigned)(tm * tn);
         if (a.out_dtype == F32)
-            hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<F32>, dim3(nt), dim3(256), 0, st, a, tm, tn);
+            hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<F32>, dim3(nt), dim3(512), 0, st, a, tm, tn);
         else if (a.out_dtype == F16)
-            hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<F16>, dim3(nt), dim3(256), 0, st, a, tm, tn);
+            hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<F16>, dim3(nt), dim3(512), 0, st, a, tm, tn);
         else
-            hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<BF16>, dim3(nt), dim3(256), 0, st, a, tm, tn);
+            hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<BF16>, dim3(nt), dim3(512), 0, st, a, tm, tn);
         return hipGetLastError();
     }
     const unsigned gx = (unsigned)((a.N + BN - 1) / BN);
