@@ -239,7 +239,6 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
 
 
 constexpr int BBM = 256, BBN = 256;
-constexpr int W8_EPR = 132;  // epilogue strip row, words (128 + 4 pad)
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
@@ -250,21 +249,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // -------------------------------------------------------------------------
-// Three-stage kernel (per-channel scales, M > 128, K % 128 == 0): 256 x 256
-// tile per 512-thread workgroup, eight waves in 4 (M) x 2 (N), two per SIMD,
-// each a 64 x 128 block of 4 x 8 v_mfma_i32_16x16x64_i8 tiles with its 128
-// INT32 accumulators in VGPRs; K advances 128 per step.
+// Three-stage persistent kernel (per-channel scales, M > 128, K % 128 == 0):
+// one 512-thread workgroup per CU walks its 256 x 256 output tiles; eight
+// waves in 2 (M) x 4 (N), two per SIMD, each a 128 x 64 block of 8 x 4
+// v_mfma_i32_16x16x64_i8 tiles with its 128 INT32 accumulators in VGPRs; K
+// advances 128 per step.
 //   * Codes (32 KB per step) and packed weights (16 KB per step) go global ->
 //     LDS with buffer_load ... lds (no VGPR staging) into a ring of three
-//     stages (144 KB).  16-byte chunks are XOR-swizzled inside a row (codes:
-//     chunk c of row r at c ^ (r & 7), 128-byte rows; weights: chunk c of
-//     column n at c ^ ((n >> 1) & 3), 64-byte rows) so that the fragment reads
-//     spread over the banks.  The swizzle is applied on the fetch side: each
-//     lane writes a fixed LDS slot and fetches the logical chunk that belongs
-//     there.
+//     48 KB slots.  The ring runs across tiles: the last two steps of a tile
+//     fetch the first two stages of the workgroup's next tile, and the
+//     epilogue of a tile works in the slot its last step freed, so output
+//     stores overlap the next tile's loads.
+//   * Codes are stored fragment-major: one 1 KB block per (16-row block,
+//     k-substep) holding lane l's 16-byte MFMA operand at l * 16, so every
+//     fragment read is a linear, conflict-free ds_read_b128.  Each fetch lane
+//     gathers the 16 bytes that its LDS slot needs.
+//   * Packed weights keep their 64-byte rows (one per output column), 16-byte
+//     chunk c of column n stored at c ^ ((n >> 1) & 3), which spreads a
+//     fragment read over all banks.
 //   * Every byte offset, row and k included, travels in the per-lane voffset,
 //     so the buffer range check covers it: rows past M or N and k past K read
-//     as zero.
+//     as zero, and a missing next tile is a zero-sized buffer.
 //   * Every step waits only for its own stage (vmcnt leaves the next stage's
 //     loads in flight), meets the other waves at a bare s_barrier
 //     (__syncthreads would also wait for the loads still in flight) and then
@@ -272,7 +277,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 //   * Two waves per SIMD keep the matrix core busy while the other waits on
 //     LDS or the barrier; with at most 256 registers per lane the compiler
 //     keeps the accumulators in VGPRs, where every MFMA updates its
-//     accumulator in place.
+//     accumulator in place.  A 64-column block per wave keeps the nibble
+//     unpacking (VALU) at four weight fragments per step.
+//   * Tiles are numbered so that each XCD (workgroups are dealt round-robin
+//     over 8, and the grid is a multiple of 8) owns a contiguous, M-grouped
+//     range of tiles.
 // Lane (j, q) covers k = q*32 .. q*32+31 of a step: k-substep t uses
 // k = q*32 + t*16 .. +15 for both operands (low / high half of the lane's 16
 // packed weight bytes).
@@ -280,9 +289,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 constexpr int R3_BK = 128;
 constexpr int R3_ASTAGE = BBM * R3_BK;       // 32 KB of codes
 constexpr int R3_WSTAGE = BBN * R3_BK / 2;   // 16 KB of packed weights
+constexpr int R3_SLOT = R3_ASTAGE + R3_WSTAGE;
 constexpr int R3_WAVES = 8;
 constexpr int R3_ALOADS = R3_ASTAGE / 1024 / R3_WAVES;  // 1 KB per load: 4 per wave
 constexpr int R3_WLOADS = R3_WSTAGE / 1024 / R3_WAVES;  // 2 per wave
+constexpr int R3_EPR = 68;  // epilogue strip row in words (64 + 4 pad)
+static_assert(R3_WAVES * 16 * R3_EPR * 4 + 2 * BBN * 4 <= R3_SLOT, "epilogue must fit in one slot");
 
 __device__ __forceinline__ v4i r3_half(v4u p, int t)
 {
@@ -292,195 +304,223 @@ __device__ __forceinline__ v4i r3_half(v4u p, int t)
     return (v4i){(int)a, (int)b, (int)c, (int)d};
 }
 
+struct R3Tile {
+    int64_t m0, n0;
+    __amdgpu_buffer_rsrc_t ra, rw;
+};
+
+__device__ __forceinline__ R3Tile r3_tile(const GemmArgs& a, int t, int ntiles, int tiles_n)
+{
+    R3Tile r;
+    if (t >= ntiles) {  // no such tile: zero-sized buffers, every load reads zero
+        r.m0 = 0; r.n0 = 0;
+        r.ra = make_rsrc(a.codes, 0);
+        r.rw = make_rsrc(a.wp, 0);
+        return r;
+    }
+    const int q8 = ntiles >> 3, r8 = ntiles & 7;
+    const int xcd = t & 7, loc = t >> 3;
+    const int tile = xcd * q8 + min(xcd, r8) + loc;
+    constexpr int GROUP_M = 8;
+    const int tiles_m = ntiles / tiles_n;
+    const int per_group = GROUP_M * tiles_n;
+    const int first_m = (tile / per_group) * GROUP_M;
+    const int gsize = min(tiles_m - first_m, GROUP_M);
+    const int in_g = tile - (tile / per_group) * per_group;
+    r.m0 = (int64_t)(first_m + in_g % gsize) * BBM;
+    r.n0 = (int64_t)(in_g / gsize) * BBN;
+    r.ra = make_rsrc(a.codes + r.m0 * a.K, (uint64_t)(a.M - r.m0) * a.K);
+    r.rw = make_rsrc(a.wp + r.n0 * (a.K >> 1), (uint64_t)(a.N - r.n0) * (a.K >> 1));
+    return r;
+}
+
 template <int ODT>
 __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int tiles_m, int tiles_n)
 {
-    __shared__ __align__(16) int8_t smem[3 * (R3_ASTAGE + R3_WSTAGE)];
+    __shared__ __align__(16) int8_t smem[3 * R3_SLOT];
     static_assert(R3_ALOADS + R3_WLOADS == 6, "vmcnt immediates below assume 6 loads per stage");
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, q = lane >> 4;
-    const int wm = wave >> 1, wn = wave & 1;  // 64-row block wm, 128-column block wn
+    const int wm = wave & 1, wn = wave >> 1;  // 128-row block wm, 64-column block wn
 
     const int ntiles = tiles_m * tiles_n;
-    const int bid = blockIdx.x;
-    const int q8 = ntiles >> 3, r8 = ntiles & 7;
-    const int xcd = bid & 7, loc = bid >> 3;
-    const int tile = xcd * q8 + min(xcd, r8) + loc;
-    constexpr int GROUP_M = 8;
-    const int per_group = GROUP_M * tiles_n;
-    const int first_m = (tile / per_group) * GROUP_M;
-    const int gsize = min(tiles_m - first_m, GROUP_M);
-    const int in_g = tile - (tile / per_group) * per_group;
-    const int64_t m0 = (int64_t)(first_m + in_g % gsize) * BBM;
-    const int64_t n0 = (int64_t)(in_g / gsize) * BBN;
     const int64_t K = a.K, M = a.M, N = a.N;
     const int nsteps = (int)(K / R3_BK);
+    int t = blockIdx.x;
+    const int G = gridDim.x;
 
-    const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(a.codes + m0 * K, (uint64_t)(M - m0) * K);
-    const __amdgpu_buffer_rsrc_t rw_rsrc =
-        make_rsrc(a.wp + n0 * (K >> 1), (uint64_t)(N - n0) * (K >> 1));
-
-    // codes: wave w fills tile rows w*32 .. w*32+31, eight rows per load; lane
-    // l writes LDS chunk (l & 7) of row (l >> 3).
-    const int a_vo = (int)((wave * 32 + (lane >> 3)) * K + (((lane & 7) ^ (lane >> 3)) * 16));
-    const int a_row8 = (int)(8 * K);
+    // codes: block b = 2 * (16-row block) + substep; wave w fills blocks
+    // w*4 .. w*4+3; lane l of a block holds row (l & 15), k-chunk 2*(l >> 4) + t.
+    const int a_vo = (int)(j * K + q * 32);
+    const int a_rb = (int)(16 * K);
     // weights: wave w fills tile columns w*32 .. w*32+31, sixteen per load;
     // lane l writes chunk (l & 3) of column (l >> 2).
     const int w_vo = (int)((wave * 32 + (lane >> 2)) * (K >> 1) + (((lane & 3) ^ ((lane >> 3) & 3)) * 16));
     const int w_col16 = (int)(16 * (K >> 1));
-    auto issue = [&](int stage, int st) {
-        int8_t* as = smem + stage * R3_ASTAGE;
-        int8_t* ws = smem + 3 * R3_ASTAGE + stage * R3_WSTAGE;
+    auto issue = [&](int slot, const __amdgpu_buffer_rsrc_t& ra, const __amdgpu_buffer_rsrc_t& rw, int st) {
+        int8_t* as = smem + slot * R3_SLOT;
+        int8_t* ws = as + R3_ASTAGE;
         const int ka = st * R3_BK, kw = st * (R3_BK / 2);
 #pragma unroll
-        for (int i = 0; i < R3_ALOADS; ++i)
+        for (int i = 0; i < R3_ALOADS; ++i) {
+            const int blk = wave * R3_ALOADS + i;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra_rsrc, (__attribute__((address_space(3))) void*)(as + (wave * 32 + i * 8) * R3_BK), 16,
-                a_vo + i * a_row8 + ka, 0, 0, 0);
+                ra, (__attribute__((address_space(3))) void*)(as + blk * 1024), 16,
+                a_vo + (blk >> 1) * a_rb + (blk & 1) * 16 + ka, 0, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < R3_WLOADS; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw_rsrc, (__attribute__((address_space(3))) void*)(ws + (wave * 32 + i * 16) * (R3_BK / 2)), 16,
+                rw, (__attribute__((address_space(3))) void*)(ws + (wave * 32 + i * 16) * (R3_BK / 2)), 16,
                 w_vo + i * w_col16 + kw, 0, 0, 0);
     };
 
-    v4i acc[4][8];
+    v4i acc[8][4];
+    // fragment offsets inside a slot
+    const int w_ro = R3_ASTAGE + (wn * 64 + j) * (R3_BK / 2) + ((q ^ ((j >> 1) & 3)) * 16);
+    const int a_ro = wm * 8 * 2 * 1024 + lane * 16;
+    // One step: the weight fragments and the code fragments of substep 0,
+    // then those of substep 1 while substep 0 multiplies.
+    auto compute = [&](int slot) {
+        const int8_t* as = smem + slot * R3_SLOT + a_ro;
+        const int8_t* ws = smem + slot * R3_SLOT + w_ro;
+        v4u wp[4];
+        v4i af[2][8];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+        for (int nt = 0; nt < 4; ++nt) wp[nt] = *(const v4u*)(ws + nt * 16 * (R3_BK / 2));
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = (v4i){0, 0, 0, 0};
-
-    // fragment offsets inside a stage
-    const int w_ro = (wn * 128 + j) * (R3_BK / 2) + ((q ^ ((j >> 1) & 3)) * 16);
-    const int a_ro = (wm * 64 + j) * R3_BK;
-    // One step: the weight fragments, then the code fragment of each
-    // (substep, row block) one block ahead of its eight MFMAs.
-    auto compute = [&](int stage) {
-        const int8_t* as = smem + stage * R3_ASTAGE + a_ro;
-        const int8_t* ws = smem + 3 * R3_ASTAGE + stage * R3_WSTAGE + w_ro;
-        auto afrag = [&](int b) {  // block b = t*4 + mt
-            const int t = b >> 2, mt = b & 3;
-            return *(const v4i*)(as + mt * 16 * R3_BK + (((q * 2 + t) ^ (j & 7)) * 16));
-        };
-        v4u wp[8];
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) wp[nt] = *(const v4u*)(ws + nt * 16 * (R3_BK / 2));
-        v4i an = afrag(0);
+            for (int mt = 0; mt < 8; ++mt) af[tt][mt] = *(const v4i*)(as + (mt * 2 + tt) * 1024);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            v4i bf[8];
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) bf[nt] = r3_half(wp[nt], t);
+            for (int nt = 0; nt < 4; ++nt) {
+                const v4i bf = r3_half(wp[nt], tt);
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const v4i af = an;
-                const int b = t * 4 + mt + 1;
-                if (b < 8) an = afrag(b);
-#pragma unroll
-                for (int nt = 0; nt < 8; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[nt], acc[mt][nt], 0, 0, 0);
+                for (int mt = 0; mt < 8; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[tt][mt], bf, acc[mt][nt], 0, 0, 0);
             }
-        }
     };
 
-    // Loads are issued unconditionally: stages past the end of K fall outside
-    // the buffer range (zeros) or land in a ring slot nobody reads, so the
-    // loop carries no control flow around them.
-    issue(0, 0);
-    issue(1, 1);
-    // One loop step per K step; the ring slot is picked at run time, so the
-    // accumulators stay in place across iterations.
+    R3Tile cur_t = r3_tile(a, t, ntiles, tiles_n);
+    R3Tile nxt_t = r3_tile(a, t + G, ntiles, tiles_n);
+    // Loads are issued unconditionally: stages past the end of a tile belong
+    // to the next tile (or read zeros when there is none), so the loop carries
+    // no control flow around them.
+    issue(0, cur_t.ra, cur_t.rw, 0);
+    issue(1, cur_t.ra, cur_t.rw, 1);
     int cur = 0, nxt2 = 2;
-    for (int s = 0; s < nsteps; ++s) {
-        __builtin_amdgcn_s_waitcnt(0x0f76);  // vmcnt(6): stage s has landed
-        __builtin_amdgcn_s_barrier();
-        issue(nxt2, s + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(cur);
-        cur = cur == 2 ? 0 : cur + 1;
-        nxt2 = nxt2 == 2 ? 0 : nxt2 + 1;
-    }
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-    __syncthreads();
+    for (;;) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = (v4i){0, 0, 0, 0};
+        for (int s = 0; s < nsteps; ++s) {
+            __builtin_amdgcn_s_waitcnt(0x0f76);  // vmcnt(6): stage s has landed
+            __builtin_amdgcn_s_barrier();
+            const bool same = s + 2 < nsteps;
+            issue(nxt2, same ? cur_t.ra : nxt_t.ra, same ? cur_t.rw : nxt_t.rw,
+                  same ? s + 2 : s + 2 - nsteps);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(cur);
+            cur = cur == 2 ? 0 : cur + 1;
+            nxt2 = nxt2 == 2 ? 0 : nxt2 + 1;
+        }
 
-    // ---- epilogue: scales and bias widened in LDS; each wave writes its
-    // accumulators out as 16 x 128 strips through LDS so that every lane
-    // stores 32 consecutive outputs with 16-byte stores
-    float* scol = (float*)(smem + R3_WAVES * 16 * W8_EPR * 4);
-    float* bcol = scol + BBN;
-    {
-        const int c = tid & (BBN - 1);
-        const int64_t col = n0 + c;
-        const int64_t cc = col < N ? col : N - 1;
-        if (tid < BBN) scol[c] = load_any_f32(a.sw_dtype, a.sw, cc);
-        else bcol[c] = a.bias ? load_any_f32(a.bias_dtype, a.bias, cc) : 0.0f;
-    }
-    __syncthreads();
-    int* strip = (int*)smem + wave * 16 * W8_EPR;
-    const int er = lane >> 2;
-    const int ec = (lane & 3) * 32;
-    const int64_t col0 = n0 + wn * 128 + ec;
-    const float* sc = scol + wn * 128 + ec;
-    const float* bc = bcol + wn * 128 + ec;
-    const bool has_bias = a.bias != nullptr;
-    const bool vec_ok = (col0 + 32 <= N) && (N % 8) == 0;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) strip[(4 * q + r) * W8_EPR + nt * 16 + j] = acc[mt][nt][r] >> 4;
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-        const int64_t row = m0 + wm * 64 + mt * 16 + er;
-        int iv[32];
-#pragma unroll
-        for (int c4 = 0; c4 < 8; ++c4) {
-            const int4 v = *(const int4*)(strip + er * W8_EPR + ec + 4 * c4);
-            iv[4 * c4] = v.x; iv[4 * c4 + 1] = v.y; iv[4 * c4 + 2] = v.z; iv[4 * c4 + 3] = v.w;
+        // ---- epilogue in the slot the last step used (every wave has left it
+        // after the barrier below); the next tile's first two stages are
+        // already in flight into the other two.  Scales and bias are widened
+        // in LDS; each wave writes its accumulators out as 16 x 64 strips so
+        // that every lane stores 16 consecutive outputs with 16-byte stores.
+        int8_t* eslot = smem + nxt2 * R3_SLOT;  // == slot of the step just computed
+        __builtin_amdgcn_s_barrier();
+        float* scol = (float*)(eslot + R3_WAVES * 16 * R3_EPR * 4);
+        float* bcol = scol + BBN;
+        const int64_t m0 = cur_t.m0, n0 = cur_t.n0;
+        {
+            const int c = tid & (BBN - 1);
+            const int64_t col = n0 + c;
+            const int64_t cc = col < N ? col : N - 1;
+            if (tid < BBN) scol[c] = load_any_f32(a.sw_dtype, a.sw, cc);
+            else bcol[c] = a.bias ? load_any_f32(a.bias_dtype, a.bias, cc) : 0.0f;
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-        if (row < M) {
-            const float sa = a.sa[row];
-            float o[32];
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS writes done
+        __builtin_amdgcn_s_barrier();
+        int* strip = (int*)eslot + wave * 16 * R3_EPR;
+        const int er = lane >> 2;
+        const int ec = (lane & 3) * 16;
+        const int64_t col0 = n0 + wn * 64 + ec;
+        const float* sc = scol + wn * 64 + ec;
+        const float* bc = bcol + wn * 64 + ec;
+        const bool has_bias = a.bias != nullptr;
+        const bool vec_ok = (col0 + 16 <= N) && (N % 8) == 0;
 #pragma unroll
-            for (int c = 0; c < 32; ++c) {
-                float t = mul_rn(mul_rn((float)iv[c], sa), sc[c]);
-                o[c] = has_bias ? add_rn(t, bc[c]) : t;
+        for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) strip[(4 * q + r) * R3_EPR + nt * 16 + j] = acc[mt][nt][r] >> 4;
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            const int64_t row = m0 + wm * 128 + mt * 16 + er;
+            int iv[16];
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const int4 v = *(const int4*)(strip + er * R3_EPR + ec + 4 * c4);
+                iv[4 * c4] = v.x; iv[4 * c4 + 1] = v.y; iv[4 * c4 + 2] = v.z; iv[4 * c4 + 3] = v.w;
             }
-            if constexpr (ODT == F32) {
-                float* dst = (float*)a.out + row * N + col0;
-                if (vec_ok) {
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            if (row < M) {
+                const float sa = a.sa[row];
+                float o[16];
 #pragma unroll
-                    for (int c4 = 0; c4 < 8; ++c4)
-                        *(float4*)(dst + 4 * c4) =
-                            make_float4(o[4 * c4], o[4 * c4 + 1], o[4 * c4 + 2], o[4 * c4 + 3]);
-                } else {
-                    for (int c = 0; c < 32; ++c)
-                        if (col0 + c < N) dst[c] = o[c];
+                for (int c = 0; c < 16; ++c) {
+                    float tv = mul_rn(mul_rn((float)iv[c], sa), sc[c]);
+                    o[c] = has_bias ? add_rn(tv, bc[c]) : tv;
                 }
-            } else {
-                uint16_t* dst = (uint16_t*)a.out + row * N + col0;
-                uint32_t pk[16];
+                if constexpr (ODT == F32) {
+                    float* dst = (float*)a.out + row * N + col0;
+                    if (vec_ok) {
 #pragma unroll
-                for (int c2 = 0; c2 < 16; ++c2)
-                    pk[c2] = (uint32_t)f32_to_h<ODT>(o[2 * c2]) |
-                             ((uint32_t)f32_to_h<ODT>(o[2 * c2 + 1]) << 16);
-                if (vec_ok) {
-#pragma unroll
-                    for (int c8 = 0; c8 < 4; ++c8)
-                        *(uint4*)(dst + 8 * c8) =
-                            make_uint4(pk[4 * c8], pk[4 * c8 + 1], pk[4 * c8 + 2], pk[4 * c8 + 3]);
+                        for (int c4 = 0; c4 < 4; ++c4)
+                            *(float4*)(dst + 4 * c4) =
+                                make_float4(o[4 * c4], o[4 * c4 + 1], o[4 * c4 + 2], o[4 * c4 + 3]);
+                    } else {
+                        for (int c = 0; c < 16; ++c)
+                            if (col0 + c < N) dst[c] = o[c];
+                    }
                 } else {
-                    for (int c = 0; c < 32; ++c)
-                        if (col0 + c < N) dst[c] = (uint16_t)(pk[c >> 1] >> (16 * (c & 1)));
+                    uint16_t* dst = (uint16_t*)a.out + row * N + col0;
+                    uint32_t pk[8];
+#pragma unroll
+                    for (int c2 = 0; c2 < 8; ++c2)
+                        pk[c2] = (uint32_t)f32_to_h<ODT>(o[2 * c2]) |
+                                 ((uint32_t)f32_to_h<ODT>(o[2 * c2 + 1]) << 16);
+                    if (vec_ok) {
+#pragma unroll
+                        for (int c8 = 0; c8 < 2; ++c8)
+                            *(uint4*)(dst + 8 * c8) =
+                                make_uint4(pk[4 * c8], pk[4 * c8 + 1], pk[4 * c8 + 2], pk[4 * c8 + 3]);
+                    } else {
+                        for (int c = 0; c < 16; ++c)
+                            if (col0 + c < N) dst[c] = (uint16_t)(pk[c >> 1] >> (16 * (c & 1)));
+                    }
                 }
             }
         }
+        t += G;
+        if (t >= ntiles) break;
+        cur_t = nxt_t;
+        nxt_t = r3_tile(a, t + G, ntiles, tiles_n);
+        // the output stores are counted by vmcnt ahead of nothing the next
+        // step needs, but the first wait below counts only loads: drain them
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     }
+    __builtin_amdgcn_s_waitcnt(0x0070);
 }
 
 __global__ void fill_zero_i64(int64_t* p, int64_t n)
@@ -514,16 +554,29 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
     // else (small M, group scales, low-rank term, INT32 export, K chunks,
     // K not a multiple of 128, unaligned operands) the 128 x 128 kernel.
     const bool ring3 = !group && a.lora == nullptr && a.acc_out == nullptr && a.k_chunk == 0 &&
-                       a.M > 128 && (a.K % R3_BK) == 0 && aligned;
+                       a.M > 128 && (a.K % R3_BK) == 0 && a.K >= 2 * R3_BK && aligned &&
+                       ((uintptr_t)a.out % 16) == 0;
     if (ring3) {
         const int tm = (int)((a.M + BBM - 1) / BBM), tn = (int)((a.N + BBN - 1) / BBN);
-        const unsigned nt = (unsigned)(tm * tn);
+        const int nt = tm * tn;
+        // persistent grid: one workgroup per CU (a multiple of 8 so that a
+        // workgroup's tiles all fall in its XCD), or one per tile if fewer
+        static int n_cu = 0;
+        if (n_cu == 0) {
+            int dev = 0, v = 0;
+            if (hipGetDevice(&dev) == hipSuccess &&
+                hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v >= 8)
+                n_cu = v & ~7;
+            else
+                n_cu = 256;
+        }
+        const unsigned grid = (unsigned)(nt < n_cu ? nt : n_cu);
         if (a.out_dtype == F32)
-            hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<F32>, dim3(nt), dim3(512), 0, st, a, tm, tn);
+            hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<F32>, dim3(grid), dim3(512), 0, st, a, tm, tn);
         else if (a.out_dtype == F16)
-            hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<F16>, dim3(nt), dim3(512), 0, st, a, tm, tn);
+            hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<F16>, dim3(grid), dim3(512), 0, st, a, tm, tn);
         else
-            hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<BF16>, dim3(nt), dim3(512), 0, st, a, tm, tn);
+            hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<BF16>, dim3(grid), dim3(512), 0, st, a, tm, tn);
         return hipGetLastError();
     }
     const unsigned gx = (unsigned)((a.N + BN - 1) / BN);

@@ -152,3 +152,17 @@ def test_output_bit_exact_without_acc_export(M, K, N, odt):
     out2 = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, odt), bias=dev(b, odt),
                                    out_dtype=out.dtype, k_chunk=128)
     assert np.array_equal(bits(host(out2)), bits(oout))
+
+
+@pytest.mark.parametrize("M,K,N", [(4100, 256, 4130), (4352, 384, 4112)])
+def test_several_tiles_per_workgroup(M, K, N):
+    # more 256 x 256 tiles than CUs: the persistent kernel walks several tiles
+    # per workgroup and prefetches the next tile during the last steps; ragged
+    # M and N on the last tiles, K at two and three 128-steps
+    need_gpu()
+    codes, sa, wp, sw, b = _operands(M, K, N, "bf16", "bf16", seed=M + K + N)
+    out = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, "bf16"),
+                                  bias=dev(b, "bf16"), out_dtype=torch.bfloat16)
+    oacc = oracle.gemm(codes, oracle.unpack(wp, K))
+    oout = oracle.epilogue(oacc, sa, sw, "bf16", "bf16", bias=b, bias_dtype="bf16")
+    assert np.array_equal(bits(host(out)), bits(oout))
