@@ -298,7 +298,7 @@ constexpr int R3_WAVES = 8;
 constexpr int R3_ALOADS = R3_ASTAGE / 1024 / R3_WAVES;  // 1 KB per load: 4 per wave
 constexpr int R3_WLOADS = R3_WSTAGE / 1024 / R3_WAVES;  // 2 per wave
 constexpr int R3_EPR = 68;  // epilogue strip row in words (64 + 4 pad)
-static_assert(R3_WAVES * 16 * R3_EPR * 4 + 2 * BBN * 4 <= R3_SLOT, "epilogue must fit in one slot");
+static_assert(R3_WAVES * 16 * R3_EPR * 4 + 2 * BBN * 4 + BBM * 4 <= R3_SLOT, "epilogue must fit in one slot");
 
 __device__ __forceinline__ v4i r3_half(v4u p, int t)
 {
@@ -441,30 +441,44 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
         // ---- epilogue in the slot the last step used (every wave has left it
         // after the barrier below); the next tile's first two stages are
         // already in flight into the other two.  Scales and bias are widened
-        // in LDS; each wave writes its accumulators out as 16 x 64 strips so
-        // that every lane stores 16 consecutive outputs with 16-byte stores.
+        // in LDS; each wave passes its accumulators through LDS as 16 x 64
+        // strips so that every store instruction writes whole output rows.
         int8_t* eslot = smem + nxt2 * R3_SLOT;  // == slot of the step just computed
         __builtin_amdgcn_s_barrier();
         float* scol = (float*)(eslot + R3_WAVES * 16 * R3_EPR * 4);
         float* bcol = scol + BBN;
+        float* srow = bcol + BBN;
         const int64_t m0 = cur_t.m0, n0 = cur_t.n0;
         {
+            // one round trip per tile for the column scales, the bias and the
+            // row scales
             const int c = tid & (BBN - 1);
-            const int64_t col = n0 + c;
+            const int64_t col = n0 + c, row = m0 + c;
             const int64_t cc = col < N ? col : N - 1;
-            if (tid < BBN) scol[c] = load_any_f32(a.sw_dtype, a.sw, cc);
-            else bcol[c] = a.bias ? load_any_f32(a.bias_dtype, a.bias, cc) : 0.0f;
+            if (tid < BBN) {
+                scol[c] = load_any_f32(a.sw_dtype, a.sw, cc);
+                srow[c] = a.sa[row < M ? row : M - 1];
+            } else {
+                bcol[c] = a.bias ? load_any_f32(a.bias_dtype, a.bias, cc) : 0.0f;
+            }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS writes done
         __builtin_amdgcn_s_barrier();
         int* strip = (int*)eslot + wave * 16 * R3_EPR;
-        const int er = lane >> 2;
-        const int ec = (lane & 3) * 16;
-        const int64_t col0 = n0 + wn * 64 + ec;
-        const float* sc = scol + wn * 64 + ec;
-        const float* bc = bcol + wn * 64 + ec;
+        // store mapping: each store instruction writes whole rows of the
+        // 16 x 64 strip (128 bytes for 16-bit outputs, 256 for fp32): VPR
+        // outputs per lane and store, LPR lanes per row, RPI rows per store
+        constexpr int VPR = ODT == F32 ? 4 : 8;
+        constexpr int LPR = 64 / VPR;
+        constexpr int RPI = 64 / LPR;
+        const int sr = lane / LPR;            // first strip row of this lane
+        const int cb = (lane % LPR) * VPR;    // column offset inside the 64
+        const int64_t col0 = n0 + wn * 64 + cb;
         const bool has_bias = a.bias != nullptr;
-        const bool vec_ok = (col0 + 16 <= N) && (N % 8) == 0;
+        // a full tile with 16-byte aligned rows stores with no per-lane checks
+        const bool full = m0 + BBM <= M && n0 + BBN <= N && (N % 8) == 0;
+        const float* scl = scol + wn * 64 + cb;
+        const float* bia = bcol + wn * 64 + cb;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
@@ -473,49 +487,54 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
                 for (int r = 0; r < 4; ++r) strip[(4 * q + r) * R3_EPR + nt * 16 + j] = acc[mt][nt][r] >> 4;
             __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_wave_barrier();
-            const int64_t row = m0 + wm * 128 + mt * 16 + er;
-            int iv[16];
+            int iv[16 / RPI][VPR];
 #pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const int4 v = *(const int4*)(strip + er * R3_EPR + ec + 4 * c4);
-                iv[4 * c4] = v.x; iv[4 * c4 + 1] = v.y; iv[4 * c4 + 2] = v.z; iv[4 * c4 + 3] = v.w;
-            }
+            for (int i = 0; i < 16 / RPI; ++i)
+#pragma unroll
+                for (int c4 = 0; c4 < VPR / 4; ++c4) {
+                    const int4 v = *(const int4*)(strip + (sr + i * RPI) * R3_EPR + cb + 4 * c4);
+                    iv[i][4 * c4] = v.x; iv[i][4 * c4 + 1] = v.y; iv[i][4 * c4 + 2] = v.z; iv[i][4 * c4 + 3] = v.w;
+                }
             __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_wave_barrier();
-            if (row < M) {
-                const float sa = a.sa[row];
-                float o[16];
 #pragma unroll
-                for (int c = 0; c < 16; ++c) {
-                    float tv = mul_rn(mul_rn((float)iv[c], sa), sc[c]);
-                    o[c] = has_bias ? add_rn(tv, bc[c]) : tv;
+            for (int i = 0; i < 16 / RPI; ++i) {
+                const int tr = wm * 128 + mt * 16 + sr + i * RPI;  // row inside the tile
+                const int64_t row = m0 + tr;
+                const float sa = srow[tr];
+                float o[VPR];
+#pragma unroll
+                for (int c = 0; c < VPR; ++c) {
+                    const float tv = mul_rn(mul_rn((float)iv[i][c], sa), scl[c]);
+                    const float tb = add_rn(tv, bia[c]);
+                    o[c] = has_bias ? tb : tv;
                 }
                 if constexpr (ODT == F32) {
                     float* dst = (float*)a.out + row * N + col0;
-                    if (vec_ok) {
+                    if (full) {
+                        *(float4*)dst = make_float4(o[0], o[1], o[2], o[3]);
+                    } else if (row < M) {
 #pragma unroll
-                        for (int c4 = 0; c4 < 4; ++c4)
-                            *(float4*)(dst + 4 * c4) =
-                                make_float4(o[4 * c4], o[4 * c4 + 1], o[4 * c4 + 2], o[4 * c4 + 3]);
-                    } else {
-                        for (int c = 0; c < 16; ++c)
+                        for (int c = 0; c < VPR; ++c)
                             if (col0 + c < N) dst[c] = o[c];
                     }
                 } else {
                     uint16_t* dst = (uint16_t*)a.out + row * N + col0;
-                    uint32_t pk[8];
+                    uint32_t pk[4];
 #pragma unroll
-                    for (int c2 = 0; c2 < 8; ++c2)
+                    for (int c2 = 0; c2 < 4; ++c2)
                         pk[c2] = (uint32_t)f32_to_h<ODT>(o[2 * c2]) |
                                  ((uint32_t)f32_to_h<ODT>(o[2 * c2 + 1]) << 16);
-                    if (vec_ok) {
+                    if (full) {
+                        *(uint4*)dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+                    } else if (row < M) {
+                        if (col0 + VPR <= N && (N % 8) == 0) {
+                            *(uint4*)dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+                        } else {
 #pragma unroll
-                        for (int c8 = 0; c8 < 2; ++c8)
-                            *(uint4*)(dst + 8 * c8) =
-                                make_uint4(pk[4 * c8], pk[4 * c8 + 1], pk[4 * c8 + 2], pk[4 * c8 + 3]);
-                    } else {
-                        for (int c = 0; c < 16; ++c)
-                            if (col0 + c < N) dst[c] = (uint16_t)(pk[c >> 1] >> (16 * (c & 1)));
+                            for (int c = 0; c < VPR; ++c)
+                                if (col0 + c < N) dst[c] = (uint16_t)(pk[c >> 1] >> (16 * (c & 1)));
+                        }
                     }
                 }
             }
