@@ -349,6 +349,385 @@ __global__ __launch_bounds__(256) void rq_mfma_kernel(
 }
 
 // -------------------------------------------------------------------------
+// Column-major path for 16-bit activations stored with unit row stride
+// (x[m, k] at x[k * sk + m], e.g. the transpose of a contiguous (K, M)
+// buffer).  One 512-thread workgroup per 32-row block walks the K/g rotation
+// groups twice: the first pass rotates and keeps the per-row absmax, the
+// second rotates again and quantizes with the now known row scale (the rows
+// are too long to park their rotated values on chip).
+//   * A group's tile (g k-rows of 32 consecutive x values = 64 bytes) goes
+//     global -> LDS with buffer_load ... lds into a ring of tiles, so each
+//     load instruction reads 16 whole 64-byte segments; neighbouring row
+//     blocks run on the same XCD, where they share 128-byte lines in L2.
+//   * The two 32-byte halves of a k-row are swapped in odd quarters of the
+//     group (k-rows g/4 .. g/2-1 and 3g/4 ..), so the four lane groups of a
+//     transposing read, which read the same rows of k-rows g/4 apart, do not
+//     all land on the same banks.
+//   * MFMA A operands come straight out of the [k][m] tile with
+//     ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+//     (i & 3) of the 4-element reads of lanes 4e + (i >> 2), e = 0..3, so
+//     when lane L reads k-row 8q' + (L >> 2) at rows 4 (L & 3) .. +3, lane i
+//     gets x[i][8q' + e]; two such reads give the 8 k of a fragment.
+//   * The k-slots of each MFMA step match the contiguous-row MFMA kernel
+//     (lane group q, step ks: k = q * g/4 + 8 ks + e), so both give the same
+//     rotated bits.
+//   * The rotation B operand (a slice per wave) stays in VGPRs.
+//   * Waves 0-3 issue every tile load and waves 4-7 every store, so each
+//     wave's vmcnt counts one kind of operation (loads and stores may retire
+//     out of order with respect to each other) and a loader's wait for its
+//     own tile leaves the next tile in flight.  Codes (and the optional
+//     rotated export) are staged per group in LDS and leave as 16-byte
+//     buffer stores whose range check drops rows past M.
+// -------------------------------------------------------------------------
+// LDS writes visible, then a workgroup barrier that does not wait for the
+// loads and stores still in flight (__syncthreads would).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rq_rsrc(const void* base, uint64_t bytes)
+{
+    const uint32_t n = bytes > 0x7fffffffull ? 0x7fffffffu : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, 0x00020000);
+}
+
+constexpr int CM_ROWS = 32;            // rows per workgroup
+constexpr int CM_OOB = 0x7ffffff0;     // byte offset past every range used below
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// NKS pairs of transposing reads from LDS byte address a: pair ks reads at
+// a + 512 ks and a + 512 ks + 256 (k-rows 8 ks and 8 ks + 4 of a 64-byte-row
+// tile).  Written as inline asm because the compiler makes the builtin form
+// wait for every outstanding global load first.  The block first waits for
+// earlier stores to have read their data registers (expcnt: the compiler
+// does not order those against asm outputs) and waits for its own reads
+// before it ends, so no register is handed out while a read is in flight;
+// the outputs are early-clobber so that none shares the address register,
+// which later reads of the block still use.
+template <int NKS> struct TrReads;
+template <> struct TrReads<8> {
+    static __device__ __forceinline__ void run(unsigned a, v4s (&lo)[8], v4s (&hi)[8])
+    {
+        asm volatile(
+            "s_waitcnt expcnt(0)\n\tds_read_b64_tr_b16 %0, %16\n\tds_read_b64_tr_b16 %1, %16 offset:256\n\t"
+            "ds_read_b64_tr_b16 %2, %16 offset:512\n\tds_read_b64_tr_b16 %3, %16 offset:768\n\t"
+            "ds_read_b64_tr_b16 %4, %16 offset:1024\n\tds_read_b64_tr_b16 %5, %16 offset:1280\n\t"
+            "ds_read_b64_tr_b16 %6, %16 offset:1536\n\tds_read_b64_tr_b16 %7, %16 offset:1792\n\t"
+            "ds_read_b64_tr_b16 %8, %16 offset:2048\n\tds_read_b64_tr_b16 %9, %16 offset:2304\n\t"
+            "ds_read_b64_tr_b16 %10, %16 offset:2560\n\tds_read_b64_tr_b16 %11, %16 offset:2816\n\t"
+            "ds_read_b64_tr_b16 %12, %16 offset:3072\n\tds_read_b64_tr_b16 %13, %16 offset:3328\n\t"
+            "ds_read_b64_tr_b16 %14, %16 offset:3584\n\tds_read_b64_tr_b16 %15, %16 offset:3840\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
+              "=&v"(lo[3]), "=&v"(hi[3]), "=&v"(lo[4]), "=&v"(hi[4]), "=&v"(lo[5]), "=&v"(hi[5]),
+              "=&v"(lo[6]), "=&v"(hi[6]), "=&v"(lo[7]), "=&v"(hi[7])
+            : "v"(a)
+            : "memory");
+    }
+};
+template <> struct TrReads<4> {
+    static __device__ __forceinline__ void run(unsigned a, v4s (&lo)[4], v4s (&hi)[4])
+    {
+        asm volatile(
+            "s_waitcnt expcnt(0)\n\tds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %8 offset:256\n\t"
+            "ds_read_b64_tr_b16 %2, %8 offset:512\n\tds_read_b64_tr_b16 %3, %8 offset:768\n\t"
+            "ds_read_b64_tr_b16 %4, %8 offset:1024\n\tds_read_b64_tr_b16 %5, %8 offset:1280\n\t"
+            "ds_read_b64_tr_b16 %6, %8 offset:1536\n\tds_read_b64_tr_b16 %7, %8 offset:1792\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]),
+              "=&v"(lo[3]), "=&v"(hi[3])
+            : "v"(a)
+            : "memory");
+    }
+};
+template <> struct TrReads<2> {
+    static __device__ __forceinline__ void run(unsigned a, v4s (&lo)[2], v4s (&hi)[2])
+    {
+        asm volatile(
+            "s_waitcnt expcnt(0)\n\tds_read_b64_tr_b16 %0, %4\n\tds_read_b64_tr_b16 %1, %4 offset:256\n\t"
+            "ds_read_b64_tr_b16 %2, %4 offset:512\n\tds_read_b64_tr_b16 %3, %4 offset:768\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
+            : "v"(a)
+            : "memory");
+    }
+};
+
+// One 16-byte LDS read, in asm for the same reason as TrReads.
+__device__ __forceinline__ v4i lds_read16(const void* p)
+{
+    v4i v;
+    asm volatile("s_waitcnt expcnt(0)\n\tds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v)
+                 : "v"((unsigned)(size_t)(__attribute__((address_space(3))) const void*)p)
+                 : "memory");
+    return v;
+}
+
+// s_waitcnt immediate for vmcnt(n), n < 64 (expcnt and lgkmcnt not waited)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
+
+template <int DT, int GP, bool SMOOTH, bool YOUT, int NSTG>
+__global__ __launch_bounds__(512) void rq_colmajor_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t sk,
+    const float* __restrict__ rot, const uint16_t* __restrict__ smooth,
+    int8_t* __restrict__ codes, float* __restrict__ scales, uint16_t* __restrict__ yout)
+{
+    constexpr int TROW = CM_ROWS * 2;                 // bytes per k-row of a tile
+    constexpr int TILE = GP * TROW;                   // bytes per group tile
+    constexpr int NLD = TILE / 1024 / 4;              // 1 KB loads per loader wave per tile
+    constexpr int NJT = GP / 16;                      // 16-wide output column tiles
+    constexpr int JPW = NJT >= 8 ? NJT / 8 : 1;       // column tiles per wave
+    constexpr int MPW = NJT >= 8 ? 2 : 1;             // 16-row tiles per wave
+    constexpr int NKS = GP / 32;                      // 32-deep MFMA steps
+    constexpr int LPL = GP / 4;                       // k per lane group per group-row
+    constexpr int CCH = CM_ROWS * GP / 16;            // 16-byte code chunks per group
+    constexpr int YCH = YOUT ? CM_ROWS * GP * 2 / 16 : 0;
+    constexpr int NCS = (CCH + 255) / 256;            // code stores per storer thread
+    constexpr int NYS = (YCH + 255) / 256;            // rotated-value stores per storer thread
+    static_assert(NJT >= 8 || NJT == 4, "group width 64, 128 or 256");
+    static_assert(NLD >= 1 && NLD <= 4, "one to four loads per loader wave");
+
+    __shared__ __align__(16) uint8_t stg[NSTG][TILE];
+    static_assert(NSTG >= 3 && NLD * (NSTG - 2) < 64, "ring depth");
+    __shared__ __align__(16) int8_t ctile[CM_ROWS * GP];
+    __shared__ __align__(16) uint16_t ytile[YOUT ? CM_ROWS * GP : 8];
+    __shared__ uint32_t rowmax[CM_ROWS];
+    __shared__ float rowsc[CM_ROWS], rowinv[CM_ROWS];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, q = lane >> 4;
+    const int jt0 = NJT >= 8 ? wave * JPW : (wave & 3);
+    const int mt0 = NJT >= 8 ? 0 : (wave >> 2);
+    const bool loader = wave < 4;
+    const int st_tid = tid - 256;                     // storer thread index (waves 4-7)
+    // workgroups are dealt round-robin over the 8 XCDs; give each XCD a
+    // contiguous range of row blocks so that the two halves of every
+    // 128-byte line (two neighbouring blocks) meet in the same L2
+    const int nb = gridDim.x, bid = blockIdx.x;
+    const int q8 = nb >> 3, r8 = nb & 7, xcd = bid & 7;
+    const int rb = xcd * q8 + min(xcd, r8) + (bid >> 3);
+    const int64_t m0 = (int64_t)rb * CM_ROWS;
+    const int G = (int)(K / GP);
+
+    if (tid < CM_ROWS) rowmax[tid] = 0u;
+
+    // rotation slice, rounded to T: lane (n, q), step ks holds
+    // R[q * LPL + 8 ks + e][column jt * 16 + n]
+    v8s bfr[JPW][NKS];
+#pragma unroll
+    for (int jj = 0; jj < JPW; ++jj)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kk = q * LPL + ks * 8 + e;
+                bfr[jj][ks][e] = (short)f32_to_h<DT>(rot[kk * GP + (jt0 + jj) * 16 + n]);
+            }
+
+    // tile loads: loader wave w issues loads w*NLD .. w*NLD+NLD-1; load i fills
+    // k-rows 16 i .. 16 i + 15; lane l takes k-row 16 i + (l >> 2), rows
+    // 8 (l & 3) .. +7 of the block
+    const uint64_t xelems = (uint64_t)(K - 1) * sk + M;
+    auto issue = [&](int stage, int b) {
+        const uint64_t base = (uint64_t)b * GP * sk + m0;
+        const __amdgpu_buffer_rsrc_t r = rq_rsrc(x + base, (xelems - base) * 2);
+#pragma unroll
+        for (int u = 0; u < NLD; ++u) {
+            const int i = wave * NLD + u;
+            // 16-byte chunk (lane & 3) of k-row 16 i + (lane >> 2) holds
+            // logical chunk (lane & 3) ^ cm_swz(k-row)
+            const int c = (lane & 3) ^ (2 * (((16 * i) / LPL) & 1));
+            const int vo = (int)(((lane >> 2) * sk + 8 * c) * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void*)(&stg[stage][i * 1024]), 16,
+                vo + (int)(16 * i * sk * 2), 0, 0, 0);
+        }
+    };
+
+    const __amdgpu_buffer_rsrc_t rc = rq_rsrc(codes, (uint64_t)M * K);
+    const __amdgpu_buffer_rsrc_t ry = rq_rsrc(yout, YOUT ? (uint64_t)M * K * 2 : 0);
+    uint32_t rmax[MPW][4];
+#pragma unroll
+    for (int mi = 0; mi < MPW; ++mi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rmax[mi][r] = 0u;
+
+    float rsc[MPW][4], rinv[MPW][4];  // row scales of this lane's rows (pass 2)
+    const int nsteps = 2 * G;
+    if (loader)
+        for (int i = 0; i < NSTG - 1 && i < nsteps; ++i) issue(i, i % G);
+    int cur = 0;  // ring slot of step s
+    for (int s = 0; s < nsteps; ++s) {
+        const int b = s < G ? s : s - G;
+        const bool pass2 = s >= G;
+        // a loader waits for its part of this step's tile; the next NSTG - 2
+        // tiles' loads stay in flight (near the end, none)
+        if (loader) {
+            if (s + NSTG - 2 < nsteps) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NLD * (NSTG - 2)));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        __builtin_amdgcn_s_barrier();
+        const int nxt = cur == 0 ? NSTG - 1 : cur - 1;  // slot of step s - 1, free now
+        if (loader && s + NSTG - 1 < nsteps) issue(nxt, (s + NSTG - 1) % G);
+        uint8_t* tile = stg[cur];
+        cur = cur == NSTG - 1 ? 0 : cur + 1;
+        if constexpr (SMOOTH) {
+            // x' = T(x / smooth[k]) in place: thread t handles k-rows t / 4,
+            // t / 4 + 128, ..., 16 bytes each
+            for (int kr = tid >> 2; kr < GP; kr += 128) {
+                const float sv = h_to_f32<DT>(smooth[(int64_t)b * GP + kr]);
+                v8s* p = (v8s*)(tile + kr * TROW + (tid & 3) * 16);
+                v8s v = *p;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[e] = (short)f32_to_h<DT>(h_to_f32<DT>((uint16_t)v[e]) / sv);
+                *p = v;
+            }
+            lds_barrier();
+        }
+        v4f acc[MPW][JPW];
+#pragma unroll
+        for (int mi = 0; mi < MPW; ++mi)
+#pragma unroll
+            for (int jj = 0; jj < JPW; ++jj) acc[mi][jj] = (v4f){0.f, 0.f, 0.f, 0.f};
+        // all A fragments of the step first (LDS returns them in order, so the
+        // MFMAs only wait for the ones they use)
+        v4s afl[MPW][NKS], afh[MPW][NKS];
+#pragma unroll
+        for (int mi = 0; mi < MPW; ++mi) {
+            // lane L of group q reads k-rows q * LPL + 8 ks + (L >> 2) (+4),
+            // rows 16 mt + 4 (L & 3) .. +3
+            const int kr = q * LPL + (n >> 2);
+            const int lc = 2 * (mt0 + mi) + ((n & 3) >> 1);  // logical 16-byte chunk
+            const uint8_t* p = tile + kr * TROW + (lc ^ (2 * (q & 1))) * 16 + (n & 1) * 8;
+            static_assert(8 * TROW == 512 && 4 * TROW == 256, "read offsets in TrReads");
+            TrReads<NKS>::run((unsigned)(size_t)(__attribute__((address_space(3))) const uint8_t*)p,
+                              afl[mi], afh[mi]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+            for (int mi = 0; mi < MPW; ++mi) {
+                const v4s lo = afl[mi][ks], hi = afh[mi][ks];
+                const v8s af = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+                for (int jj = 0; jj < JPW; ++jj) {
+                    if constexpr (DT == BF16)
+                        acc[mi][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(v8bf, af), __builtin_bit_cast(v8bf, bfr[jj][ks]), acc[mi][jj], 0, 0, 0);
+                    else
+                        acc[mi][jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(v8h, af), __builtin_bit_cast(v8h, bfr[jj][ks]), acc[mi][jj], 0, 0, 0);
+                }
+            }
+        }
+        if (!pass2) {
+            // lane (n, q) holds rows 16 mt + 4 q + r, column 16 jt + n
+#pragma unroll
+            for (int mi = 0; mi < MPW; ++mi)
+#pragma unroll
+                for (int jj = 0; jj < JPW; ++jj)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint16_t yb = f32_to_h<DT>(acc[mi][jj][r]);
+                        rmax[mi][r] = max(rmax[mi][r], __float_as_uint(h_to_f32<DT>(yb)) & 0x7fffffffu);
+                    }
+            if (s == G - 1) {
+                // row absmax across the 16 lanes of a row, then across waves
+#pragma unroll
+                for (int mi = 0; mi < MPW; ++mi)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint32_t v = wave_max16(rmax[mi][r]);
+                        if (n == 0) atomicMax(&rowmax[(mt0 + mi) * 16 + 4 * q + r], v);
+                    }
+                lds_barrier();
+                if (tid < CM_ROWS) {
+                    const float sc = row_scale(rowmax[tid]);
+                    rowsc[tid] = sc;
+                    rowinv[tid] = 1.0f / sc;
+                }
+                if (st_tid >= 0 && st_tid < CM_ROWS && m0 + st_tid < M)
+                    scales[m0 + st_tid] = row_scale(rowmax[st_tid]);
+                lds_barrier();
+#pragma unroll
+                for (int mi = 0; mi < MPW; ++mi)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        rsc[mi][r] = rowsc[(mt0 + mi) * 16 + 4 * q + r];
+                        rinv[mi][r] = rowinv[(mt0 + mi) * 16 + 4 * q + r];
+                    }
+            }
+            continue;
+        }
+        // pass 2: quantize into the LDS code tile.  y * (1/s), clamped to
+        // [-7, 7], plus 1.5 * 2^23 is rounded to nearest even by the addition
+        // and its low byte is the code; a quotient within 2^-17 of a
+        // half-integer, or a non-finite scale, sends the wave to the exact
+        // division.
+        float yv[MPW][JPW][4];
+        bool near = false;
+#pragma unroll
+        for (int mi = 0; mi < MPW; ++mi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = (mt0 + mi) * 16 + 4 * q + r;
+                const float ri = rinv[mi][r];
+                near |= !(fabsf(rsc[mi][r]) < __builtin_inff());
+#pragma unroll
+                for (int jj = 0; jj < JPW; ++jj) {
+                    const uint16_t yb = f32_to_h<DT>(acc[mi][jj][r]);
+                    const int col = (jt0 + jj) * 16 + n;
+                    yv[mi][jj][r] = h_to_f32<DT>(yb);
+                    const float qv = yv[mi][jj][r] * ri;
+                    const float t = __builtin_amdgcn_fmed3f(qv, -7.0f, 7.0f) + kRoundMagic;
+                    near |= fabsf(qv - (t - kRoundMagic)) > 0.5f - 0x1p-17f;
+                    ctile[row * GP + col] = (int8_t)__float_as_uint(t);
+                    if constexpr (YOUT) ytile[row * GP + col] = yb;
+                }
+            }
+        if (__any(near)) {
+#pragma unroll
+            for (int mi = 0; mi < MPW; ++mi)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = (mt0 + mi) * 16 + 4 * q + r;
+#pragma unroll
+                    for (int jj = 0; jj < JPW; ++jj)
+                        ctile[row * GP + (jt0 + jj) * 16 + n] =
+                            (int8_t)quant_code(yv[mi][jj][r], rsc[mi][r], rinv[mi][r]);
+                }
+        }
+        lds_barrier();
+        if (!loader) {
+#pragma unroll
+            for (int u = 0; u < NCS; ++u) {
+                const int c = st_tid + 256 * u;
+                const int row = c / (GP / 16), ch = c % (GP / 16);
+                const v4i v = lds_read16(ctile + (c < CCH ? row * GP + ch * 16 : 0));
+                const int off = c < CCH ? (int)((m0 + row) * K + (int64_t)b * GP + ch * 16) : CM_OOB;
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
+            }
+            if constexpr (YOUT) {
+#pragma unroll
+                for (int u = 0; u < NYS; ++u) {
+                    const int c = st_tid + 256 * u;
+                    const int row = c / (GP / 8), ch = c % (GP / 8);
+                    const v4i v = lds_read16(ytile + (c < YCH ? row * GP + ch * 8 : 0));
+                    const int off = c < YCH ? (int)(((m0 + row) * K + (int64_t)b * GP + ch * 8) * 2) : CM_OOB;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// -------------------------------------------------------------------------
 // Register-resident path for 16-bit activations, group width 32 or 64,
 // contiguous rows.  Persistent workgroups (R loaded once per workgroup) walk
 // blocks of rows; a block's group-rows are dealt to the four waves as 16-row
@@ -1136,7 +1515,54 @@ static hipError_t launch_wave_dt(const RQArgs& a, int GP, hipStream_t st)
     return launch_wave_t<DT, 64, false, false>(a, st);
 }
 
-// Chooses the kernel; returns the path taken in *path (0 generic, 1 MFMA LDS, 2 MFMA registers).
+// ring depth: as many tiles in flight as fit next to the staging tiles
+template <int GP, bool YOUT> constexpr int cm_stages() { return GP == 256 ? (YOUT ? 5 : 6) : 8; }
+
+template <int DT, int GP, bool SMOOTH, bool YOUT>
+static hipError_t launch_colmajor_t(const RQArgs& a, hipStream_t st)
+{
+    const unsigned grid = (unsigned)((a.M + CM_ROWS - 1) / CM_ROWS);
+    hipLaunchKernelGGL((rq_colmajor_kernel<DT, GP, SMOOTH, YOUT, cm_stages<GP, YOUT>()>), dim3(grid), dim3(512), 0, st,
+                       (const uint16_t*)a.x, a.M, a.K, a.sk, a.rot, (const uint16_t*)a.smooth, a.codes,
+                       a.scales, (uint16_t*)a.yout);
+    return hipGetLastError();
+}
+
+template <int DT, int GP>
+static hipError_t launch_colmajor_g(const RQArgs& a, hipStream_t st)
+{
+    if (a.smooth)
+        return a.yout ? launch_colmajor_t<DT, GP, true, true>(a, st) : launch_colmajor_t<DT, GP, true, false>(a, st);
+    return a.yout ? launch_colmajor_t<DT, GP, false, true>(a, st) : launch_colmajor_t<DT, GP, false, false>(a, st);
+}
+
+template <int DT>
+static hipError_t launch_colmajor_dt(const RQArgs& a, hipStream_t st)
+{
+    if (a.g == 64) return launch_colmajor_g<DT, 64>(a, st);
+    if (a.g == 128) return launch_colmajor_g<DT, 128>(a, st);
+    return launch_colmajor_g<DT, 256>(a, st);
+}
+
+// Unit row stride (a transposed view): the column-major kernel applies when
+// its loads and stores line up on 16 bytes and every buffer offset fits in
+// 31 bits.
+static bool colmajor_ok(const RQArgs& a)
+{
+    const bool sixteen = a.dtype == F16 || a.dtype == BF16;
+    if (!sixteen || !a.rot || a.sm != 1 || a.sk < a.M || a.M <= 0) return false;
+    if (!(a.g == 64 || a.g == 128 || a.g == 256) || (a.K % a.g) != 0) return false;
+    if ((a.M % 8) != 0 || (a.sk % 8) != 0) return false;
+    if (((uintptr_t)a.x % 16) != 0 || ((uintptr_t)a.codes % 16) != 0) return false;
+    if (a.yout && ((uintptr_t)a.yout % 16) != 0) return false;
+    const int64_t lim = 0x7ffffff0ll;
+    if (a.M * a.K > lim || (a.yout && 2 * a.M * a.K > lim)) return false;
+    if (2 * (int64_t)a.g * a.sk > lim) return false;
+    return true;
+}
+
+// Chooses the kernel; returns the path taken in *path (0 generic, 1 MFMA LDS, 2 MFMA registers,
+// 3 wave per row, 4 column-major).
 hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path)
 {
     // MFMA path: 16-bit activations, group width 16..256, K a multiple of
@@ -1149,6 +1575,10 @@ hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path)
               (a.yout == nullptr || ((uintptr_t)a.yout % 16) == 0) &&
               (a.smooth == nullptr || ((uintptr_t)a.smooth % 16) == 0);
     if (a.rot && !(a.g == 16 || a.g == 32 || a.g == 64 || a.g == 128 || a.g == 256)) ok = false;
+    if (colmajor_ok(a)) {
+        if (path) *path = 4;
+        return a.dtype == BF16 ? launch_colmajor_dt<BF16>(a, st) : launch_colmajor_dt<F16>(a, st);
+    }
     if (ok && mfma_lds_bytes(GP, a.K, 1) > 160 * 1024) ok = false;
     const bool contig = a.sk == 1 && (a.sm % 8) == 0 && ((uintptr_t)a.x % 16) == 0;
     if (ok && contig && GP <= 64 && a.K / GP <= 64 &&

@@ -180,3 +180,42 @@ def test_empty_and_rejections():
     R = _rot_dev(workloads.hadamard(64))
     with pytest.raises(ValueError):
         w4.w4a4_rotate_quant_rowwise(torch.zeros((2, 96), dtype=torch.bfloat16, device="cuda"), R, 64)
+
+
+@pytest.mark.parametrize("dt,g,M,K", [("f16", 256, 64, 1024), ("bf16", 256, 96, 2560),
+                                      ("f16", 128, 40, 512), ("bf16", 64, 256, 192),
+                                      ("f16", 256, 32, 256)])
+def test_column_major_views_match_contiguous(dt, g, M, K):
+    # a transposed view with M % 8 == 0 takes the column-major kernel (two
+    # passes over 32-row blocks); the rotated bits, scales and codes must equal
+    # those of a contiguous copy, and the codes those of the oracle quantizer
+    need_gpu()
+    buf = _draw(dt, K, M, seed=M + g)
+    xt = dev(buf, dt).t()
+    assert xt.stride() == (1, M)
+    R = workloads.asymmetric_rotation(g, g)
+    c, s, yg = w4.w4a4_rotate_quant_rowwise(xt, _rot_dev(R), g, return_rotated=True)
+    c1, s1, y1 = w4.w4a4_rotate_quant_rowwise(xt.contiguous(), _rot_dev(R), g, return_rotated=True)
+    assert np.array_equal(bits(host(yg)), bits(host(y1)))
+    assert np.array_equal(bits(host(s)), bits(host(s1)))
+    assert np.array_equal(host(c), host(c1))
+    oc, os2 = oracle.quantize(host(yg), dt)
+    assert np.array_equal(host(c), oc) and np.array_equal(bits(host(s)), bits(os2))
+    # without the rotated export the codes are the same
+    c2, s2 = w4.w4a4_rotate_quant_rowwise(xt, _rot_dev(R), g)
+    assert np.array_equal(host(c2), host(c)) and np.array_equal(bits(host(s2)), bits(host(s)))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_column_major_with_smoothing(dt):
+    need_gpu()
+    M, K, g = 48, 1024, 256
+    buf = _draw(dt, K, M, seed=21)
+    xt = dev(buf, dt).t()
+    sm = workloads.f32_to_storage(np.random.default_rng(4).uniform(0.5, 2.0, size=K), dt)
+    R = workloads.hadamard(g)
+    c, s, yg = w4.w4a4_rotate_quant_rowwise(xt, _rot_dev(R), g, smooth=dev(sm, dt), return_rotated=True)
+    c1, s1, y1 = w4.w4a4_rotate_quant_rowwise(xt.contiguous(), _rot_dev(R), g, smooth=dev(sm, dt),
+                                              return_rotated=True)
+    assert np.array_equal(bits(host(yg)), bits(host(y1)))
+    assert np.array_equal(host(c), host(c1)) and np.array_equal(bits(host(s)), bits(host(s1)))
