@@ -467,6 +467,26 @@ __device__ __forceinline__ v4i lds_read16(const void* p)
     return v;
 }
 
+// LDS stores in asm: as a compiler-visible store after the LDS-DMA loads
+// the compiler would first wait for all of them.  Completion is covered by
+// the lgkmcnt(0) before the next barrier.
+__device__ __forceinline__ void lds_write4(void* p, uint32_t v)
+{
+    asm volatile("ds_write_b32 %0, %1"
+                 :
+                 : "v"((unsigned)(size_t)(__attribute__((address_space(3))) void*)p), "v"(v)
+                 : "memory");
+}
+
+__device__ __forceinline__ void lds_write8(void* p, uint32_t lo, uint32_t hi)
+{
+    asm volatile("ds_write_b64 %0, %1"
+                 :
+                 : "v"((unsigned)(size_t)(__attribute__((address_space(3))) void*)p),
+                   "v"(__builtin_bit_cast(uint64_t, make_uint2(lo, hi)))
+                 : "memory");
+}
+
 // s_waitcnt immediate for vmcnt(n), n < 64 (expcnt and lgkmcnt not waited)
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
 
@@ -493,8 +513,8 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
 
     __shared__ __align__(16) uint8_t stg[NSTG][TILE];
     static_assert(NSTG >= 3 && NLD * (NSTG - 2) < 64, "ring depth");
-    __shared__ __align__(16) int8_t ctile[CM_ROWS * GP];
-    __shared__ __align__(16) uint16_t ytile[YOUT ? CM_ROWS * GP : 8];
+    __shared__ __align__(16) int8_t ctile[2][CM_ROWS * GP];
+    __shared__ __align__(16) uint16_t ytile[2][YOUT ? CM_ROWS * GP : 8];
     __shared__ uint32_t rowmax[CM_ROWS];
     __shared__ float rowsc[CM_ROWS], rowinv[CM_ROWS];
 
@@ -551,13 +571,37 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
 
     const __amdgpu_buffer_rsrc_t rc = rq_rsrc(codes, (uint64_t)M * K);
     const __amdgpu_buffer_rsrc_t ry = rq_rsrc(yout, YOUT ? (uint64_t)M * K * 2 : 0);
-    uint32_t rmax[MPW][4];
+    uint32_t rmax[MPW];
 #pragma unroll
-    for (int mi = 0; mi < MPW; ++mi)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) rmax[mi][r] = 0u;
+    for (int mi = 0; mi < MPW; ++mi) rmax[mi] = 0u;
 
-    float rsc[MPW][4], rinv[MPW][4];  // row scales of this lane's rows (pass 2)
+    // storer waves: codes (and rotated values) of step st from the LDS
+    // staging tiles to global memory, 16 bytes per store
+    auto store_group = [&](int st) {
+        const int bs = st - G;
+        const int8_t* ct = ctile[st & 1];
+#pragma unroll
+        for (int u = 0; u < NCS; ++u) {
+            const int c = st_tid + 256 * u;
+            const int row = c / (GP / 16), ch = c % (GP / 16);
+            const v4i v = lds_read16(ct + (c < CCH ? row * GP + ch * 16 : 0));
+            const int off = c < CCH ? (int)((m0 + row) * K + (int64_t)bs * GP + ch * 16) : CM_OOB;
+            __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
+        }
+        if constexpr (YOUT) {
+            const uint16_t* yt = ytile[st & 1];
+#pragma unroll
+            for (int u = 0; u < NYS; ++u) {
+                const int c = st_tid + 256 * u;
+                const int row = c / (GP / 8), ch = c % (GP / 8);
+                const v4i v = lds_read16(yt + (c < YCH ? row * GP + ch * 8 : 0));
+                const int off = c < YCH ? (int)(((m0 + row) * K + (int64_t)bs * GP + ch * 8) * 2) : CM_OOB;
+                __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
+            }
+        }
+    };
+
+    float rsc[MPW], rinv[MPW];  // scale of this lane's row in each row tile (pass 2)
     const int nsteps = 2 * G;
     if (loader)
         for (int i = 0; i < NSTG - 1 && i < nsteps; ++i) issue(i, i % G);
@@ -571,9 +615,10 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
             if (s + NSTG - 2 < nsteps) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NLD * (NSTG - 2)));
             else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
-        __builtin_amdgcn_s_barrier();
+        lds_barrier();  // also publishes the previous step's code tile
         const int nxt = cur == 0 ? NSTG - 1 : cur - 1;  // slot of step s - 1, free now
         if (loader && s + NSTG - 1 < nsteps) issue(nxt, (s + NSTG - 1) % G);
+        if (!loader && s > G) store_group(s - 1);
         uint8_t* tile = stg[cur];
         cur = cur == NSTG - 1 ? 0 : cur + 1;
         if constexpr (SMOOTH) {
@@ -595,7 +640,7 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
         for (int mi = 0; mi < MPW; ++mi)
 #pragma unroll
             for (int jj = 0; jj < JPW; ++jj) acc[mi][jj] = (v4f){0.f, 0.f, 0.f, 0.f};
-        // all A fragments of the step first (LDS returns them in order, so the
+        // all x fragments of the step first (LDS returns them in order, so the
         // MFMAs only wait for the ones they use)
         v4s afl[MPW][NKS], afh[MPW][NKS];
 #pragma unroll
@@ -609,6 +654,9 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
             TrReads<NKS>::run((unsigned)(size_t)(__attribute__((address_space(3))) const uint8_t*)p,
                               afl[mi], afh[mi]);
         }
+        // y^T = R^T . x^T: lane (n, q) of tile (mt, jt) receives
+        // y[16 mt + n][16 jt + 4 q + r], r = 0..3 (four consecutive columns of
+        // one row); same products and k order as x . R
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
@@ -619,15 +667,14 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
                 for (int jj = 0; jj < JPW; ++jj) {
                     if constexpr (DT == BF16)
                         acc[mi][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(v8bf, af), __builtin_bit_cast(v8bf, bfr[jj][ks]), acc[mi][jj], 0, 0, 0);
+                            __builtin_bit_cast(v8bf, bfr[jj][ks]), __builtin_bit_cast(v8bf, af), acc[mi][jj], 0, 0, 0);
                     else
                         acc[mi][jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(v8h, af), __builtin_bit_cast(v8h, bfr[jj][ks]), acc[mi][jj], 0, 0, 0);
+                            __builtin_bit_cast(v8h, bfr[jj][ks]), __builtin_bit_cast(v8h, af), acc[mi][jj], 0, 0, 0);
                 }
             }
         }
         if (!pass2) {
-            // lane (n, q) holds rows 16 mt + 4 q + r, column 16 jt + n
 #pragma unroll
             for (int mi = 0; mi < MPW; ++mi)
 #pragma unroll
@@ -635,17 +682,17 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const uint16_t yb = f32_to_h<DT>(acc[mi][jj][r]);
-                        rmax[mi][r] = max(rmax[mi][r], __float_as_uint(h_to_f32<DT>(yb)) & 0x7fffffffu);
+                        rmax[mi] = max(rmax[mi], __float_as_uint(h_to_f32<DT>(yb)) & 0x7fffffffu);
                     }
             if (s == G - 1) {
-                // row absmax across the 16 lanes of a row, then across waves
+                // row absmax across the four lane groups, then across waves
 #pragma unroll
-                for (int mi = 0; mi < MPW; ++mi)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const uint32_t v = wave_max16(rmax[mi][r]);
-                        if (n == 0) atomicMax(&rowmax[(mt0 + mi) * 16 + 4 * q + r], v);
-                    }
+                for (int mi = 0; mi < MPW; ++mi) {
+                    uint32_t v = rmax[mi];
+                    v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+                    v = max(v, (uint32_t)__shfl_xor((int)v, 32));
+                    if (q == 0) atomicMax(&rowmax[(mt0 + mi) * 16 + n], v);
+                }
                 lds_barrier();
                 if (tid < CM_ROWS) {
                     const float sc = row_scale(rowmax[tid]);
@@ -656,75 +703,51 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
                     scales[m0 + st_tid] = row_scale(rowmax[st_tid]);
                 lds_barrier();
 #pragma unroll
-                for (int mi = 0; mi < MPW; ++mi)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        rsc[mi][r] = rowsc[(mt0 + mi) * 16 + 4 * q + r];
-                        rinv[mi][r] = rowinv[(mt0 + mi) * 16 + 4 * q + r];
-                    }
+                for (int mi = 0; mi < MPW; ++mi) {
+                    rsc[mi] = rowsc[(mt0 + mi) * 16 + n];
+                    rinv[mi] = rowinv[(mt0 + mi) * 16 + n];
+                }
             }
             continue;
         }
-        // pass 2: quantize into the LDS code tile.  y * (1/s), clamped to
-        // [-7, 7], plus 1.5 * 2^23 is rounded to nearest even by the addition
-        // and its low byte is the code; a quotient within 2^-17 of a
-        // half-integer, or a non-finite scale, sends the wave to the exact
-        // division.
+        // pass 2: quantize four codes of one row at a time into this step's
+        // code tile (the storers write out the previous step's tile
+        // meanwhile).  A quotient within 2^-17 of a half-integer, or a
+        // non-finite scale, sends the wave to the exact division.
+        int8_t* ct = ctile[s & 1];
         float yv[MPW][JPW][4];
         bool near = false;
 #pragma unroll
-        for (int mi = 0; mi < MPW; ++mi)
+        for (int mi = 0; mi < MPW; ++mi) {
+            const int row = (mt0 + mi) * 16 + n;
+            near |= !(fabsf(rsc[mi]) < __builtin_inff());
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = (mt0 + mi) * 16 + 4 * q + r;
-                const float ri = rinv[mi][r];
-                near |= !(fabsf(rsc[mi][r]) < __builtin_inff());
+            for (int jj = 0; jj < JPW; ++jj) {
+                uint16_t yb[4];
 #pragma unroll
-                for (int jj = 0; jj < JPW; ++jj) {
-                    const uint16_t yb = f32_to_h<DT>(acc[mi][jj][r]);
-                    const int col = (jt0 + jj) * 16 + n;
-                    yv[mi][jj][r] = h_to_f32<DT>(yb);
-                    const float qv = yv[mi][jj][r] * ri;
-                    const float t = __builtin_amdgcn_fmed3f(qv, -7.0f, 7.0f) + kRoundMagic;
-                    near |= fabsf(qv - (t - kRoundMagic)) > 0.5f - 0x1p-17f;
-                    ctile[row * GP + col] = (int8_t)__float_as_uint(t);
-                    if constexpr (YOUT) ytile[row * GP + col] = yb;
+                for (int r = 0; r < 4; ++r) {
+                    yb[r] = f32_to_h<DT>(acc[mi][jj][r]);
+                    yv[mi][jj][r] = h_to_f32<DT>(yb[r]);
                 }
+                const int col = (jt0 + jj) * 16 + 4 * q;
+                lds_write4(ct + row * GP + col, quant4_finite(yv[mi][jj], rinv[mi], near));
+                if constexpr (YOUT)
+                    lds_write8(ytile[s & 1] + row * GP + col, (uint32_t)yb[0] | ((uint32_t)yb[1] << 16),
+                               (uint32_t)yb[2] | ((uint32_t)yb[3] << 16));
             }
+        }
         if (__any(near)) {
 #pragma unroll
             for (int mi = 0; mi < MPW; ++mi)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = (mt0 + mi) * 16 + 4 * q + r;
-#pragma unroll
-                    for (int jj = 0; jj < JPW; ++jj)
-                        ctile[row * GP + (jt0 + jj) * 16 + n] =
-                            (int8_t)quant_code(yv[mi][jj][r], rsc[mi][r], rinv[mi][r]);
-                }
-        }
-        lds_barrier();
-        if (!loader) {
-#pragma unroll
-            for (int u = 0; u < NCS; ++u) {
-                const int c = st_tid + 256 * u;
-                const int row = c / (GP / 16), ch = c % (GP / 16);
-                const v4i v = lds_read16(ctile + (c < CCH ? row * GP + ch * 16 : 0));
-                const int off = c < CCH ? (int)((m0 + row) * K + (int64_t)b * GP + ch * 16) : CM_OOB;
-                __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
-            }
-            if constexpr (YOUT) {
-#pragma unroll
-                for (int u = 0; u < NYS; ++u) {
-                    const int c = st_tid + 256 * u;
-                    const int row = c / (GP / 8), ch = c % (GP / 8);
-                    const v4i v = lds_read16(ytile + (c < YCH ? row * GP + ch * 8 : 0));
-                    const int off = c < YCH ? (int)(((m0 + row) * K + (int64_t)b * GP + ch * 8) * 2) : CM_OOB;
-                    __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
-                }
-            }
+                for (int jj = 0; jj < JPW; ++jj)
+                    lds_write4(ct + ((mt0 + mi) * 16 + n) * GP + (jt0 + jj) * 16 + 4 * q,
+                               quant4_exact(yv[mi][jj], rsc[mi]));
         }
     }
+    // the last step's codes
+    lds_barrier();
+    if (!loader) store_group(nsteps - 1);
 }
 
 // -------------------------------------------------------------------------
