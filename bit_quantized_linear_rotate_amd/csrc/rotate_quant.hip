@@ -487,6 +487,82 @@ __device__ __forceinline__ void lds_write8(void* p, uint32_t lo, uint32_t hi)
                  : "memory");
 }
 
+// TrReads for two row tiles (addresses a0, a1) in one block, so the read
+// latency is exposed once per step.
+template <int NKS> struct TrReads2;
+template <> struct TrReads2<8> {
+    static __device__ __forceinline__ void run(unsigned a0, unsigned a1, v4s (&lo0)[8], v4s (&hi0)[8],
+                                               v4s (&lo1)[8], v4s (&hi1)[8])
+    {
+        asm volatile(
+            "s_waitcnt expcnt(0)\n\t"
+            "ds_read_b64_tr_b16 %0, %32\n\t"
+            "ds_read_b64_tr_b16 %1, %32 offset:256\n\t"
+            "ds_read_b64_tr_b16 %2, %32 offset:512\n\t"
+            "ds_read_b64_tr_b16 %3, %32 offset:768\n\t"
+            "ds_read_b64_tr_b16 %4, %32 offset:1024\n\t"
+            "ds_read_b64_tr_b16 %5, %32 offset:1280\n\t"
+            "ds_read_b64_tr_b16 %6, %32 offset:1536\n\t"
+            "ds_read_b64_tr_b16 %7, %32 offset:1792\n\t"
+            "ds_read_b64_tr_b16 %8, %32 offset:2048\n\t"
+            "ds_read_b64_tr_b16 %9, %32 offset:2304\n\t"
+            "ds_read_b64_tr_b16 %10, %32 offset:2560\n\t"
+            "ds_read_b64_tr_b16 %11, %32 offset:2816\n\t"
+            "ds_read_b64_tr_b16 %12, %32 offset:3072\n\t"
+            "ds_read_b64_tr_b16 %13, %32 offset:3328\n\t"
+            "ds_read_b64_tr_b16 %14, %32 offset:3584\n\t"
+            "ds_read_b64_tr_b16 %15, %32 offset:3840\n\t"
+            "ds_read_b64_tr_b16 %16, %33\n\t"
+            "ds_read_b64_tr_b16 %17, %33 offset:256\n\t"
+            "ds_read_b64_tr_b16 %18, %33 offset:512\n\t"
+            "ds_read_b64_tr_b16 %19, %33 offset:768\n\t"
+            "ds_read_b64_tr_b16 %20, %33 offset:1024\n\t"
+            "ds_read_b64_tr_b16 %21, %33 offset:1280\n\t"
+            "ds_read_b64_tr_b16 %22, %33 offset:1536\n\t"
+            "ds_read_b64_tr_b16 %23, %33 offset:1792\n\t"
+            "ds_read_b64_tr_b16 %24, %33 offset:2048\n\t"
+            "ds_read_b64_tr_b16 %25, %33 offset:2304\n\t"
+            "ds_read_b64_tr_b16 %26, %33 offset:2560\n\t"
+            "ds_read_b64_tr_b16 %27, %33 offset:2816\n\t"
+            "ds_read_b64_tr_b16 %28, %33 offset:3072\n\t"
+            "ds_read_b64_tr_b16 %29, %33 offset:3328\n\t"
+            "ds_read_b64_tr_b16 %30, %33 offset:3584\n\t"
+            "ds_read_b64_tr_b16 %31, %33 offset:3840\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(lo0[0]), "=&v"(hi0[0]), "=&v"(lo0[1]), "=&v"(hi0[1]), "=&v"(lo0[2]), "=&v"(hi0[2]), "=&v"(lo0[3]), "=&v"(hi0[3]), "=&v"(lo0[4]), "=&v"(hi0[4]), "=&v"(lo0[5]), "=&v"(hi0[5]), "=&v"(lo0[6]), "=&v"(hi0[6]), "=&v"(lo0[7]), "=&v"(hi0[7]), "=&v"(lo1[0]), "=&v"(hi1[0]), "=&v"(lo1[1]), "=&v"(hi1[1]), "=&v"(lo1[2]), "=&v"(hi1[2]), "=&v"(lo1[3]), "=&v"(hi1[3]), "=&v"(lo1[4]), "=&v"(hi1[4]), "=&v"(lo1[5]), "=&v"(hi1[5]), "=&v"(lo1[6]), "=&v"(hi1[6]), "=&v"(lo1[7]), "=&v"(hi1[7])
+            : "v"(a0), "v"(a1)
+            : "memory");
+    }
+};
+template <> struct TrReads2<4> {
+    static __device__ __forceinline__ void run(unsigned a0, unsigned a1, v4s (&lo0)[4], v4s (&hi0)[4],
+                                               v4s (&lo1)[4], v4s (&hi1)[4])
+    {
+        asm volatile(
+            "s_waitcnt expcnt(0)\n\t"
+            "ds_read_b64_tr_b16 %0, %16\n\t"
+            "ds_read_b64_tr_b16 %1, %16 offset:256\n\t"
+            "ds_read_b64_tr_b16 %2, %16 offset:512\n\t"
+            "ds_read_b64_tr_b16 %3, %16 offset:768\n\t"
+            "ds_read_b64_tr_b16 %4, %16 offset:1024\n\t"
+            "ds_read_b64_tr_b16 %5, %16 offset:1280\n\t"
+            "ds_read_b64_tr_b16 %6, %16 offset:1536\n\t"
+            "ds_read_b64_tr_b16 %7, %16 offset:1792\n\t"
+            "ds_read_b64_tr_b16 %8, %17\n\t"
+            "ds_read_b64_tr_b16 %9, %17 offset:256\n\t"
+            "ds_read_b64_tr_b16 %10, %17 offset:512\n\t"
+            "ds_read_b64_tr_b16 %11, %17 offset:768\n\t"
+            "ds_read_b64_tr_b16 %12, %17 offset:1024\n\t"
+            "ds_read_b64_tr_b16 %13, %17 offset:1280\n\t"
+            "ds_read_b64_tr_b16 %14, %17 offset:1536\n\t"
+            "ds_read_b64_tr_b16 %15, %17 offset:1792\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(lo0[0]), "=&v"(hi0[0]), "=&v"(lo0[1]), "=&v"(hi0[1]), "=&v"(lo0[2]), "=&v"(hi0[2]), "=&v"(lo0[3]), "=&v"(hi0[3]), "=&v"(lo1[0]), "=&v"(hi1[0]), "=&v"(lo1[1]), "=&v"(hi1[1]), "=&v"(lo1[2]), "=&v"(hi1[2]), "=&v"(lo1[3]), "=&v"(hi1[3])
+            : "v"(a0), "v"(a1)
+            : "memory");
+    }
+};
+
 // s_waitcnt immediate for vmcnt(n), n < 64 (expcnt and lgkmcnt not waited)
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
 
@@ -643,16 +719,22 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
         // all x fragments of the step first (LDS returns them in order, so the
         // MFMAs only wait for the ones they use)
         v4s afl[MPW][NKS], afh[MPW][NKS];
-#pragma unroll
-        for (int mi = 0; mi < MPW; ++mi) {
+        {
             // lane L of group q reads k-rows q * LPL + 8 ks + (L >> 2) (+4),
             // rows 16 mt + 4 (L & 3) .. +3
-            const int kr = q * LPL + (n >> 2);
-            const int lc = 2 * (mt0 + mi) + ((n & 3) >> 1);  // logical 16-byte chunk
-            const uint8_t* p = tile + kr * TROW + (lc ^ (2 * (q & 1))) * 16 + (n & 1) * 8;
             static_assert(8 * TROW == 512 && 4 * TROW == 256, "read offsets in TrReads");
-            TrReads<NKS>::run((unsigned)(size_t)(__attribute__((address_space(3))) const uint8_t*)p,
-                              afl[mi], afh[mi]);
+            unsigned ad[MPW];
+#pragma unroll
+            for (int mi = 0; mi < MPW; ++mi) {
+                const int kr = q * LPL + (n >> 2);
+                const int lc = 2 * (mt0 + mi) + ((n & 3) >> 1);  // logical 16-byte chunk
+                const uint8_t* p = tile + kr * TROW + (lc ^ (2 * (q & 1))) * 16 + (n & 1) * 8;
+                ad[mi] = (unsigned)(size_t)(__attribute__((address_space(3))) const uint8_t*)p;
+            }
+            if constexpr (MPW == 2)
+                TrReads2<NKS>::run(ad[0], ad[MPW - 1], afl[0], afh[0], afl[MPW - 1], afh[MPW - 1]);
+            else
+                TrReads<NKS>::run(ad[0], afl[0], afh[0]);
         }
         // y^T = R^T . x^T: lane (n, q) of tile (mt, jt) receives
         // y[16 mt + n][16 jt + 4 q + r], r = 0..3 (four consecutive columns of
