@@ -219,3 +219,47 @@ def test_column_major_with_smoothing(dt):
                                               return_rotated=True)
     assert np.array_equal(bits(host(yg)), bits(host(y1)))
     assert np.array_equal(host(c), host(c1)) and np.array_equal(bits(host(s)), bits(host(s1)))
+
+
+@pytest.mark.parametrize("dt,M,K,sm", [
+    ("bf16", 1, 64, 64),          # one row, one group: TW 1, eight rows per block
+    ("f16", 9, 512, 512),         # two rows per block, odd M: a partial block
+    ("bf16", 67, 1024, 1024),     # 16 groups per row: TW 1, one row per block
+    ("f16", 33, 1536, 1536),      # TW 2
+    ("bf16", 130, 4096, 4096),    # 64 groups per row: every lane of TW 4
+    ("bf16", 2600, 3840, 3840),   # more row blocks than waves: each wave takes several
+    ("f16", 300, 3840, 4160),     # strided rows (a column slice of a wider buffer)
+])
+def test_row_major_g64_shapes(dt, M, K, sm):
+    # row-major 16-bit rows with g = 64 (one to four 16-group tiles per row,
+    # one to eight rows per wave, strided rows): the oracle's quantizer must reproduce codes and scales bit for bit from
+    # the exported rotated values, which stay within 1 ulp of the oracle's,
+    # and the codes must not depend on whether the rotated values are exported
+    need_gpu()
+    g = 64
+    buf = _draw(dt, M, sm, seed=M + K)
+    x = dev(buf, dt)[:, :K]
+    assert x.stride() == (sm, 1)
+    R = workloads.asymmetric_rotation(g, seed=5)
+    c, s, yg = w4.w4a4_rotate_quant_rowwise(x, _rot_dev(R), g, return_rotated=True)
+    oc, os2 = oracle.quantize(host(yg), dt)
+    assert np.array_equal(host(c), oc) and np.array_equal(bits(host(s)), bits(os2))
+    yo = oracle.rotate(np.ascontiguousarray(buf[:, :K]), R, g, dt)
+    assert ulp_distance(yo, host(yg), dt).max() <= 1
+    c2, s2 = w4.w4a4_rotate_quant_rowwise(x, _rot_dev(R), g)
+    assert np.array_equal(host(c2), host(c)) and np.array_equal(bits(host(s2)), bits(host(s)))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_row_major_g64_with_smoothing(dt):
+    need_gpu()
+    M, K, g = 50, 2048, 64
+    x = _draw(dt, M, K, seed=13)
+    sm = workloads.f32_to_storage(np.random.default_rng(6).uniform(0.5, 2.0, size=K), dt)
+    R = workloads.hadamard(g)
+    c, s, yg = w4.w4a4_rotate_quant_rowwise(dev(x, dt), _rot_dev(R), g, smooth=dev(sm, dt),
+                                            return_rotated=True)
+    yo = oracle.rotate(oracle.smooth(x, sm, dt), R, g, dt)
+    assert ulp_distance(yo, host(yg), dt).max() <= 1
+    oc, os2 = oracle.quantize(host(yg), dt)
+    assert np.array_equal(host(c), oc) and np.array_equal(bits(host(s)), bits(os2))
