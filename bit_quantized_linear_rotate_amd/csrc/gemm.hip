@@ -13,12 +13,13 @@
 // separately rounded fp32 operation.
 //
 // Design for CDNA4 (two kernels; launch_gemm picks one per call):
-//   * w4a4_gemm_ring3_kernel, for prefill-sized layers: 256 x 256 output tile
-//     per workgroup, one wave per SIMD, each wave a 128 x 128 block of 8 x 8
-//     v_mfma_i32_16x16x64_i8 tiles with its 256 INT32 accumulators in AGPRs.
-//     Codes and packed weights stream global -> LDS through buffer_load ... lds
-//     into a three-stage ring, so two K-steps are in flight while one is
-//     multiplied; the weights are unpacked in registers right before the MFMAs.
+//   * w4a4_gemm_ring3_kernel, for prefill-sized layers: persistent, one
+//     workgroup per CU walking 256 x 256 output tiles; eight waves, two per
+//     SIMD, each a 128 x 64 block of 8 x 4 v_mfma_i32_16x16x64_i8 tiles with
+//     its 128 INT32 accumulators in VGPRs.  Codes and packed weights stream
+//     global -> LDS through buffer_load ... lds into a three-stage ring, so two
+//     K-steps are in flight while one is multiplied; the weights are unpacked
+//     in registers right before the MFMAs.
 //   * w4a4_gemm_kernel, for everything else (decode-sized M, per-64-group
 //     weight scales, the low-rank term, INT32 export, K-chunked runs): 128 x 128
 //     output tile, 4 waves in 2 x 2, each a 64 x 64 block of 4 x 4 MFMA tiles;
