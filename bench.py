@@ -25,6 +25,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -184,7 +185,7 @@ def measure(name, steps, warmup, torch, np, w4, workloads):
     return w, inp, res
 
 
-def cpu_baseline(w, inp, np, target_s=12.0):
+def cpu_baseline(w, inp, np, target_s=15.0):
     """The oracle as it stands, on a bounded sample of rows of the same
     workload (every column, the whole layer per row)."""
     import oracle
@@ -201,7 +202,7 @@ def cpu_baseline(w, inp, np, target_s=12.0):
     fixed = max(t8 - 8 * per_row, 0.0)
     n = int(min(w.M, max(64, (target_s - fixed) / per_row)))
     # when the whole workload takes well under the target, repeat it
-    reps = max(1, int(round(target_s / (fixed + per_row * n))))
+    reps = max(1, int(math.ceil(target_s / (fixed + per_row * n))))
     dt = sum(run(n) for _ in range(reps))
     ops = 2.0 * n * w.N * w.K * reps
     what = (f"all {w.M} rows" if n == w.M else f"first {n} of {w.M} rows") + \
