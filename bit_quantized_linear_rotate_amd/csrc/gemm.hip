@@ -242,6 +242,7 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
 constexpr int BBM = 256, BBN = 256;
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes)
 {
@@ -573,11 +574,110 @@ __global__ void split_epilogue_kernel(GemmArgs a)
         store_any(a.out_dtype, a.out, i, t);
     }
 }
+// -------------------------------------------------------------------------
+// Skinny-M kernel (M <= 64, per-channel weight scales, no K-chunks): the
+// packed-weight stream is the whole cost, so the grid is one 1024-thread
+// workgroup per 16 output columns and its 16 waves split the K steps of 64
+// (wave w takes steps w, w + 16, ...).  A wave issues the code and weight
+// loads of up to SK_MAXS steps at once, straight into registers (buffer loads:
+// rows past M and columns past N read zeros), then multiplies them with
+// v_mfma_i32_16x16x64_i8 (weights unpacked as 16*w).  The 16 partial tiles
+// are summed in LDS as exact integers; one thread per output applies the
+// epilogue.
+// -------------------------------------------------------------------------
+constexpr int SK_WAVES = 16;
+constexpr int SK_MAXS = 4;    // K steps per wave in flight at once
+constexpr int SK_LD = 20;     // LDS row stride of a partial tile, in words
+
+template <int MT>
+__global__ __launch_bounds__(1024) void w4a4_gemm_skinny_kernel(GemmArgs a)
+{
+    __shared__ int32_t part[SK_WAVES][MT * 16 * SK_LD];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int j = lane & 15, kq = lane >> 4;
+    const int64_t M = a.M, K = a.K, N = a.N;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int nsteps = (int)(K / 64);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes, (uint64_t)M * K);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.wp + n0 * (K >> 1), (uint64_t)(N - n0) * (K >> 1));
+    // lane (j, kq): code row mt*16 + j, bytes kq*16 .. +15 of a step; weight
+    // column n0 + j, packed bytes kq*8 .. +7 of a step
+    const int a_off = (int)(j * K + kq * 16);
+    const int w_off = (int)(j * (K >> 1) + kq * 8);
+
+    v4i acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = (v4i){0, 0, 0, 0};
+    for (int s0 = wave; s0 < nsteps; s0 += SK_WAVES * SK_MAXS) {
+        v4u af[SK_MAXS][MT];
+        v2u wf[SK_MAXS];
+#pragma unroll
+        for (int i = 0; i < SK_MAXS; ++i) {
+            const int st = s0 + i * SK_WAVES;
+            const int k0 = st * 64;
+            if (st < nsteps) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    af[i][mt] = __builtin_amdgcn_raw_buffer_load_b128(rc, a_off + (int)(mt * 16 * K) + k0, 0, 0);
+                wf[i] = __builtin_amdgcn_raw_buffer_load_b64(rw, w_off + (k0 >> 1), 0, 0);
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) af[i][mt] = (v4u){0u, 0u, 0u, 0u};
+                wf[i] = (v2u){0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < SK_MAXS; ++i) {
+            uint32_t b0, b1, b2, b3;
+            unpack16(wf[i].x, b0, b1);
+            unpack16(wf[i].y, b2, b3);
+            const v4i bf = (v4i){(int)b0, (int)b1, (int)b2, (int)b3};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, af[i][mt]), bf, acc[mt], 0, 0, 0);
+        }
+    }
+    // lane (j, kq) holds rows 4 kq + r, column j of each 16 x 16 tile
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[wave][(mt * 16 + 4 * kq + r) * SK_LD + j] = acc[mt][r];
+    __syncthreads();
+    if (tid < MT * 16 * 16) {
+        const int m = tid >> 4, n = tid & 15;
+        int32_t sum = 0;
+#pragma unroll
+        for (int w = 0; w < SK_WAVES; ++w) sum += part[w][m * SK_LD + n];
+        const int64_t row = m, col = n0 + n;
+        if (row < M && col < N) {
+            const int32_t iv = sum >> 4;
+            if (a.acc_out) a.acc_out[row * N + col] = iv;
+            float t = mul_rn((float)iv, a.sa[row]);
+            t = mul_rn(t, load_any_f32(a.sw_dtype, a.sw, col));
+            t = epilogue_tail(t, a, row, col);
+            store_any(a.out_dtype, a.out, row * N + col, t);
+        }
+    }
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
 {
     const bool aligned = (a.K % 32) == 0 && ((uintptr_t)a.codes % 16) == 0 &&
                          ((uintptr_t)a.wp % 16) == 0;
     const bool group = a.sw_group > 0;
+    // decode-sized M: the skinny kernel (every epilogue variant but group
+    // scales and K-chunks)
+    if (!group && a.k_chunk == 0 && a.M >= 1 && a.M <= 64 && (a.K % 64) == 0 &&
+        ((uintptr_t)a.codes % 16) == 0 && ((uintptr_t)a.wp % 8) == 0) {
+        const unsigned gx = (unsigned)((a.N + 15) / 16);
+        if (a.M <= 16)
+            hipLaunchKernelGGL(w4a4_gemm_skinny_kernel<1>, dim3(gx), dim3(1024), 0, st, a);
+        else if (a.M <= 32)
+            hipLaunchKernelGGL(w4a4_gemm_skinny_kernel<2>, dim3(gx), dim3(1024), 0, st, a);
+        else
+            hipLaunchKernelGGL(w4a4_gemm_skinny_kernel<4>, dim3(gx), dim3(1024), 0, st, a);
+        return hipGetLastError();
+    }
     // Prefill-sized layers take the 256 x 256 three-stage kernel; everything
     // else (small M, group scales, low-rank term, INT32 export, K chunks,
     // K not a multiple of 128, unaligned operands) the 128 x 128 kernel.

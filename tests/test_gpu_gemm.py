@@ -166,3 +166,57 @@ def test_several_tiles_per_workgroup(M, K, N):
     oacc = oracle.gemm(codes, oracle.unpack(wp, K))
     oout = oracle.epilogue(oacc, sa, sw, "bf16", "bf16", bias=b, bias_dtype="bf16")
     assert np.array_equal(bits(host(out)), bits(oout))
+
+
+SKINNY = [  # (M, K, N): decode-sized M takes the skinny kernel (K % 64 == 0)
+    (1, 64, 16), (16, 192, 200), (17, 3840, 384), (32, 3840, 3840), (33, 640, 129), (64, 4096, 272),
+    (48, 128, 1),
+]
+
+
+@pytest.mark.parametrize("M,K,N", SKINNY)
+@pytest.mark.parametrize("odt", ["f32", "bf16", "f16"])
+def test_skinny_m_bit_exact(M, K, N, odt):
+    # one workgroup per 16 columns, K steps split over 16 waves and summed in
+    # LDS: the INT32 sums and the outputs must still be the oracle's exactly
+    need_gpu()
+    codes, sa, wp, sw, b = _operands(M, K, N, odt, "bf16", seed=M * 3 + K + N)
+    out, acc = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, "bf16"), bias=dev(b, odt),
+                                       out_dtype={"f32": torch.float32, "f16": torch.float16,
+                                                  "bf16": torch.bfloat16}[odt], return_acc=True)
+    oacc = oracle.gemm(codes, oracle.unpack(wp, K))
+    assert np.array_equal(host(acc).astype(np.int64), oacc)
+    oout = oracle.epilogue(oacc, sa, sw, "bf16", odt, bias=b, bias_dtype=odt)
+    assert np.array_equal(bits(host(out)), bits(oout))
+    # without the INT32 export and without bias
+    out2 = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, "bf16"),
+                                   out_dtype={"f32": torch.float32, "f16": torch.float16,
+                                              "bf16": torch.bfloat16}[odt])
+    oout2 = oracle.epilogue(oacc, sa, sw, "bf16", odt)
+    assert np.array_equal(bits(host(out2)), bits(oout2))
+
+
+def test_skinny_m_with_lowrank_term():
+    need_gpu()
+    M, K, N, R = 24, 1024, 96, 32
+    codes, sa, wp, sw, _ = _operands(M, K, N, "bf16", "bf16", bias=False, seed=8)
+    rng = np.random.default_rng(9)
+    L = rng.standard_normal((M, R)).astype(np.float32)
+    up = workloads.f32_to_storage(rng.normal(0, 0.1, size=(N, R)), "bf16")
+    oacc = oracle.gemm(codes, oracle.unpack(wp, K))
+    out = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, "bf16"),
+                                  lora_act=dev(L), proj_up=dev(up, "bf16"), out_dtype=torch.bfloat16)
+    oout = oracle.epilogue(oacc, sa, sw, "bf16", "bf16", L=L, proj_up=up, up_dtype="bf16")
+    assert ulp_distance(host(out), oout, "bf16").max() <= 1
+
+
+def test_skinny_m_equals_large_m_rows():
+    # the first rows of a large-M GEMM (256 x 256 tiles) and the same rows
+    # alone (skinny kernel) are the same bits
+    need_gpu()
+    M, K, N = 512, 3840, 384
+    codes, sa, wp, sw, b = _operands(M, K, N, "bf16", "bf16", seed=21)
+    big = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, "bf16"), bias=dev(b, "bf16"))
+    small = w4.w4a4_gemm_from_codes(dev(codes[:40]), dev(sa[:40]), dev(wp), dev(sw, "bf16"),
+                                    bias=dev(b, "bf16"))
+    assert torch.equal(big[:40].view(torch.int16), small.view(torch.int16))
