@@ -11,6 +11,9 @@ weight / output sets are cycled so that consecutive steps do not find their
 operands in the 256 MB last-level cache.  Each kernel is also timed alone with
 HIP events on the stream it runs on, giving the roofline fractions.
 
+The line also carries the wide-K (K=10240, transposed-view fp16) and the
+decode-like (M=32) workloads, each as a step and per kernel.
+
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload prefill]
                        [--no-cpu] [--no-extra] [--copy-calibration]
 
@@ -167,6 +170,10 @@ def measure(name, steps, warmup, torch, np, w4, workloads):
         gemm(i)
     ms_gemm = _time_loop(gemm, steps, torch)
     ops = 2.0 * M * N * K
+    # bytes the GEMM must move: codes, packed weights, scales, bias, output
+    gemm_bytes = (M * K + N * K // 2 + 4 * M + base["w_scale"].numel() * base["w_scale"].element_size()
+                  + (N * base["bias"].element_size() if base["bias"] is not None else 0)
+                  + M * N * outs[0].element_size())
     res = {
         "workload": f"{name}: M={M} K={K} N={N} g={g} {w.dtype}"
                     + (" transposed-view input" if w.transposed else "")
@@ -178,7 +185,8 @@ def measure(name, steps, warmup, torch, np, w4, workloads):
                          "frac_hbm": rq_bytes / (ms_rq * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "algorithmic_bytes": rq_bytes},
         "gemm": {"ms": ms_gemm, "TOPS": ops / (ms_gemm * 1e-3) / 1e12,
-                 "frac_int8": ops / (ms_gemm * 1e-3) / 1e12 / INT8_PEAK_TOPS, "ops": ops},
+                 "frac_int8": ops / (ms_gemm * 1e-3) / 1e12 / INT8_PEAK_TOPS, "ops": ops,
+                 "GB_s": gemm_bytes / (ms_gemm * 1e-3) / 1e9, "algorithmic_bytes": gemm_bytes},
     }
     if gemm_note:
         res["gemm"]["note"] = gemm_note
@@ -244,10 +252,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w, inp, main_res = measure(args.workload, args.steps, args.warmup, torch, np, w4, workloads)
-    extra = None
+    extras = {}
     if not args.no_extra and args.workload == "prefill":
-        _, _, extra = measure("widek", max(10, args.steps // 2), args.warmup, torch, np, w4,
-                              workloads)
+        for name in ("widek", "decode"):
+            _, _, extras[name] = measure(name, max(10, args.steps // 2), args.warmup, torch, np, w4,
+                                         workloads)
     g = main_res["gemm"]
     line = {
         "metric": METRIC,
@@ -276,13 +285,13 @@ def main():
                                   "traffic": _traffic("rotate_quant", args.workload),
                                   "kernel": "rotate-quant (block rotation on MFMA, row absmax, INT4 codes)"},
     }
-    if extra:
-        line["widek"] = {"workload": extra["workload"], "ms_per_step": round(extra["ms_per_step"], 5),
-                         "tops": round(extra["tops"], 2),
-                         "rotate_quant": {k: (round(v, 4) if isinstance(v, float) else v)
-                                          for k, v in extra["rotate_quant"].items()},
-                         "gemm": {k: (round(v, 4) if isinstance(v, float) else v)
-                                  for k, v in extra["gemm"].items()}}
+    for name, extra in extras.items():
+        line[name] = {"workload": extra["workload"], "ms_per_step": round(extra["ms_per_step"], 5),
+                      "tops": round(extra["tops"], 2),
+                      "rotate_quant": {k: (round(v, 4) if isinstance(v, float) else v)
+                                       for k, v in extra["rotate_quant"].items()},
+                      "gemm": {k: (round(v, 4) if isinstance(v, float) else v)
+                               for k, v in extra["gemm"].items()}}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, inp, np)
     print(json.dumps(line), flush=True)
