@@ -1686,7 +1686,20 @@ hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path)
     }
     if (ok && mfma_lds_bytes(GP, a.K, 1) > 160 * 1024) ok = false;
     const bool contig = a.sk == 1 && (a.sm % 8) == 0 && ((uintptr_t)a.x % 16) == 0;
-    if (ok && contig && GP <= 64 && a.K / GP <= 64 &&
+    // The wave-per-row-block kernel needs many row blocks to keep the GPU
+    // busy (each wave works through its rows alone); with fewer, the
+    // register kernel, which spreads a block's tiles over four waves, is
+    // faster (measured crossover near 1,500 blocks at K/g = 60).
+    bool many_blocks = false;
+    if (GP <= 64 && a.K / GP <= 64) {
+        const int gpr = (int)(a.K / GP);
+        int tw = (gpr + 15) / 16;
+        tw = tw <= 1 ? 1 : tw <= 2 ? 2 : 4;
+        int rpb = (16 * tw) / (gpr > 0 ? gpr : 1);
+        if (rpb < 1) rpb = 1;
+        many_blocks = (a.M + rpb - 1) / rpb >= 1536;
+    }
+    if (ok && contig && GP <= 64 && a.K / GP <= 64 && many_blocks &&
         (a.yout == nullptr || ((uintptr_t)a.yout % 8) == 0) && ((uintptr_t)a.codes % 16) == 0) {
         if (path) *path = 3;
         return a.dtype == BF16 ? launch_wave_dt<BF16>(a, GP, st) : launch_wave_dt<F16>(a, GP, st);
