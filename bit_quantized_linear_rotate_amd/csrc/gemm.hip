@@ -207,9 +207,59 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
         __syncthreads();
     }
 
+    // ---- low-rank term (rank <= 32): the tile's rows of L and columns of
+    // proj_up go to LDS as fp32 (the staging buffers are free after the loop;
+    // ranks padded with zeros to a multiple of 4), and each lane sums
+    // l[m,n] = sum_r L[m,r] * up[n,r] for its outputs, one row block at a
+    // time, in increasing r with fmaf, four terms per read: the same
+    // operations as epilogue_tail
+    constexpr int LDL = 36;  // fp32 row stride: 16-byte reads of 16 columns hit distinct banks
+    static_assert(BM * LDL * 4 <= 2 * BM * LDR && BN * LDL * 4 <= 2 * BN * LDR, "low-rank staging");
+    const bool lds_lora = !SPLIT && a.lora != nullptr && a.rank >= 1 && a.rank <= 32;
+    const float* Ls = (const float*)&As[0][0];
+    const float* Us = (const float*)&Bs[0][0];
+    const int RP = (a.rank + 3) & ~3;
+    if (lds_lora) {
+        float* Lw = (float*)&As[0][0];
+        float* Uw = (float*)&Bs[0][0];
+        const int R = a.rank;
+        for (int i = tid; i < BM * RP; i += 256) {
+            const int rr = i / RP, c = i - rr * RP;
+            const int64_t gm = m0 + rr;
+            Lw[rr * LDL + c] = (gm < M && c < R) ? a.lora[gm * R + c] : 0.0f;
+        }
+        for (int i = tid; i < BN * RP; i += 256) {
+            const int cc = i / RP, c = i - cc * RP;
+            const int64_t gn = n0 + cc;
+            Uw[cc * LDL + c] = (gn < N && c < R) ? load_any_f32(a.up_dtype, a.up, gn * R + c) : 0.0f;
+        }
+        __syncthreads();
+    }
+
     // ---- epilogue: lane (j, q) holds rows 4q..4q+3, column j of each tile.
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
+        float lsum[4][4];
+        if (lds_lora) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) lsum[nt][r] = 0.0f;
+            for (int c4 = 0; c4 < RP; c4 += 4) {
+                v4f lr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    lr[r] = *(const v4f*)(Ls + (wm * 64 + mt * 16 + 4 * q + r) * LDL + c4);
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    const v4f u = *(const v4f*)(Us + (wn * 64 + nt * 16 + j) * LDL + c4);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) lsum[nt][r] = fmaf(lr[r][e], u[e], lsum[nt][r]);
+                }
+            }
+        }
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -231,10 +281,16 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
                         t = mul_rn(t, a.sa[row]);
                         t = mul_rn(t, load_any_f32(a.sw_dtype, a.sw, col));
                     }
-                    t = epilogue_tail(t, a, row, col);
+                    if (lds_lora) {
+                        t = add_rn(t, lsum[nt][r]);
+                        if (a.bias) t = add_rn(t, load_any_f32(a.bias_dtype, a.bias, col));
+                    } else {
+                        t = epilogue_tail(t, a, row, col);
+                    }
                     store_any(a.out_dtype, a.out, row * N + col, t);
                 }
             }
+    }
 }
 
 
