@@ -11,8 +11,9 @@ weight / output sets are cycled so that consecutive steps do not find their
 operands in the 256 MB last-level cache.  Each kernel is also timed alone with
 HIP events on the stream it runs on, giving the roofline fractions.
 
-The line also carries the wide-K (K=10240, transposed-view fp16) and the
-decode-like (M=32) workloads, each as a step and per kernel.
+The line also carries the other four workloads (wide-K transposed-view fp16,
+decode-like M=32, tiny fp32, large-K with smoothing, per-64-group scales and a
+rank-32 term), each as a step and per kernel.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload prefill]
                        [--no-cpu] [--no-extra] [--copy-calibration]
@@ -254,7 +255,7 @@ def main():
     w, inp, main_res = measure(args.workload, args.steps, args.warmup, torch, np, w4, workloads)
     extras = {}
     if not args.no_extra and args.workload == "prefill":
-        for name in ("widek", "decode"):
+        for name in ("widek", "decode", "tiny", "lowrank"):
             _, _, extras[name] = measure(name, max(10, args.steps // 2), args.warmup, torch, np, w4,
                                          workloads)
     g = main_res["gemm"]

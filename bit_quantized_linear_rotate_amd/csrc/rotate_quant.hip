@@ -1346,6 +1346,184 @@ __global__ __launch_bounds__(256, TW >= 4 ? 2 : 3) void rq_wave_kernel(
 }
 
 // -------------------------------------------------------------------------
+// g = 256 on contiguous rows (16-bit, K/256 <= 64 group-rows per row): the
+// rotation's 128 MFMA A fragments (R^T, rounded to T; 128 KB) live in LDS for
+// the life of a persistent workgroup, so each of its eight waves can own one
+// 16-group-row tile of one of its two current rows and apply the whole
+// rotation to it:
+// x is loaded (and smoothed) exactly once, the rotated values stay in
+// registers (two per VGPR), and only the row absmax crosses waves, through
+// LDS with one barrier per row.  The k-slots of each MFMA step are those of
+// the column-major kernel (lane group q, step ks: k = 64 q + 8 ks + e), so
+// the two give the same rotated bits.
+// -------------------------------------------------------------------------
+template <int DT, bool SMOOTH>
+__global__ __launch_bounds__(512) void rq_g256_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t sm,
+    const float* __restrict__ rot, const uint16_t* __restrict__ smooth,
+    int8_t* __restrict__ codes, float* __restrict__ scales, uint16_t* __restrict__ yout)
+{
+    constexpr int GP = 256, CT = 16, NKS = 8, LPL = 64;
+    __shared__ __align__(16) v8s rs[CT * NKS][64];   // fragment (ct, ks), lane-major
+    __shared__ uint32_t wmax[2][8];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wr = wave >> 2, wt = wave & 3;     // row of the pair, tile in the row
+    const int j = lane & 15, q = lane >> 4;
+    const int G = (int)(K / GP);
+    const int ntile = (G + 15) >> 4;
+
+    // R^T fragments: element (kk, c) of R goes to fragment (c / 16, (kk % 64) / 8),
+    // lane (kk / 64) * 16 + c % 16, slot kk % 8 (coalesced reads of R)
+    for (int idx = tid; idx < GP * GP; idx += 512) {
+        const int kk = idx >> 8, c = idx & 255;
+        uint16_t* dst = (uint16_t*)&rs[(c >> 4) * NKS + ((kk & 63) >> 3)][(kk >> 6) * 16 + (c & 15)];
+        dst[kk & 7] = f32_to_h<DT>(rot[idx]);
+    }
+    __syncthreads();
+
+    const int gr = wt * 16 + j;                  // this lane's group-row in the row
+    const bool tlive = wt < ntile && gr < G;
+    const int xo = gr * GP + q * LPL;            // element offset of the lane's slice
+
+    auto load_row = [&](int64_t row, v8s (&xf)[NKS]) {
+        if (tlive && row < M) {
+            const v4i* src = (const v4i*)(x + row * sm + xo);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) xf[ks] = __builtin_bit_cast(v8s, __builtin_nontemporal_load(src + ks));
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) xf[ks] = (v8s){0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    };
+
+    v8s xa[NKS], xb[NKS];
+    int par = 0;
+    const int64_t rstep = 2 * (int64_t)gridDim.x;
+    load_row(2 * (int64_t)blockIdx.x + wr, xa);
+    for (int64_t row0 = 2 * (int64_t)blockIdx.x; row0 < M; row0 += rstep, par ^= 1) {
+        const int64_t row = row0 + wr;
+        const bool live = tlive && row < M;
+        load_row(row + rstep, xb);
+        if constexpr (SMOOTH) {
+            if (live) {
+                const v4i* sp = (const v4i*)(smooth + xo);
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const v8s sv = __builtin_bit_cast(v8s, sp[ks]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        xa[ks][e] = (short)f32_to_h<DT>(h_to_f32<DT>((uint16_t)xa[ks][e]) /
+                                                        h_to_f32<DT>((uint16_t)sv[e]));
+                }
+            }
+        }
+        // rotate: lane (j, q) gets output columns 16 ct + 4 q .. + 3 of
+        // group-row j, rounded to T and packed two per register
+        uint32_t yp[CT][2];
+        uint32_t m = 0u;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const v8s af = rs[ct * NKS + ks][lane];
+                if constexpr (DT == BF16)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, af),
+                                                                  __builtin_bit_cast(v8bf, xa[ks]), acc, 0, 0, 0);
+                else
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, af),
+                                                                 __builtin_bit_cast(v8h, xa[ks]), acc, 0, 0, 0);
+            }
+            uint16_t h[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                h[r] = f32_to_h<DT>(acc[r]);
+                m = max(m, __float_as_uint(h_to_f32<DT>(h[r])) & 0x7fffffffu);
+            }
+            yp[ct][0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+            yp[ct][1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+        }
+        // row absmax: a wave max, then the four waves' through LDS (two
+        // buffers by row parity, so one barrier per row suffices)
+        m = wave_max_dpp(live ? m : 0u);
+        if (lane == 0) wmax[par][wave] = m;
+        __syncthreads();
+        const uint32_t* wm = wmax[par] + 4 * wr;
+        const uint32_t v = max(max(wm[0], wm[1]), max(wm[2], wm[3]));
+        const float sv = row_scale(v);
+        const float ri = 1.0f / sv;
+        if (wt == 0 && lane == 0 && row < M) scales[row] = sv;
+        // quantize: exact division only where a quotient is near a tie or the
+        // scale is not finite
+        const bool fin = fabsf(sv) < 3.0e38f;
+        int8_t* cb = codes + (live ? row : 0) * K + gr * GP;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            float yy[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yy[r] = h_to_f32<DT>((uint16_t)(yp[ct][r >> 1] >> (16 * (r & 1))));
+            uint32_t pk;
+            if (!fin) {
+                pk = quant4_exact(yy, sv);
+            } else {
+                float t[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float qv = yy[r] * ri;
+                    t[r] = __builtin_amdgcn_fmed3f(qv, -7.0f, 7.0f) + kRoundMagic;
+                    const bool nr = fabsf(qv - (t[r] - kRoundMagic)) > 0.5f - 0x1p-17f;
+                    if (__any(nr)) t[r] = __builtin_amdgcn_fmed3f(yy[r] / sv, -7.0f, 7.0f) + kRoundMagic;
+                }
+                pk = pack4_magic(t[0], t[1], t[2], t[3]);
+            }
+            if (live) {
+                *(uint32_t*)(cb + ct * 16 + 4 * q) = pk;
+                if (yout) *(uint2*)(yout + row * K + gr * GP + ct * 16 + 4 * q) = make_uint2(yp[ct][0], yp[ct][1]);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) xa[ks] = xb[ks];
+    }
+}
+
+template <int DT>
+static hipError_t launch_g256_dt(const RQArgs& a, hipStream_t st)
+{
+    static int n_cu = 0;
+    if (n_cu == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n_cu = v;
+        else
+            n_cu = 256;
+    }
+    const int64_t pairs = (a.M + 1) / 2;
+    const int64_t grid = pairs < n_cu ? pairs : n_cu;   // one workgroup per CU (128 KB of LDS)
+    if (a.smooth)
+        hipLaunchKernelGGL((rq_g256_kernel<DT, true>), dim3((unsigned)grid), dim3(512), 0, st, (const uint16_t*)a.x,
+                           a.M, a.K, a.sm, a.rot, (const uint16_t*)a.smooth, a.codes, a.scales, (uint16_t*)a.yout);
+    else
+        hipLaunchKernelGGL((rq_g256_kernel<DT, false>), dim3((unsigned)grid), dim3(512), 0, st, (const uint16_t*)a.x,
+                           a.M, a.K, a.sm, a.rot, (const uint16_t*)a.smooth, a.codes, a.scales, (uint16_t*)a.yout);
+    return hipGetLastError();
+}
+
+// g = 256 with rotation, 16-bit, contiguous 16-byte aligned rows, at most 64
+// group-rows per row, 4-byte aligned codes, 8-byte aligned rotated export,
+// 16-byte aligned smoothing factors.
+static bool g256_ok(const RQArgs& a)
+{
+    const bool sixteen = a.dtype == F16 || a.dtype == BF16;
+    if (!sixteen || !a.rot || a.g != 256 || a.M <= 0 || a.sk != 1) return false;
+    if ((a.K % 256) != 0 || a.K / 256 > 64 || (a.sm % 8) != 0 || ((uintptr_t)a.x % 16) != 0) return false;
+    if (((uintptr_t)a.codes % 4) != 0 || (a.yout && ((uintptr_t)a.yout % 8) != 0)) return false;
+    if (a.smooth && ((uintptr_t)a.smooth % 16) != 0) return false;
+    return true;
+}
+
+// -------------------------------------------------------------------------
 // Generic path (fp32 activations, or shapes the MFMA path does not take):
 // one workgroup per row, the (smoothed) row staged in LDS as fp32, the
 // rotation evaluated on VALU twice (absmax pass, then quantize pass) as an
@@ -1683,6 +1861,10 @@ hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path)
     if (colmajor_ok(a)) {
         if (path) *path = 4;
         return a.dtype == BF16 ? launch_colmajor_dt<BF16>(a, st) : launch_colmajor_dt<F16>(a, st);
+    }
+    if (g256_ok(a)) {
+        if (path) *path = 5;
+        return a.dtype == BF16 ? launch_g256_dt<BF16>(a, st) : launch_g256_dt<F16>(a, st);
     }
     if (ok && mfma_lds_bytes(GP, a.K, 1) > 160 * 1024) ok = false;
     const bool contig = a.sk == 1 && (a.sm % 8) == 0 && ((uintptr_t)a.x % 16) == 0;
