@@ -19,6 +19,10 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
+# per-source extra flags: the GEMM kernels' MFMA results live in ordinary
+# VGPRs (the group-scale loop converts every result with VALU instructions,
+# which cannot read accumulation registers)
+SOURCE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:
@@ -28,7 +32,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for src in SOURCES:
         obj = os.path.join(CSRC, "_build", src.replace(".hip", ".o"))
         os.makedirs(os.path.dirname(obj), exist_ok=True)
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True)))

@@ -40,6 +40,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace w4a4 {
 
 constexpr int BM = 128, BN = 128, BK = 64, LDR = 80;
@@ -65,9 +67,12 @@ __device__ __forceinline__ float epilogue_tail(float t, const GemmArgs& a, int64
     return t;
 }
 
-template <bool GROUP, bool SPLIT, bool ALIGNED>
+// GSW: -1 for one weight scale per column, else the dtype of the per-64-group
+// weight scales (F32, F16 or BF16)
+template <int GSW, bool SPLIT, bool ALIGNED>
 __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
 {
+    constexpr bool GROUP = GSW >= 0;
     __shared__ __align__(16) int8_t As[2][BM * LDR];
     __shared__ __align__(16) int8_t Bs[2][BN * LDR];
 
@@ -162,49 +167,88 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
             for (int nt = 0; nt < 4; ++nt) facc[mt][nt] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
 
-    if (nsteps > 0) {
-        gload(kbeg);
-        sstore(0);
-    }
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nsteps) gload(kbeg + (int64_t)(s + 1) * BK);
-        v4i af[4], bf[4];
+    uint32_t scol[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            af[mt] = *(const v4i*)(&As[buf][(wm * 64 + mt * 16 + j) * LDR + q * 16]);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-            bf[nt] = *(const v4i*)(&Bs[buf][(wn * 64 + nt * 16 + j) * LDR + q * 16]);
-        if constexpr (GROUP) {
-            const int64_t gidx = (kbeg + (int64_t)s * BK) / 64;
-            float swv[4];
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int64_t col = n0 + wn * 64 + nt * 16 + j;
-                swv[nt] = col < N ? load_any_f32(a.sw_dtype, a.sw, gidx * N + col) : 0.0f;
-            }
+    for (int nt = 0; nt < 4; ++nt)
+        scol[nt] = (uint32_t)min(n0 + wn * 64 + nt * 16 + j, N - 1);
+
+    // The K loop. With group scales the MFMA sums carry the weights' factor
+    // 16 (high-nibble unpack); FAST multiplies float(16 s) by scale / 16,
+    // which is the same real number as s * scale and so rounds to the same
+    // float, whenever scale / 16 is exact (every scale but subnormal or NaN
+    // ones). It returns false if some scale was not; the workgroup then runs
+    // the loop again with the shift back to s.
+    auto kloop = [&](auto fast_c) -> bool {
+        constexpr bool FAST = decltype(fast_c)::value;
+        bool exact = true;
+        if (nsteps > 0) {
+            gload(kbeg);
+            sstore(0);
+        }
+        __syncthreads();
+        for (int s = 0; s < nsteps; ++s) {
+            const int buf = s & 1;
+            if (s + 1 < nsteps) gload(kbeg + (int64_t)(s + 1) * BK);
+            v4i af[4], bf[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
+                af[mt] = *(const v4i*)(&As[buf][(wm * 64 + mt * 16 + j) * LDR + q * 16]);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                bf[nt] = *(const v4i*)(&Bs[buf][(wn * 64 + nt * 16 + j) * LDR + q * 16]);
+            if constexpr (GROUP) {
+                // this step's group scales for the lane's four columns (columns
+                // past N read column N - 1; their sums are never stored)
+                const int64_t gidx = (kbeg + (int64_t)s * BK) / 64;
+                float swv[4];
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
-                    v4i t = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt], bf[nt], (v4i){0, 0, 0, 0},
-                                                                  0, 0, 0);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        facc[mt][nt][r] = add_rn(facc[mt][nt][r], mul_rn((float)(t[r] >> 4), swv[nt]));
+                    float v;
+                    if constexpr (GSW == F32)
+                        v = ((const float*)a.sw + gidx * N)[scol[nt]];
+                    else
+                        v = h_to_f32<GSW>(((const uint16_t*)a.sw + gidx * N)[scol[nt]]);
+                    if constexpr (FAST) {
+                        swv[nt] = v * 0.0625f;
+                        exact = exact && swv[nt] * 16.0f == v;
+                    } else {
+                        swv[nt] = v;
+                    }
                 }
-        } else {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) {
+                        v4i t = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt], bf[nt], (v4i){0, 0, 0, 0},
+                                                                      0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            facc[mt][nt][r] = add_rn(facc[mt][nt][r],
+                                                     mul_rn((float)(FAST ? t[r] : t[r] >> 4), swv[nt]));
+                    }
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt)
+                        acc[mt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt], bf[nt], acc[mt][nt],
+                                                                            0, 0, 0);
+            }
+            if (s + 1 < nsteps) sstore(buf ^ 1);
+            __syncthreads();
+        }
+        return exact;
+    };
+    if constexpr (GROUP) {
+        if (__syncthreads_or(!kloop(std::true_type{}))) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt], bf[nt], acc[mt][nt],
-                                                                        0, 0, 0);
+                for (int nt = 0; nt < 4; ++nt) facc[mt][nt] = (v4f){0.f, 0.f, 0.f, 0.f};
+            kloop(std::false_type{});
         }
-        if (s + 1 < nsteps) sstore(buf ^ 1);
-        __syncthreads();
+    } else {
+        kloop(std::false_type{});
     }
 
     // ---- low-rank term (rank <= 32): the tile's rows of L and columns of
@@ -771,28 +815,35 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
         const int64_t n = a.M * a.N;
         hipLaunchKernelGGL(fill_zero_i64, dim3(1024), dim3(256), 0, st, a.acc64, n);
         if (aligned)
-            hipLaunchKernelGGL((w4a4_gemm_kernel<false, true, true>), dim3(gx, gy, gz), dim3(256), 0,
+            hipLaunchKernelGGL((w4a4_gemm_kernel<-1, true, true>), dim3(gx, gy, gz), dim3(256), 0,
                                st, a, kc);
         else
-            hipLaunchKernelGGL((w4a4_gemm_kernel<false, true, false>), dim3(gx, gy, gz), dim3(256), 0,
+            hipLaunchKernelGGL((w4a4_gemm_kernel<-1, true, false>), dim3(gx, gy, gz), dim3(256), 0,
                                st, a, kc);
         hipLaunchKernelGGL(split_epilogue_kernel, dim3(2048), dim3(256), 0, st, a);
         return hipGetLastError();
     }
     const int64_t kc = a.K;
     if (group) {
-        if (aligned)
-            hipLaunchKernelGGL((w4a4_gemm_kernel<true, false, true>), dim3(gx, gy, 1), dim3(256), 0,
-                               st, a, kc);
-        else
-            hipLaunchKernelGGL((w4a4_gemm_kernel<true, false, false>), dim3(gx, gy, 1), dim3(256), 0,
-                               st, a, kc);
+#define W4A4_GROUP_LAUNCH(DT)                                                                    \
+    do {                                                                                         \
+        if (aligned)                                                                             \
+            hipLaunchKernelGGL((w4a4_gemm_kernel<DT, false, true>), dim3(gx, gy, 1), dim3(256), 0, \
+                               st, a, kc);                                                       \
+        else                                                                                     \
+            hipLaunchKernelGGL((w4a4_gemm_kernel<DT, false, false>), dim3(gx, gy, 1), dim3(256), \
+                               0, st, a, kc);                                                    \
+    } while (0)
+        if (a.sw_dtype == F32) W4A4_GROUP_LAUNCH(F32);
+        else if (a.sw_dtype == F16) W4A4_GROUP_LAUNCH(F16);
+        else W4A4_GROUP_LAUNCH(BF16);
+#undef W4A4_GROUP_LAUNCH
     } else {
         if (aligned)
-            hipLaunchKernelGGL((w4a4_gemm_kernel<false, false, true>), dim3(gx, gy, 1), dim3(256), 0,
+            hipLaunchKernelGGL((w4a4_gemm_kernel<-1, false, true>), dim3(gx, gy, 1), dim3(256), 0,
                                st, a, kc);
         else
-            hipLaunchKernelGGL((w4a4_gemm_kernel<false, false, false>), dim3(gx, gy, 1), dim3(256), 0,
+            hipLaunchKernelGGL((w4a4_gemm_kernel<-1, false, false>), dim3(gx, gy, 1), dim3(256), 0,
                                st, a, kc);
     }
     return hipGetLastError();

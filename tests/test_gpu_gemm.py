@@ -113,6 +113,39 @@ def test_group_scales_and_lowrank(M, K, N):
     assert ulp_distance(host(out), oout, "bf16").max() <= 1
 
 
+@pytest.mark.parametrize("sw_dt", ["f32", "bf16", "f16"])
+def test_group_scales_every_scale_dtype(sw_dt):
+    need_gpu()
+    M, K, N = 150, 1024, 260
+    codes, sa, wp, sw, b = _operands(M, K, N, "f32", sw_dt, group=64, seed=21)
+    out = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, sw_dt), w_scale_group=64,
+                                  bias=dev(b, "f32"), out_dtype=torch.float32)
+    parts = oracle.gemm(codes, oracle.unpack(wp, K), group=64)
+    oout = oracle.epilogue(parts, sa, sw, sw_dt, "f32", group=64, bias=b, bias_dtype="f32")
+    assert np.array_equal(bits(host(out)), bits(oout))
+
+
+def test_group_scales_below_2_pow_minus_122():
+    """fp32 group scales so small that scale / 16 is not exact: the workgroups
+    that meet one redo their K loop in the exact form; results stay bit-exact."""
+    need_gpu()
+    M, K, N = 150, 1024, 260
+    codes, sa, wp, sw, _ = _operands(M, K, N, "f32", "f32", group=64, seed=22)
+    rng = np.random.default_rng(23)
+    sw = sw.copy()
+    sw[:, 7] = rng.uniform(1e-40, 1e-37, size=K // 64).astype(np.float32)  # one whole column
+    sw[5, 200] = np.float32(3.3e-39)                                      # one entry elsewhere
+    parts = oracle.gemm(codes, oracle.unpack(wp, K), group=64)
+    # the planted scales do make float(16 s) * (scale / 16) differ from s * scale
+    s7 = parts[:, :, 7].astype(np.float32)
+    q7 = (sw[:, 7] * np.float32(0.0625)).astype(np.float32)
+    assert not np.array_equal((s7 * np.float32(16)) * q7[None, :], s7 * sw[:, 7][None, :])
+    out = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, "f32"), w_scale_group=64,
+                                  out_dtype=torch.float32)
+    oout = oracle.epilogue(parts, sa, sw, "f32", "f32", group=64)
+    assert np.array_equal(bits(host(out)), bits(oout))
+
+
 def test_lowrank_down_matches_oracle():
     need_gpu()
     rng = np.random.default_rng(8)
