@@ -75,6 +75,7 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
     constexpr bool GROUP = GSW >= 0;
     __shared__ __align__(16) int8_t As[2][BM * LDR];
     __shared__ __align__(16) int8_t Bs[2][BN * LDR];
+    __shared__ __align__(16) float Ss[GSW >= 0 ? 2 : 1][GSW >= 0 ? 256 : 4];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -167,11 +168,6 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
             for (int nt = 0; nt < 4; ++nt) facc[mt][nt] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
 
-    uint32_t scol[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-        scol[nt] = (uint32_t)min(n0 + wn * 64 + nt * 16 + j, N - 1);
-
     // The K loop. With group scales the MFMA sums carry the weights' factor
     // 16 (high-nibble unpack); FAST multiplies float(16 s) by scale / 16,
     // which is the same real number as s * scale and so rounds to the same
@@ -181,14 +177,48 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
     auto kloop = [&](auto fast_c) -> bool {
         constexpr bool FAST = decltype(fast_c)::value;
         bool exact = true;
+        // Group scales ride the operand pipeline: thread t loads the scale of
+        // column c(t) = (t / 64 % 2) * 64 + (t % 4) * 16 + (t / 4) % 16 with its
+        // step's operands and stores it to LDS at slot t (FAST: divided by 16
+        // and checked), so that a lane's four columns are one 16-byte read.
+        // Threads 128..255 repeat threads 0..127 (no branch: a branch here
+        // lets the compiler sink the MFMA conversions past the operand wait).
+        // Columns past N read column N - 1 and steps past the end the last
+        // group: those values are never used.
+        uint32_t rsw = 0;
+        const int scl = ((tid >> 6) & 1) * 64 + (tid & 3) * 16 + ((tid >> 2) & 15);
+        const uint32_t sc = (uint32_t)min(n0 + scl, N - 1);
+        auto sgload = [&](int step) {
+            if constexpr (GROUP) {
+                const int64_t gidx = min((kbeg + (int64_t)step * BK) / 64, (K + 63) / 64 - 1);
+                if constexpr (GSW == F32) rsw = ((const uint32_t*)a.sw + gidx * N)[sc];
+                else rsw = ((const uint16_t*)a.sw + gidx * N)[sc];
+            }
+        };
+        auto ssstore = [&](int buf) {
+            if constexpr (GROUP) {
+                const float v = GSW == F32 ? __uint_as_float(rsw) : h_to_f32<GSW>((uint16_t)rsw);
+                float w = v;
+                if constexpr (FAST) {
+                    w = v * 0.0625f;
+                    exact = exact && w * 16.0f == v;
+                }
+                Ss[buf][tid] = w;
+            }
+        };
         if (nsteps > 0) {
+            sgload(0);
             gload(kbeg);
             sstore(0);
+            ssstore(0);
         }
         __syncthreads();
         for (int s = 0; s < nsteps; ++s) {
             const int buf = s & 1;
-            if (s + 1 < nsteps) gload(kbeg + (int64_t)(s + 1) * BK);
+            // (past the last step the loads are masked off and the stores
+            // fill the idle buffer with zeros: no branch in the loop)
+            sgload(s + 1);
+            gload(kbeg + (int64_t)(s + 1) * BK);
             v4i af[4], bf[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
@@ -197,24 +227,7 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
             for (int nt = 0; nt < 4; ++nt)
                 bf[nt] = *(const v4i*)(&Bs[buf][(wn * 64 + nt * 16 + j) * LDR + q * 16]);
             if constexpr (GROUP) {
-                // this step's group scales for the lane's four columns (columns
-                // past N read column N - 1; their sums are never stored)
-                const int64_t gidx = (kbeg + (int64_t)s * BK) / 64;
-                float swv[4];
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    float v;
-                    if constexpr (GSW == F32)
-                        v = ((const float*)a.sw + gidx * N)[scol[nt]];
-                    else
-                        v = h_to_f32<GSW>(((const uint16_t*)a.sw + gidx * N)[scol[nt]]);
-                    if constexpr (FAST) {
-                        swv[nt] = v * 0.0625f;
-                        exact = exact && swv[nt] * 16.0f == v;
-                    } else {
-                        swv[nt] = v;
-                    }
-                }
+                const v4f swv = *(const v4f*)(&Ss[buf][(wn * 16 + j) * 4]);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -226,6 +239,15 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
                             facc[mt][nt][r] = add_rn(facc[mt][nt][r],
                                                      mul_rn((float)(FAST ? t[r] : t[r] >> 4), swv[nt]));
                     }
+                if constexpr (FAST) {
+                    // one MFMA, then twelve VALU instructions (converting an
+                    // earlier result), sixteen times
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+                    }
+                }
             } else {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
@@ -234,7 +256,8 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
                         acc[mt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt], bf[nt], acc[mt][nt],
                                                                             0, 0, 0);
             }
-            if (s + 1 < nsteps) sstore(buf ^ 1);
+            sstore(buf ^ 1);
+            ssstore(buf ^ 1);
             __syncthreads();
         }
         return exact;
