@@ -191,6 +191,25 @@ def measure(name, steps, warmup, torch, np, w4, workloads):
     }
     if gemm_note:
         res["gemm"]["note"] = gemm_note
+    if rank:
+        # low-rank down projection alone (the first kernel of a low-rank step)
+        lbufs = [torch.empty((M, rank), dtype=torch.float32, device="cuda") for _ in sets]
+
+        def lrd(i):
+            s = sets[i % 4]
+            x = s["x"]
+            lib.w4a4_lowrank_down(
+                ctypes.c_void_p(x.data_ptr()), {torch.bfloat16: 2, torch.float16: 1, torch.float32: 0}[x.dtype],
+                M, K, x.stride(0), x.stride(1), ctypes.c_void_p(s["proj_down"].data_ptr()), rank,
+                ctypes.c_void_p(lbufs[i % 4].data_ptr()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+
+        for i in range(warmup):
+            lrd(i)
+        ms_lrd = _time_loop(lrd, steps, torch)
+        lrd_bytes = M * K * base["x"].element_size() + K * rank * base["proj_down"].element_size() + 4 * M * rank
+        res["lowrank_down"] = {"ms": ms_lrd, "GB_s": lrd_bytes / (ms_lrd * 1e-3) / 1e9,
+                               "frac_hbm": lrd_bytes / (ms_lrd * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                               "algorithmic_bytes": lrd_bytes}
     return w, inp, res
 
 
@@ -293,6 +312,9 @@ def main():
                                        for k, v in extra["rotate_quant"].items()},
                       "gemm": {k: (round(v, 4) if isinstance(v, float) else v)
                                for k, v in extra["gemm"].items()}}
+        if "lowrank_down" in extra:
+            line[name]["lowrank_down"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                          for k, v in extra["lowrank_down"].items()}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, inp, np)
     print(json.dumps(line), flush=True)

@@ -62,6 +62,97 @@ __global__ __launch_bounds__(256) void lowrank_mfma_kernel(
     }
 }
 
+// Wide variant for rank == RT (16, 32 or 64) and a 16-byte aligned proj_down:
+// one workgroup of sixteen waves per 16 rows (one workgroup per CU at
+// prefill sizes, four waves per SIMD). Wave w takes the 32-deep K slices
+// w, w + 16, w + 32, ...; a slice of proj_down (32 x RT values, contiguous)
+// is read with 16-byte loads and transposed through a wave-private LDS tile
+// into the MFMA's B layout (a lane holds eight consecutive k of one column),
+// four slices' loads in flight at a time. The sixteen partial sums are added
+// in wave order through LDS.
+template <int DT, int RT>
+__global__ __launch_bounds__(1024) void lowrank_wide_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t sm,
+    const uint16_t* __restrict__ down, float* __restrict__ L)
+{
+    constexpr int NCT = RT / 16;  // 16-column MFMA tiles
+    constexpr int NLD = RT / 16;  // 16-byte proj_down loads per lane per slice
+    constexpr int DP = 40;        // LDS pitch (values) of a transposed column
+    constexpr int UNR = 4;        // slices in flight
+    constexpr int TILE_B = RT * DP * 2;
+    constexpr int PART_B = 16 * 16 * (RT + 1) * 4;
+    constexpr int SMEM_B = 16 * TILE_B > PART_B ? 16 * TILE_B : PART_B;
+    __shared__ __align__(16) unsigned char smem[SMEM_B];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int j = lane & 15, q = lane >> 4;
+    uint16_t* Dw = (uint16_t*)(smem + wave * TILE_B);
+    const int64_t m0 = (int64_t)blockIdx.x * 16;
+    const int64_t row = m0 + j;
+    const int64_t nsl = K / 32;
+
+    v4f acc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t t0 = wave; t0 < nsl; t0 += 16 * UNR) {
+        uint4 xa[UNR], da[UNR][NLD];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int64_t t = t0 + 16 * u;
+            const bool ok = t < nsl;
+            xa[u] = make_uint4(0, 0, 0, 0);
+            if (ok && row < M) xa[u] = *(const uint4*)(x + row * sm + t * 32 + q * 8);
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                da[u][i] = make_uint4(0, 0, 0, 0);
+                if (ok) da[u][i] = *(const uint4*)(down + t * 32 * RT + lane * 8 + i * 512);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            // value e of this lane's load i is proj_down[k = e0 / RT][c0 + e]
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const int e0 = lane * 8 + i * 512;
+                const int kl = e0 / RT, c0 = e0 % RT;
+                const uint32_t w[4] = {da[u][i].x, da[u][i].y, da[u][i].z, da[u][i].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    Dw[(c0 + e) * DP + kl] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const v8s bf = *(const v8s*)(&Dw[(ct * 16 + j) * DP + q * 8]);
+                const v8s af = __builtin_bit_cast(v8s, xa[u]);
+                if constexpr (DT == BF16)
+                    acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(v8bf, af), __builtin_bit_cast(v8bf, bf), acc[ct], 0, 0, 0);
+                else
+                    acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(v8h, af), __builtin_bit_cast(v8h, bf), acc[ct], 0, 0, 0);
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+    __syncthreads();
+    float* part = (float*)smem;  // [16 waves][16 rows][RT + 1]
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[(wave * 16 + 4 * q + r) * (RT + 1) + ct * 16 + j] = acc[ct][r];
+    __syncthreads();
+    if (tid < 16 * RT) {
+        const int rr = tid / RT, c = tid % RT;
+        if (m0 + rr < M) {
+            float s = part[rr * (RT + 1) + c];
+            for (int w = 1; w < 16; ++w) s = add_rn(s, part[(w * 16 + rr) * (RT + 1) + c]);
+            L[(m0 + rr) * RT + c] = s;
+        }
+    }
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void lowrank_generic_kernel(
     const void* __restrict__ x, int64_t M, int64_t K, int64_t sm, int64_t sk,
@@ -81,6 +172,23 @@ hipError_t launch_lowrank_down(const LowRankArgs& a, hipStream_t st)
 {
     const bool mf = (a.dtype == BF16 || a.dtype == F16) && a.sk == 1 && (a.sm % 8) == 0 &&
                     (a.K % 32) == 0 && ((uintptr_t)a.x % 16) == 0 && a.rank <= 64;
+    if (mf && (a.rank == 16 || a.rank == 32 || a.rank == 64) && ((uintptr_t)a.down % 16) == 0) {
+        const unsigned grid = (unsigned)((a.M + 15) / 16);
+#define W4A4_LRW(DTV, RTV)                                                                        \
+    hipLaunchKernelGGL((lowrank_wide_kernel<DTV, RTV>), dim3(grid), dim3(1024), 0, st,           \
+                       (const uint16_t*)a.x, a.M, a.K, a.sm, (const uint16_t*)a.down, a.lora)
+        if (a.dtype == BF16) {
+            if (a.rank == 16) W4A4_LRW(BF16, 16);
+            else if (a.rank == 32) W4A4_LRW(BF16, 32);
+            else W4A4_LRW(BF16, 64);
+        } else {
+            if (a.rank == 16) W4A4_LRW(F16, 16);
+            else if (a.rank == 32) W4A4_LRW(F16, 32);
+            else W4A4_LRW(F16, 64);
+        }
+#undef W4A4_LRW
+        return hipGetLastError();
+    }
     if (mf) {
         const unsigned grid = (unsigned)((a.M + 15) / 16);
         const int rt = a.rank <= 16 ? 16 : a.rank <= 32 ? 32 : 64;

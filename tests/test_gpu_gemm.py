@@ -149,7 +149,12 @@ def test_group_scales_below_2_pow_minus_122():
 def test_lowrank_down_matches_oracle():
     need_gpu()
     rng = np.random.default_rng(8)
-    for dt, M, K, R in [("bf16", 37, 2048, 32), ("f16", 16, 512, 16), ("f32", 5, 256, 8)]:
+    # ranks 16/32/64 take the sixteen-wave kernel (K slices of 32, four in
+    # flight per wave; K = 2080 leaves a ragged last round), other ranks the
+    # four-wave one, fp32 the plain loop
+    for dt, M, K, R in [("bf16", 37, 2048, 32), ("f16", 16, 512, 16), ("f32", 5, 256, 8),
+                        ("bf16", 100, 2080, 64), ("f16", 33, 16384, 32), ("bf16", 20, 96, 16),
+                        ("bf16", 40, 1024, 20), ("f16", 17, 544, 48)]:
         x = workloads.f32_to_storage(rng.standard_normal((M, K)), dt)
         down = workloads.f32_to_storage(rng.standard_normal((K, R)) / np.sqrt(K), dt)
         L = host(w4.w4a4_lowrank_down(dev(x, dt), dev(down, dt)))
