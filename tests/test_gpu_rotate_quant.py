@@ -206,13 +206,31 @@ def test_column_major_views_match_contiguous(dt, g, M, K):
     assert np.array_equal(host(c2), host(c)) and np.array_equal(bits(host(s2)), bits(host(s)))
 
 
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
-def test_column_major_with_smoothing(dt):
+@pytest.mark.parametrize("dt,M,K,edge", [
+    ("f16", 48, 1024, False), ("bf16", 48, 1024, False),
+    # about a million smoothed values: a few hundred products land near a
+    # rounding boundary of T, where the row-major kernel divides instead
+    ("bf16", 64, 16384, False), ("f16", 128, 8192, False),
+    # zeros in x, subnormal and huge smoothing factors
+    ("bf16", 48, 2048, True), ("f16", 48, 2048, True),
+])
+def test_column_major_with_smoothing(dt, M, K, edge):
+    """The contiguous copy takes the row-major kernel (product with a reciprocal,
+    division near rounding boundaries), the transposed view the column-major one
+    (IEEE division everywhere): the same bits."""
     need_gpu()
-    M, K, g = 48, 1024, 256
+    g = 256
     buf = _draw(dt, K, M, seed=21)
+    sm = np.random.default_rng(4).uniform(0.5, 2.0, size=K)
+    if edge:
+        buf = buf.copy()
+        buf[::7, ::5] = 0
+        tiny, huge = (1e-40, 2.0 ** 120) if dt == "bf16" else (3e-7, 6e4)
+        sm[::11] = tiny          # (buf is x transposed: its row k is column k of x)
+        buf[::11, :] = 0         # 0 / tiny = 0, with no overflow into the rotation
+        sm[5::13] = huge
+    sm = workloads.f32_to_storage(sm, dt)
     xt = dev(buf, dt).t()
-    sm = workloads.f32_to_storage(np.random.default_rng(4).uniform(0.5, 2.0, size=K), dt)
     R = workloads.hadamard(g)
     c, s, yg = w4.w4a4_rotate_quant_rowwise(xt, _rot_dev(R), g, smooth=dev(sm, dt), return_rotated=True)
     c1, s1, y1 = w4.w4a4_rotate_quant_rowwise(xt.contiguous(), _rot_dev(R), g, smooth=dev(sm, dt),
