@@ -67,6 +67,13 @@ __device__ __forceinline__ float epilogue_tail(float t, const GemmArgs& a, int64
     return t;
 }
 
+// Buffer resource over `bytes` bytes at `base`: loads past the end read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes)
+{
+    const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, 0x00020000);
+}
+
 // GSW: -1 for one weight scale per column, else the dtype of the per-64-group
 // weight scales (F32, F16 or BF16)
 template <int GSW, bool SPLIT, bool ALIGNED>
@@ -105,7 +112,27 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
     // global -> register staging
     uint4 ra[2];
     uint4 rw;
+    // ALIGNED without K-chunks (K % 64 == 0): buffer loads over the tile's
+    // code rows and weight columns, fixed lane offsets plus the step's k as the
+    // scalar offset; rows past M and columns past N read zeros (a load past
+    // the last step reads the next row, and only fills the idle buffer)
+    constexpr bool BUF = ALIGNED && !SPLIT;
+    const __amdgpu_buffer_rsrc_t rca =
+        make_rsrc(a.codes + (m0 < M ? m0 : 0) * K, (uint64_t)(m0 < M ? min(M - m0, (int64_t)BM) : 0) * K);
+    const __amdgpu_buffer_rsrc_t rcw = make_rsrc(
+        a.wp + (n0 < N ? n0 : 0) * (K >> 1), (uint64_t)(n0 < N ? min(N - n0, (int64_t)BN) : 0) * (K >> 1));
     auto gload = [&](int64_t k) {
+        if constexpr (BUF) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int c = tid + 256 * i;
+                ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rca, (int)((c >> 2) * K + (c & 3) * 16), (int)k, 0));
+            }
+            rw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                rcw, (int)((tid >> 1) * (K >> 1) + (tid & 1) * 16), (int)(k >> 1), 0));
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int c = tid + 256 * i;
@@ -256,6 +283,9 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
                         acc[mt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt], bf[nt], acc[mt][nt],
                                                                             0, 0, 0);
             }
+            // (keep the stores after the MFMAs and conversions: they wait for
+            // this step's loads)
+            __builtin_amdgcn_sched_barrier(0);
             sstore(buf ^ 1);
             ssstore(buf ^ 1);
             __syncthreads();
@@ -367,11 +397,6 @@ constexpr int BBM = 256, BBN = 256;
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes)
-{
-    const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, 0x00020000);
-}
 
 // -------------------------------------------------------------------------
 // Three-stage persistent kernel (per-channel scales, M > 128, K % 128 == 0):
@@ -847,10 +872,13 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
         return hipGetLastError();
     }
     const int64_t kc = a.K;
+    // (the aligned kernels without K-chunks stage through buffer loads that
+    // need whole 64-deep K steps and 32-bit offsets within a 128-row tile)
+    const bool aligned_buf = aligned && (a.K % 64) == 0 && a.K <= (1 << 24);
     if (group) {
 #define W4A4_GROUP_LAUNCH(DT)                                                                    \
     do {                                                                                         \
-        if (aligned)                                                                             \
+        if (aligned_buf)                                                                         \
             hipLaunchKernelGGL((w4a4_gemm_kernel<DT, false, true>), dim3(gx, gy, 1), dim3(256), 0, \
                                st, a, kc);                                                       \
         else                                                                                     \
@@ -862,7 +890,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
         else W4A4_GROUP_LAUNCH(BF16);
 #undef W4A4_GROUP_LAUNCH
     } else {
-        if (aligned)
+        if (aligned_buf)
             hipLaunchKernelGGL((w4a4_gemm_kernel<-1, false, true>), dim3(gx, gy, 1), dim3(256), 0,
                                st, a, kc);
         else
