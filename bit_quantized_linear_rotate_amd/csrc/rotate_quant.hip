@@ -1388,9 +1388,12 @@ __global__ __launch_bounds__(512) void rq_g256_kernel(
 
     auto load_row = [&](int64_t row, v8s (&xf)[NKS]) {
         if (tlive && row < M) {
+            // plain loads: each lane reads one whole 128-byte line in eight
+            // 16-byte pieces, and only a cached line serves the later seven
+            // (non-temporal loads sent every piece to L2)
             const v4i* src = (const v4i*)(x + row * sm + xo);
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) xf[ks] = __builtin_bit_cast(v8s, __builtin_nontemporal_load(src + ks));
+            for (int ks = 0; ks < NKS; ++ks) xf[ks] = __builtin_bit_cast(v8s, src[ks]);
         } else {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) xf[ks] = (v8s){0, 0, 0, 0, 0, 0, 0, 0};
