@@ -67,7 +67,8 @@ __global__ __launch_bounds__(256) void lowrank_mfma_kernel(
 // prefill sizes, four waves per SIMD). Wave w takes the 32-deep K slices
 // w, w + 16, w + 32, ...; a slice of proj_down (32 x RT values, contiguous)
 // is read with 16-byte loads and transposed through a wave-private LDS tile
-// into the MFMA's B layout (a lane holds eight consecutive k of one column),
+// into the MFMA's B layout (a lane holds eight consecutive k of one column,
+// 16-byte chunks swizzled per column),
 // four slices' loads in flight at a time. The sixteen partial sums are added
 // in wave order through LDS.
 template <int DT, int RT>
@@ -87,6 +88,10 @@ __global__ __launch_bounds__(1024) void lowrank_wide_kernel(
     const int wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, q = lane >> 4;
     uint16_t* Dw = (uint16_t*)(smem + wave * TILE_B);
+    // column c's four 8-value k chunks are stored in the order chunk ^ swz(c):
+    // the transposing 2-byte stores and the 16-byte fragment reads are then
+    // free of bank conflicts (64 banks of 4 bytes) for R = 16, 32 and 64
+    auto swz = [](int c) { return ((c >> 4) * 3) & 3; };
     const int64_t m0 = (int64_t)blockIdx.x * 16;
     const int64_t row = m0 + j;
     const int64_t nsl = K / 32;
@@ -118,13 +123,17 @@ __global__ __launch_bounds__(1024) void lowrank_wide_kernel(
                 const int kl = e0 / RT, c0 = e0 % RT;
                 const uint32_t w[4] = {da[u][i].x, da[u][i].y, da[u][i].z, da[u][i].w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    Dw[(c0 + e) * DP + kl] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                for (int e = 0; e < 8; ++e) {
+                    const int c = c0 + e;
+                    Dw[c * DP + ((((kl >> 3) ^ swz(c)) << 3) | (kl & 7))] =
+                        (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                }
             }
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const v8s bf = *(const v8s*)(&Dw[(ct * 16 + j) * DP + q * 8]);
+                const int c = ct * 16 + j;
+                const v8s bf = *(const v8s*)(&Dw[c * DP + ((q ^ swz(c)) << 3)]);
                 const v8s af = __builtin_bit_cast(v8s, xa[u]);
                 if constexpr (DT == BF16)
                     acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
