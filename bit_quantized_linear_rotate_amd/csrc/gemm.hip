@@ -12,7 +12,7 @@
 // with l[m,n] = sum_r L[m,r] * up[n,r]; every listed multiply and add is a
 // separately rounded fp32 operation.
 //
-// Design for CDNA4 (two kernels; launch_gemm picks one per call):
+// Design for CDNA4 (three kernels; launch_gemm picks one per call):
 //   * w4a4_gemm_ring3_kernel, for prefill-sized layers: persistent, one
 //     workgroup per CU walking 256 x 256 output tiles; eight waves, two per
 //     SIMD, each a 128 x 64 block of 8 x 4 v_mfma_i32_16x16x64_i8 tiles with
@@ -20,11 +20,16 @@
 //     global -> LDS through buffer_load ... lds into a three-stage ring, so two
 //     K-steps are in flight while one is multiplied; the weights are unpacked
 //     in registers right before the MFMAs.
-//   * w4a4_gemm_kernel, for everything else (decode-sized M, per-64-group
-//     weight scales, the low-rank term, INT32 export, K-chunked runs): 128 x 128
-//     output tile, 4 waves in 2 x 2, each a 64 x 64 block of 4 x 4 MFMA tiles;
-//     K advances 64 per step with double-buffered LDS and the next step's
-//     global loads in flight during the MFMAs.
+//   * w4a4_gemm_skinny_kernel, for decode-sized M (<= 64): one 1024-thread
+//     workgroup per 16 output columns; its sixteen waves split K and their
+//     INT32 tiles are summed exactly in LDS.
+//   * w4a4_gemm_kernel, for everything else (per-64-group weight scales, the
+//     low-rank term with group scales, INT32 export, K-chunked runs, M <= 128):
+//     128 x 128 output tile, 4 waves in 2 x 2, each a 64 x 64 block of 4 x 4
+//     MFMA tiles; K advances 64 per step with double-buffered LDS and the next
+//     step's global loads in flight during the MFMAs.  With group scales each
+//     step's INT32 tile is converted and accumulated in fp32 in the order
+//     above, with the group's scales staged through LDS alongside the operands.
 //   * Packed weights are read as bytes (N, K/2) and unpacked as 16*w: the low
 //     nibble shifted into the high half of a byte and the high nibble masked
 //     in place are both already sign-correct int8 values, so unpacking is
