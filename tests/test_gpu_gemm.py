@@ -34,6 +34,9 @@ def _operands(M, K, N, odt, sw_dt, group=0, bias=True, seed=0):
 SHAPES = [  # (M, K, N): tiles of 128 x 128 x 64 plus ragged tails
     (1, 256, 256), (32, 3840, 384), (130, 640, 200), (257, 1024, 129), (64, 96, 64),
     (200, 2048, 300), (5, 160, 17), (128, 64, 128),
+    # 64 < M <= 128 with K % 64 == 0: the 128 x 128 kernel's buffer-load
+    # staging, rows past M and columns past N reading zeros
+    (100, 192, 130), (77, 1024, 40),
 ]
 
 
