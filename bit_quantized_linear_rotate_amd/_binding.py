@@ -75,12 +75,22 @@ def _check(rc: int, what: str):
     raise W4A4Error(f"{what}: {msg}")
 
 
+# (plain ints for pointer arguments: ctypes converts them through argtypes,
+# and building c_void_p objects per call costs host time that small layers
+# notice)
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
-def _stream(device) -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device) -> int:
+    """The current HIP stream of `device` as an integer handle."""
+    if _raw_stream is not None:
+        idx = device.index if device.index is not None else torch.cuda.current_device()
+        return _raw_stream(idx)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _dt(t: torch.Tensor) -> int:
