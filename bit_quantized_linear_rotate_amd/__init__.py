@@ -7,11 +7,13 @@ from ._binding import (  # noqa: F401
     W4A4Error,
     lib,
     w4a4_device_supported,
+    w4a4_gemm_plan,
     w4a4_gemm_from_codes,
     w4a4_gemm_workspace_size,
     w4a4_int32_guard,
     w4a4_linear,
     w4a4_linear_workspace_size,
     w4a4_lowrank_down,
+    w4a4_rotate_quant_plan,
     w4a4_rotate_quant_rowwise,
 )

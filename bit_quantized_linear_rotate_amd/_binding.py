@@ -39,6 +39,10 @@ _SIGNATURES = {
                     ctypes.c_int),
     "w4a4_linear_workspace_size": ([_i64, _i64, _i64, _i32], _sz),
     "w4a4_int32_guard": ([_i64, ctypes.POINTER(_i64)], ctypes.c_int),
+    "w4a4_rotate_quant_plan": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp,
+                                ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
+    "w4a4_gemm_plan": ([_vp, _i64, _i64, _vp, _i64, _i32, ctypes.c_int, _vp, _i64, _vp,
+                        ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
     "w4a4_last_error": ([], ctypes.c_char_p),
     "w4a4_device_supported": ([], ctypes.c_int),
 }
@@ -111,12 +115,47 @@ def _as_2d(x: torch.Tensor) -> torch.Tensor:
         return x.reshape(-1, K)
 
 
+def _need(t, name: str, shape=None, dtypes=None, contiguous: bool = True):
+    """Layout check of one tensor argument (shape, dtype, contiguity).  The
+    device is checked afterwards, for every argument at once, so that a layout
+    error is reported before any device access."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtypes is not None and t.dtype not in dtypes:
+        names = "/".join(str(d).replace("torch.", "") for d in dtypes)
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {names}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _same_device(ref: torch.Tensor, **tensors):
+    """Every tensor on the CUDA (HIP) device of `ref`."""
+    if ref.device.type != "cuda":
+        raise ValueError(f"tensors must be on a CUDA (HIP) device, got {ref.device}")
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+_FLOAT = (torch.float32, torch.float16, torch.bfloat16)
+
+
 def _rot_arg(rot: Optional[torch.Tensor], g: int):
     if rot is None:
         return None, 0
-    if rot.dtype != torch.float32 or rot.shape != (g, g) or not rot.is_contiguous():
-        raise ValueError("rot must be a contiguous (g, g) float32 tensor")
+    _need(rot, "rot", (g, g), (torch.float32,))
     return rot, g
+
+
+def _wscale_shape(w_scale_group: int, K: int, N: int):
+    if w_scale_group == 0:
+        return (N,)
+    if w_scale_group == 64:
+        return (K // 64, N)
+    raise ValueError(f"w_scale_group must be 0 or 64, got {w_scale_group}")
 
 
 def w4a4_int32_guard(K: int):
@@ -134,6 +173,39 @@ def w4a4_gemm_workspace_size(M: int, N: int, K: int, k_chunk: int = 0) -> int:
     return int(lib().w4a4_gemm_workspace_size(M, N, K, k_chunk))
 
 
+# kernel names of the plan queries (include/w4a4.h)
+RQ_KERNELS = {0: "generic", 1: "mfma_lds", 2: "reg", 3: "wave", 4: "colmajor", 5: "g256"}
+GEMM_KERNELS = {0: "tile128", 1: "tile128_splitk", 2: "ring3", 3: "skinny"}
+_ALIGNED = 1 << 12   # stands for a buffer the binding allocates (torch aligns to >= 256 bytes)
+
+
+def w4a4_rotate_quant_plan(x: torch.Tensor, rot: Optional[torch.Tensor], g: int,
+                           smooth: Optional[torch.Tensor] = None,
+                           return_rotated: bool = False) -> str:
+    """Name of the rotate-quant kernel w4a4_rotate_quant_rowwise would launch
+    for these arguments (host-only; nothing runs)."""
+    x2 = _as_2d(x)
+    M, K = x2.shape
+    rot, g = _rot_arg(rot, g)
+    k = ctypes.c_int(-1)
+    rc = lib().w4a4_rotate_quant_plan(_ptr(x2), _dt(x2), M, K, x2.stride(0), x2.stride(1),
+                                      _ptr(rot), g, _ptr(smooth), _ALIGNED,
+                                      _ALIGNED if return_rotated else None, ctypes.byref(k))
+    _check(rc, "w4a4_rotate_quant_plan")
+    return RQ_KERNELS.get(k.value, "none")
+
+
+def w4a4_gemm_plan(M: int, K: int, N: int, w_scale_group: int = 0, lowrank: bool = False,
+                   return_acc: bool = False, k_chunk: int = 0) -> str:
+    """Name of the GEMM kernel w4a4_gemm_from_codes (or w4a4_linear) would
+    launch for operands the binding allocates (host-only; nothing runs)."""
+    k = ctypes.c_int(-1)
+    rc = lib().w4a4_gemm_plan(_ALIGNED, M, K, _ALIGNED, N, w_scale_group, int(lowrank),
+                              _ALIGNED if return_acc else None, k_chunk, _ALIGNED, ctypes.byref(k))
+    _check(rc, "w4a4_gemm_plan")
+    return GEMM_KERNELS.get(k.value, "none")
+
+
 def w4a4_device_supported() -> bool:
     return lib().w4a4_device_supported() == OK
 
@@ -143,15 +215,17 @@ def w4a4_rotate_quant_rowwise(x: torch.Tensor, rot: Optional[torch.Tensor], g: i
                               return_rotated: bool = False):
     """Rotate + quantize rows of x (..., K).  Returns (codes int8 (M, K),
     scales fp32 (M,)) and, if requested, the rotated values (M, K) in x.dtype."""
-    x2 = _as_2d(x)
+    x2 = _as_2d(_need(x, "x", contiguous=False))
     M, K = x2.shape
+    _dt(x2)
     rot, g = _rot_arg(rot, g)
+    if smooth is not None:
+        _need(smooth, "smooth", (K,), (x2.dtype,))
+    _same_device(x2, rot=rot, smooth=smooth)
     dev = x2.device
     codes = torch.empty((M, K), dtype=torch.int8, device=dev)
     scales = torch.empty((M,), dtype=torch.float32, device=dev)
     rotated = torch.empty((M, K), dtype=x2.dtype, device=dev) if return_rotated else None
-    if smooth is not None and (smooth.dtype != x2.dtype or not smooth.is_contiguous()):
-        raise ValueError("smooth must be contiguous and in x.dtype")
     rc = lib().w4a4_rotate_quant_rowwise(
         _ptr(x2), _dt(x2), M, K, x2.stride(0), x2.stride(1), _ptr(rot), g, _ptr(smooth),
         _ptr(codes), _ptr(scales), _ptr(rotated), _stream(dev))
@@ -160,12 +234,17 @@ def w4a4_rotate_quant_rowwise(x: torch.Tensor, rot: Optional[torch.Tensor], g: i
 
 
 def w4a4_lowrank_down(x: torch.Tensor, proj_down: torch.Tensor) -> torch.Tensor:
-    x2 = _as_2d(x)
+    x2 = _as_2d(_need(x, "x", contiguous=False))
     M, K = x2.shape
+    _dt(x2)
+    _need(proj_down, "proj_down", dtypes=(x2.dtype,))
+    if proj_down.dim() != 2 or proj_down.shape[0] != K:
+        raise ValueError(f"proj_down has shape {tuple(proj_down.shape)}, expected ({K}, rank)")
     R = proj_down.shape[1]
+    _same_device(x2, proj_down=proj_down)
     lora = torch.empty((M, R), dtype=torch.float32, device=x2.device)
     rc = lib().w4a4_lowrank_down(_ptr(x2), _dt(x2), M, K, x2.stride(0), x2.stride(1),
-                                 _ptr(proj_down.contiguous()), R, _ptr(lora), _stream(x2.device))
+                                 _ptr(proj_down), R, _ptr(lora), _stream(x2.device))
     _check(rc, "w4a4_lowrank_down")
     return lora
 
@@ -179,8 +258,29 @@ def w4a4_gemm_from_codes(codes: torch.Tensor, scales: torch.Tensor, w_packed: to
                          return_acc: bool = False, k_chunk: int = 0):
     """INT4-code GEMM with the fused epilogue.  Returns out (M, N) and, if
     requested, the exact int32 sums (M, N)."""
+    _need(codes, "codes", dtypes=(torch.int8,))
+    if codes.dim() != 2:
+        raise ValueError(f"codes must be (M, K), got shape {tuple(codes.shape)}")
     M, K = codes.shape
+    _need(w_packed, "w_packed", dtypes=(torch.uint8,))
+    if w_packed.dim() != 2 or w_packed.shape[1] * 2 != K:
+        raise ValueError(f"w_packed has shape {tuple(w_packed.shape)}, expected (N, {K // 2})")
     N = w_packed.shape[0]
+    _need(scales, "scales", (M,), (torch.float32,))
+    _need(w_scale, "w_scale", _wscale_shape(w_scale_group, K, N), _FLOAT)
+    if bias is not None:
+        _need(bias, "bias", (N,), _FLOAT)
+    if (lora_act is None) != (proj_up is None):
+        raise ValueError("lora_act and proj_up go together")
+    if lora_act is not None:
+        _need(lora_act, "lora_act", dtypes=(torch.float32,))
+        if lora_act.dim() != 2 or lora_act.shape[0] != M:
+            raise ValueError(f"lora_act has shape {tuple(lora_act.shape)}, expected ({M}, rank)")
+        _need(proj_up, "proj_up", (N, lora_act.shape[1]), _FLOAT)
+    if out_dtype not in _FLOAT:
+        raise ValueError(f"out_dtype {out_dtype} is not float32/float16/bfloat16")
+    _same_device(codes, scales=scales, w_packed=w_packed, w_scale=w_scale, bias=bias,
+                 lora_act=lora_act, proj_up=proj_up)
     dev = codes.device
     out = torch.empty((M, N), dtype=out_dtype, device=dev)
     acc = torch.empty((M, N), dtype=torch.int32, device=dev) if return_acc else None
@@ -204,17 +304,45 @@ def w4a4_linear(x: torch.Tensor, rot: Optional[torch.Tensor], g: int, w_packed: 
                 workspace: Optional[torch.Tensor] = None,
                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The whole W4A4 linear: y = layer(x) of shape (..., N)."""
-    lead = x.shape[:-1]
+    lead = _need(x, "x", contiguous=False).shape[:-1]
     x2 = _as_2d(x)
     M, K = x2.shape
-    N = w_packed.shape[0]
+    _dt(x2)
     rot, g = _rot_arg(rot, g)
+    _need(w_packed, "w_packed", dtypes=(torch.uint8,))
+    if w_packed.dim() != 2 or w_packed.shape[1] * 2 != K:
+        raise ValueError(f"w_packed has shape {tuple(w_packed.shape)}, expected (N, {K // 2})")
+    N = w_packed.shape[0]
+    _need(w_scale, "w_scale", _wscale_shape(w_scale_group, K, N), _FLOAT)
+    # the layer reads bias, smooth and the low-rank factors in x's dtype
+    if bias is not None:
+        _need(bias, "bias", (N,), (x2.dtype,))
+    if smooth is not None:
+        _need(smooth, "smooth", (K,), (x2.dtype,))
+    if (proj_down is None) != (proj_up is None):
+        raise ValueError("proj_down and proj_up go together")
+    rank = 0
+    if proj_down is not None:
+        _need(proj_down, "proj_down", dtypes=(x2.dtype,))
+        if proj_down.dim() != 2 or proj_down.shape[0] != K:
+            raise ValueError(f"proj_down has shape {tuple(proj_down.shape)}, expected ({K}, rank)")
+        rank = proj_down.shape[1]
+        _need(proj_up, "proj_up", (N, rank), (x2.dtype,))
+    out_dtype = out_dtype or (out.dtype if out is not None else x2.dtype)
+    if out_dtype not in _FLOAT:
+        raise ValueError(f"out_dtype {out_dtype} is not float32/float16/bfloat16")
+    if out is not None:
+        _need(out, "out", (M, N), (out_dtype,))
+    need = w4a4_linear_workspace_size(M, K, N, rank)
+    if workspace is not None:
+        _need(workspace, "workspace", dtypes=(torch.uint8,))
+        if workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, need {need}")
+    _same_device(x2, rot=rot, w_packed=w_packed, w_scale=w_scale, bias=bias, smooth=smooth,
+                 proj_down=proj_down, proj_up=proj_up, out=out, workspace=workspace)
     dev = x2.device
-    out_dtype = out_dtype or x2.dtype
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=dev)
-    rank = 0 if proj_down is None else proj_down.shape[1]
-    need = w4a4_linear_workspace_size(M, K, N, rank)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     rc = lib().w4a4_linear(

@@ -190,6 +190,38 @@ int w4a4_gemm_from_codes(const int8_t* codes, const float* scales, int64_t M, in
     return W4A4_OK;
 }
 
+int w4a4_rotate_quant_plan(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                           int64_t stride_k, const float* rot, int32_t g, const void* smooth,
+                           const int8_t* codes, const void* rotated_out, int* kernel)
+{
+    int rc = rq_validate(x, x_dtype, M, K, stride_m, stride_k, rot, g, (int8_t*)codes, (float*)1);
+    if (rc) return rc;
+    RQArgs a{x, x_dtype, M, K, stride_m, stride_k, rot, rot ? g : 0, smooth, (int8_t*)codes,
+             nullptr, (void*)rotated_out};
+    const int p = M > 0 ? rotate_quant_path(a) : -1;
+    if (M > 0 && p < 0)
+        return fail(W4A4_UNSUPPORTED, "no rotate_quant kernel for this shape (K=%lld)", (long long)K);
+    if (kernel) *kernel = p;
+    return W4A4_OK;
+}
+
+int w4a4_gemm_plan(const int8_t* codes, int64_t M, int64_t K, const uint8_t* w_packed, int64_t N,
+                   int32_t w_scale_group, int has_lowrank, const int32_t* acc_out, int64_t k_chunk,
+                   const void* out, int* kernel)
+{
+    const float* fake_lora = has_lowrank ? (const float*)1 : nullptr;
+    int rc = gemm_validate(codes, (const float*)1, M, K, w_packed, N, (const void*)1, W4A4_F32,
+                           w_scale_group, nullptr, 0, fake_lora, fake_lora, W4A4_F32,
+                           has_lowrank ? 1 : 0, (void*)out, W4A4_F32, k_chunk);
+    if (rc) return rc;
+    const int64_t kc = k_chunk > 0 ? k_chunk : (w_scale_group ? 0 : guard_chunk(K));
+    GemmArgs a{codes, nullptr, M, K, N, w_packed, nullptr, W4A4_F32, w_scale_group,
+               nullptr, 0, fake_lora, fake_lora, W4A4_F32, has_lowrank ? 1 : 0,
+               (void*)out, W4A4_F32, (int32_t*)acc_out, kc, nullptr};
+    if (kernel) *kernel = (M > 0 && N > 0) ? gemm_path(a) : -1;
+    return W4A4_OK;
+}
+
 size_t w4a4_linear_workspace_size(int64_t M, int64_t K, int64_t N, int32_t rank)
 {
     if (M <= 0) return 0;
@@ -241,13 +273,17 @@ int w4a4_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride
     int64_t* acc64 = kc > 0 ? (int64_t*)ws : nullptr;
     hipStream_t st = (hipStream_t)stream;
 
+    // decide every launch before the first one, so that a call that is
+    // refused leaves nothing enqueued
+    RQArgs qa{x, x_dtype, M, K, stride_m, stride_k, rot, rot ? g : 0, smooth, codes, scales, nullptr};
+    if (rotate_quant_path(qa) < 0)
+        return fail(W4A4_UNSUPPORTED, "no rotate_quant kernel for this shape (K=%lld)", (long long)K);
     hipError_t e;
     if (r) {
         LowRankArgs la{x, x_dtype, M, K, stride_m, stride_k, proj_down, r, lora};
         e = launch_lowrank_down(la, st);
         if (e != hipSuccess) return hip_fail(e, "lowrank_down launch");
     }
-    RQArgs qa{x, x_dtype, M, K, stride_m, stride_k, rot, rot ? g : 0, smooth, codes, scales, nullptr};
     int path = 0;
     e = launch_rotate_quant(qa, st, &path);
     if (e == hipErrorNotSupported)

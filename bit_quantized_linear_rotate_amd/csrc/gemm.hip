@@ -118,9 +118,12 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
     uint4 ra[2];
     uint4 rw;
     // ALIGNED without K-chunks (K % 64 == 0): buffer loads over the tile's
-    // code rows and weight columns, fixed lane offsets plus the step's k as the
-    // scalar offset; rows past M and columns past N read zeros (a load past
-    // the last step reads the next row, and only fills the idle buffer)
+    // code rows and weight columns.  The step's k is added to the per-lane
+    // offset, never passed as the scalar offset: the range check covers only
+    // the per-lane part, so every byte must travel there.  Rows past M and
+    // columns past N read zeros; the load past the last step reads the next
+    // row of the tile (only into the idle buffer) or, on the tile's last row,
+    // falls outside the range and reads zeros.
     constexpr bool BUF = ALIGNED && !SPLIT;
     const __amdgpu_buffer_rsrc_t rca =
         make_rsrc(a.codes + (m0 < M ? m0 : 0) * K, (uint64_t)(m0 < M ? min(M - m0, (int64_t)BM) : 0) * K);
@@ -132,10 +135,10 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
             for (int i = 0; i < 2; ++i) {
                 const int c = tid + 256 * i;
                 ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                    rca, (int)((c >> 2) * K + (c & 3) * 16), (int)k, 0));
+                    rca, (int)((c >> 2) * K + (c & 3) * 16 + k), 0, 0));
             }
             rw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                rcw, (int)((tid >> 1) * (K >> 1) + (tid & 1) * 16), (int)(k >> 1), 0));
+                rcw, (int)((tid >> 1) * (K >> 1) + (tid & 1) * 16 + (k >> 1)), 0, 0));
             return;
         }
 #pragma unroll
@@ -813,7 +816,7 @@ __global__ __launch_bounds__(1024) void w4a4_gemm_skinny_kernel(GemmArgs a)
     }
 }
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
+int gemm_path(const GemmArgs& a)
 {
     const bool aligned = (a.K % 32) == 0 && ((uintptr_t)a.codes % 16) == 0 &&
                          ((uintptr_t)a.wp % 16) == 0;
@@ -821,7 +824,25 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
     // decode-sized M: the skinny kernel (every epilogue variant but group
     // scales and K-chunks)
     if (!group && a.k_chunk == 0 && a.M >= 1 && a.M <= 64 && (a.K % 64) == 0 &&
-        ((uintptr_t)a.codes % 16) == 0 && ((uintptr_t)a.wp % 8) == 0) {
+        ((uintptr_t)a.codes % 16) == 0 && ((uintptr_t)a.wp % 8) == 0)
+        return kGemmSkinny;
+    // Prefill-sized layers take the 256 x 256 three-stage kernel; everything
+    // else (small M, group scales, low-rank term, INT32 export, K chunks,
+    // K not a multiple of 128, unaligned operands) the 128 x 128 kernel.
+    if (!group && a.lora == nullptr && a.acc_out == nullptr && a.k_chunk == 0 && a.M > 128 &&
+        (a.K % R3_BK) == 0 && a.K >= 2 * R3_BK && aligned && ((uintptr_t)a.out % 16) == 0)
+        return kGemmRing3;
+    if (a.k_chunk > 0 && !group) return kGemmTileSplitK;
+    return kGemmTile;
+}
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
+{
+    const bool aligned = (a.K % 32) == 0 && ((uintptr_t)a.codes % 16) == 0 &&
+                         ((uintptr_t)a.wp % 16) == 0;
+    const bool group = a.sw_group > 0;
+    const int path = gemm_path(a);
+    if (path == kGemmSkinny) {
         const unsigned gx = (unsigned)((a.N + 15) / 16);
         if (a.M <= 16)
             hipLaunchKernelGGL(w4a4_gemm_skinny_kernel<1>, dim3(gx), dim3(1024), 0, st, a);
@@ -831,13 +852,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
             hipLaunchKernelGGL(w4a4_gemm_skinny_kernel<4>, dim3(gx), dim3(1024), 0, st, a);
         return hipGetLastError();
     }
-    // Prefill-sized layers take the 256 x 256 three-stage kernel; everything
-    // else (small M, group scales, low-rank term, INT32 export, K chunks,
-    // K not a multiple of 128, unaligned operands) the 128 x 128 kernel.
-    const bool ring3 = !group && a.lora == nullptr && a.acc_out == nullptr && a.k_chunk == 0 &&
-                       a.M > 128 && (a.K % R3_BK) == 0 && a.K >= 2 * R3_BK && aligned &&
-                       ((uintptr_t)a.out % 16) == 0;
-    if (ring3) {
+    if (path == kGemmRing3) {
         const int tm = (int)((a.M + BBM - 1) / BBM), tn = (int)((a.N + BBN - 1) / BBN);
         const int nt = tm * tn;
         // persistent grid: one workgroup per CU (a multiple of 8 so that a
@@ -862,7 +877,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
     }
     const unsigned gx = (unsigned)((a.N + BN - 1) / BN);
     const unsigned gy = (unsigned)((a.M + BM - 1) / BM);
-    if (a.k_chunk > 0 && !group) {
+    if (path == kGemmTileSplitK) {
         const int64_t kc = a.k_chunk;
         const unsigned gz = (unsigned)((a.K + kc - 1) / kc);
         const int64_t n = a.M * a.N;
@@ -879,7 +894,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
     const int64_t kc = a.K;
     // (the aligned kernels without K-chunks stage through buffer loads that
     // need whole 64-deep K steps and 32-bit offsets within a 128-row tile)
-    const bool aligned_buf = aligned && (a.K % 64) == 0 && a.K <= (1 << 24);
+    const bool aligned_buf = aligned && (a.K % 64) == 0 && a.K < (1 << 24);
     if (group) {
 #define W4A4_GROUP_LAUNCH(DT)                                                                    \
     do {                                                                                         \

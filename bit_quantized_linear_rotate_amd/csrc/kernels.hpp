@@ -18,6 +18,9 @@ struct RQArgs {
     void* yout;             // (M, K) in dtype or nullptr
 };
 
+// The kernel that launch_rotate_quant takes for these arguments (>= 0), or -1
+// when no kernel serves them; host-only, no device access.
+int rotate_quant_path(const RQArgs& a);
 hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path);
 
 struct GemmArgs {
@@ -41,6 +44,9 @@ struct GemmArgs {
     int64_t* acc64;         // workspace (M, N) int64 when k_chunk > 0
 };
 
+// GEMM kernels, as gemm_path names them (host-only choice, no device access)
+enum { kGemmTile = 0, kGemmTileSplitK = 1, kGemmRing3 = 2, kGemmSkinny = 3 };
+int gemm_path(const GemmArgs& a);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 
 struct LowRankArgs {

@@ -1847,9 +1847,11 @@ static bool colmajor_ok(const RQArgs& a)
     return true;
 }
 
-// Chooses the kernel; returns the path taken in *path (0 generic, 1 MFMA LDS, 2 MFMA registers,
-// 3 wave per row, 4 column-major).
-hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path)
+// Which kernel serves a call (decided on the host from shapes, strides and
+// alignments alone): 0 generic, 1 MFMA with an LDS row buffer, 2 MFMA
+// registers, 3 wave per row block, 4 column-major, 5 g = 256 row-major; -1
+// when none does (a row too long for the generic kernel's LDS buffer).
+int rotate_quant_path(const RQArgs& a)
 {
     // MFMA path: 16-bit activations, group width 16..256, K a multiple of
     // the MFMA group width, 16-byte aligned operands for the vector loads.
@@ -1861,14 +1863,8 @@ hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path)
               (a.yout == nullptr || ((uintptr_t)a.yout % 16) == 0) &&
               (a.smooth == nullptr || ((uintptr_t)a.smooth % 16) == 0);
     if (a.rot && !(a.g == 16 || a.g == 32 || a.g == 64 || a.g == 128 || a.g == 256)) ok = false;
-    if (colmajor_ok(a)) {
-        if (path) *path = 4;
-        return a.dtype == BF16 ? launch_colmajor_dt<BF16>(a, st) : launch_colmajor_dt<F16>(a, st);
-    }
-    if (g256_ok(a)) {
-        if (path) *path = 5;
-        return a.dtype == BF16 ? launch_g256_dt<BF16>(a, st) : launch_g256_dt<F16>(a, st);
-    }
+    if (colmajor_ok(a)) return 4;
+    if (g256_ok(a)) return 5;
     if (ok && mfma_lds_bytes(GP, a.K, 1) > 160 * 1024) ok = false;
     const bool contig = a.sk == 1 && (a.sm % 8) == 0 && ((uintptr_t)a.x % 16) == 0;
     // The wave-per-row-block kernel needs many row blocks to keep the GPU
@@ -1885,27 +1881,36 @@ hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path)
         many_blocks = (a.M + rpb - 1) / rpb >= 1536;
     }
     if (ok && contig && GP <= 64 && a.K / GP <= 64 && many_blocks &&
-        (a.yout == nullptr || ((uintptr_t)a.yout % 8) == 0) && ((uintptr_t)a.codes % 16) == 0) {
-        if (path) *path = 3;
-        return a.dtype == BF16 ? launch_wave_dt<BF16>(a, GP, st) : launch_wave_dt<F16>(a, GP, st);
-    }
+        (a.yout == nullptr || ((uintptr_t)a.yout % 8) == 0) && ((uintptr_t)a.codes % 16) == 0)
+        return 3;
     if (ok && contig && GP <= 64 && a.K / GP <= 256 &&
-        (a.yout == nullptr || ((uintptr_t)a.yout % 8) == 0) &&
-        ((uintptr_t)a.codes % 4) == 0) {
-        if (path) *path = 2;
-        return a.dtype == BF16 ? launch_reg_dt<BF16>(a, GP, st) : launch_reg_dt<F16>(a, GP, st);
-    }
-    if (ok) {
-        if (path) *path = 1;
-        return a.dtype == BF16 ? launch_mfma_dt<BF16>(a, GP, contig, st)
-                               : launch_mfma_dt<F16>(a, GP, contig, st);
-    }
-    if (path) *path = 0;
-    if ((size_t)a.K * 4 > 160 * 1024) return hipErrorNotSupported;  // row does not fit in LDS
-    switch (a.dtype) {
-    case F32: return launch_generic_dt<F32>(a, st);
-    case F16: return launch_generic_dt<F16>(a, st);
-    default: return launch_generic_dt<BF16>(a, st);
+        (a.yout == nullptr || ((uintptr_t)a.yout % 8) == 0) && ((uintptr_t)a.codes % 4) == 0)
+        return 2;
+    if (ok) return 1;
+    if ((size_t)a.K * 4 > 160 * 1024) return -1;  // row does not fit in LDS
+    return 0;
+}
+
+hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path)
+{
+    const int p = rotate_quant_path(a);
+    if (path) *path = p;
+    const bool bf = a.dtype == BF16;
+    const int GP = a.rot ? (a.g < 32 ? 32 : a.g) : 32;
+    const bool contig = a.sk == 1 && (a.sm % 8) == 0 && ((uintptr_t)a.x % 16) == 0;
+    switch (p) {
+    case 4: return bf ? launch_colmajor_dt<BF16>(a, st) : launch_colmajor_dt<F16>(a, st);
+    case 5: return bf ? launch_g256_dt<BF16>(a, st) : launch_g256_dt<F16>(a, st);
+    case 3: return bf ? launch_wave_dt<BF16>(a, GP, st) : launch_wave_dt<F16>(a, GP, st);
+    case 2: return bf ? launch_reg_dt<BF16>(a, GP, st) : launch_reg_dt<F16>(a, GP, st);
+    case 1: return bf ? launch_mfma_dt<BF16>(a, GP, contig, st) : launch_mfma_dt<F16>(a, GP, contig, st);
+    case 0:
+        switch (a.dtype) {
+        case F32: return launch_generic_dt<F32>(a, st);
+        case F16: return launch_generic_dt<F16>(a, st);
+        default: return launch_generic_dt<BF16>(a, st);
+        }
+    default: return hipErrorNotSupported;
     }
 }
 

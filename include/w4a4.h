@@ -148,6 +148,33 @@ size_t w4a4_linear_workspace_size(int64_t M, int64_t K, int64_t N, int32_t rank)
  */
 int w4a4_int32_guard(int64_t K, int64_t* k_chunk);
 
+/*
+ * Host-only plan queries: which kernel the library selects for a call with
+ * these arguments.  Same validation and status codes as the call itself
+ * (a fused operator that checks dtype, shape and group size and reports when
+ * it cannot serve a request: "[Feat][Ascend] Add fused RotateQuant backend",
+ * section "What this PR does / why we need it"); no device access, nothing
+ * enqueued.  Pointers are only inspected for NULL and alignment.  *kernel
+ * receives -1 when M == 0 (nothing would launch).
+ *
+ * w4a4_rotate_quant_plan, *kernel:
+ *   0 generic (exact products summed in fp64, one rounding; fp32 activations)
+ *   1 MFMA with an LDS row buffer (other 16-bit layouts)
+ *   2 MFMA with the row block's tiles over four waves (few rows, g <= 64)
+ *   3 one wave per row block (many contiguous rows, g <= 64)
+ *   4 column-major (unit row stride, i.e. a transposed view; M % 8 == 0)
+ *   5 g = 256 on contiguous rows
+ * w4a4_gemm_plan, *kernel (has_lowrank: a low-rank term will be added):
+ *   0 128 x 128 tiles          1 128 x 128 tiles over K chunks (int64 combine)
+ *   2 persistent 256 x 256 ring (prefill-sized M)     3 skinny M (M <= 64)
+ */
+int w4a4_rotate_quant_plan(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                           int64_t stride_k, const float* rot, int32_t g, const void* smooth,
+                           const int8_t* codes, const void* rotated_out, int* kernel);
+int w4a4_gemm_plan(const int8_t* codes, int64_t M, int64_t K, const uint8_t* w_packed, int64_t N,
+                   int32_t w_scale_group, int has_lowrank, const int32_t* acc_out, int64_t k_chunk,
+                   const void* out, int* kernel);
+
 /* Thread-local text for the last non-OK status returned on this thread. */
 const char* w4a4_last_error(void);
 

@@ -108,3 +108,26 @@ def test_linear_rejections(L):
     rc = L.w4a4_linear(FAKE, 2, 4, 64, 64, 1, FAKE, 16, None, FAKE, 8, FAKE, 2, 0, None, None,
                        None, 0, FAKE, 2, FAKE, 16, None)
     assert rc == INVALID                                      # workspace too small
+
+
+def test_plan_queries_name_the_config_kernels(L):
+    # host-only: which kernels the five workloads' calls take (nothing runs)
+    import torch
+    from bit_quantized_linear_rotate_amd import _binding as b
+    bf, h = torch.bfloat16, torch.float16
+    assert b.w4a4_rotate_quant_plan(torch.zeros(8192, 3840, dtype=bf), torch.zeros(64, 64), 64) == "wave"
+    xt = torch.zeros(10240, 8192, dtype=h).t()
+    assert b.w4a4_rotate_quant_plan(xt, torch.zeros(256, 256), 256) == "colmajor"
+    assert b.w4a4_rotate_quant_plan(torch.zeros(4096, 16384, dtype=bf), torch.zeros(256, 256), 256,
+                                    smooth=torch.zeros(16384, dtype=bf)) == "g256"
+    assert b.w4a4_rotate_quant_plan(torch.zeros(32, 3840, dtype=bf), torch.zeros(64, 64), 64) == "reg"
+    assert b.w4a4_rotate_quant_plan(torch.zeros(32, 256), torch.zeros(16, 16), 16) == "generic"
+    assert b.w4a4_gemm_plan(8192, 3840, 3840) == "ring3"
+    assert b.w4a4_gemm_plan(8192, 10240, 3840) == "ring3"
+    assert b.w4a4_gemm_plan(32, 3840, 3840) == "skinny"
+    assert b.w4a4_gemm_plan(4096, 16384, 6144, 64, lowrank=True) == "tile128"
+    assert b.w4a4_gemm_plan(300, 1024, 200, k_chunk=128) == "tile128_splitk"
+    assert b.w4a4_gemm_plan(300, 1024, 256, return_acc=True) == "tile128"
+    assert b.w4a4_gemm_plan(0, 1024, 256) == "none"
+    with pytest.raises(ValueError):
+        b.w4a4_rotate_quant_plan(torch.zeros(4, 63, dtype=bf), None, 0)
