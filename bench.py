@@ -8,8 +8,20 @@ low-rank down projection when the workload has one), i.e. one w4a4_linear call.
 Prints ONE JSON line.  `value` is whole-job throughput in TOPS (2*M*N*K per
 step / step time) with all inputs resident in HBM.  Four independent input /
 weight / output sets are cycled so that consecutive steps do not find their
-operands in the 256 MB last-level cache.  Each kernel is also timed alone with
-HIP events on the stream it runs on, giving the roofline fractions.
+operands in the 256 MB last-level cache.
+
+Before anything is timed, the CPU leg (the same part of the run that times the
+oracle for `cpu_baseline`) checks each workload's output against the oracle on
+a sample of rows (all columns): codes and scales of those rows, and the output
+bit for bit wherever the codes agree (1 ulp with the low-rank term); a
+mismatch ends the run with an error.  The statistics go into the line.
+--no-cpu skips the whole CPU leg (parity and baseline).
+
+Each kernel is then timed alone on the stream it runs on, over max(steps, 50)
+launches: the mean launch duration from one HIP event pair around the
+back-to-back launches (the figure rocprofv3's kernel statistics average, and
+the one `roofline.achieved` divides the kernel's algorithmic work by), and
+median, p10 and p90 from a second pass with an event pair around every launch.
 
 The line also carries the other four workloads (wide-K transposed-view fp16,
 decode-like M=32, tiny fp32, large-K with smoothing, per-64-group scales and a
@@ -39,12 +51,16 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, published
-GEMM_KERNEL = "w4a4_gemm_ring3_kernel (INT8 MFMA GEMM + fused scale/bias/cast epilogue)"
+MIN_KERNEL_LAUNCHES = 50
 TRAFFIC_FILES = {  # kernel source -> committed counter summary
     "gemm": ("bit_quantized_linear_rotate_amd/csrc/gemm.hip", "profiles/gemm_prefill_m8192_k3840_n3840_traffic.json"),
     "rotate_quant": ("bit_quantized_linear_rotate_amd/csrc/rotate_quant.hip",
                      "profiles/rotate_quant_prefill_m8192_k3840_g64_traffic.json"),
 }
+GEMM_NAMES = {"ring3": "w4a4_gemm_ring3_kernel", "skinny": "w4a4_gemm_skinny_kernel",
+              "tile128": "w4a4_gemm_kernel", "tile128_splitk": "w4a4_gemm_kernel (K chunks)"}
+RQ_NAMES = {"wave": "rq_wave_kernel", "colmajor": "rq_colmajor_kernel", "g256": "rq_g256_kernel",
+            "reg": "rq_reg_kernel", "mfma_lds": "rq_mfma_kernel", "generic": "rq_generic_kernel"}
 
 
 def _traffic(which, workload):
@@ -99,8 +115,14 @@ def _variant(d, i, torch):
     return out
 
 
-def _time_loop(fn, n, torch):
-    """Average ms per call over n calls, HIP events on the current stream."""
+def _time_each(fn, n, torch, np):
+    """Two passes of n calls each, HIP events on the current stream (the
+    stream the binding launches on):
+      * ms_mean: one event pair around n back-to-back launches, divided by n:
+        the kernel's average launch duration as rocprofv3 reports it (the
+        roofline figures use this);
+      * ms_median / ms_p10 / ms_p90: an event pair around every launch (each
+        event adds a few microseconds of its own)."""
     st = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -109,10 +131,65 @@ def _time_loop(fn, n, torch):
         fn(i)
     e1.record(st)
     e1.synchronize()
-    return e0.elapsed_time(e1) / n
+    mean = e0.elapsed_time(e1) / n
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev[i][0].record(st)
+        fn(i)
+        ev[i][1].record(st)
+    ev[-1][1].synchronize()
+    a = np.asarray([x.elapsed_time(y) for x, y in ev], dtype=np.float64)
+    return {"ms_mean": float(mean), "launches": int(n),
+            "per_launch_events": {"ms_median": float(np.median(a)), "ms_p10": float(np.percentile(a, 10)),
+                                  "ms_p90": float(np.percentile(a, 90))}}
 
 
-def measure(name, steps, warmup, torch, np, w4, workloads):
+def _dtcode(torch, t):
+    return {torch.bfloat16: 2, torch.float16: 1, torch.float32: 0}[t.dtype]
+
+
+def cpu_leg_parity(w, inp, out, codes, scales, rows, np):
+    """CPU baseline leg, parity part: the oracle on `rows` of the workload
+    (all columns) against the GPU's output, codes and scales for the same rows
+    (taken before the timed region); raises if they break the parity rule,
+    returns the statistics."""
+    import oracle
+    ref = oracle.linear(inp, w.dtype, w.g, w.sw_dtype, w.sw_group, rows=rows)
+    gc, gs = codes[rows], scales[rows]
+    same_scale = (gs.view(np.uint32) == ref["scales"].view(np.uint32)) | (
+        np.isnan(gs) & np.isnan(ref["scales"]))
+    dc = np.abs(gc.astype(np.int32) - ref["codes"])
+    go = out[rows]
+    ro = ref["out"]
+    if w.dtype == "f32":
+        ia, ib = go.view(np.int32).astype(np.int64), ro.view(np.int32).astype(np.int64)
+        top = 1 << 31
+    else:
+        ia, ib = go.view(np.int16).astype(np.int64), ro.view(np.int16).astype(np.int64)
+        top = 1 << 15
+    ia = np.where(ia < 0, -(ia + top), ia)
+    ib = np.where(ib < 0, -(ib + top), ib)
+    ulp = np.abs(ia - ib)
+    exact_rows = same_scale & (dc.max(axis=1) == 0)
+    tol = 1 if w.rank else 0
+    ok = dc.max(initial=0) <= 1 and ulp[exact_rows].max(initial=0) <= tol
+    res = {"rows": int(len(rows)), "cols": int(w.N),
+           "codes_equal_frac": float((dc == 0).mean()), "code_flips": int((dc > 0).sum()),
+           "rows_other_scale": int((~same_scale).sum()),
+           "out_bit_exact_frac": float((ulp == 0).mean()),
+           "out_max_ulp_rows_with_equal_codes": int(ulp[exact_rows].max(initial=0)),
+           "rule": "codes within 1; outputs of rows whose codes match bit-exact"
+                   + (" (1 ulp with the low-rank term)" if w.rank else ""),
+           "pass": bool(ok)}
+    if not ok:
+        raise SystemExit(f"parity check failed on {w.name}: {res}")
+    return res
+
+
+def measure(name, steps, warmup, torch, np, w4, workloads, cpu=True):
+    from bit_quantized_linear_rotate_amd import _binding as b
     w = workloads.WORKLOADS[name]
     inp = workloads.generate(w)
     base = _dev_inputs(w, inp, torch, np)
@@ -122,6 +199,8 @@ def measure(name, steps, warmup, torch, np, w4, workloads):
     outs = [torch.empty((M, N), dtype=base["x"].dtype, device="cuda") for _ in sets]
     wss = [torch.empty((w4.w4a4_linear_workspace_size(M, K, N, rank),), dtype=torch.uint8,
                        device="cuda") for _ in sets]
+    rq_kernel = w4.w4a4_rotate_quant_plan(base["x"], base["rot"], g, smooth=base["smooth"])
+    gemm_kernel = w4.w4a4_gemm_plan(M, K, N, w.sw_group, lowrank=rank > 0)
 
     def step(i):
         s = sets[i % 4]
@@ -129,30 +208,64 @@ def measure(name, steps, warmup, torch, np, w4, workloads):
                        bias=s["bias"], smooth=s["smooth"], proj_down=s["proj_down"],
                        proj_up=s["proj_up"], workspace=wss[i % 4], out=outs[i % 4])
 
-    for i in range(warmup):
-        step(i)
-    ms_step = _time_loop(step, steps, torch)
-
-    # rotate+quantize alone (the kernel w4a4_linear launches first)
+    # rotate+quantize alone (the kernel w4a4_linear launches first), through
+    # the C ABI with prepared arguments; every return code is checked
     qbufs = [(torch.empty((M, K), dtype=torch.int8, device="cuda"),
               torch.empty((M,), dtype=torch.float32, device="cuda")) for _ in sets]
     lib = w4.lib()
-    import ctypes
+    stream = torch.cuda.current_stream().cuda_stream
 
     def rq(i):
         s = sets[i % 4]
         c, sc = qbufs[i % 4]
         x = s["x"]
-        lib.w4a4_rotate_quant_rowwise(
-            ctypes.c_void_p(x.data_ptr()), {torch.bfloat16: 2, torch.float16: 1, torch.float32: 0}[x.dtype],
-            M, K, x.stride(0), x.stride(1), ctypes.c_void_p(s["rot"].data_ptr()), g,
-            ctypes.c_void_p(s["smooth"].data_ptr()) if s["smooth"] is not None else None,
-            ctypes.c_void_p(c.data_ptr()), ctypes.c_void_p(sc.data_ptr()), None,
-            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        rc = lib.w4a4_rotate_quant_rowwise(
+            x.data_ptr(), _dtcode(torch, x), M, K, x.stride(0), x.stride(1), s["rot"].data_ptr(), g,
+            s["smooth"].data_ptr() if s["smooth"] is not None else None, c.data_ptr(), sc.data_ptr(),
+            None, stream)
+        if rc:
+            b._check(rc, "w4a4_rotate_quant_rowwise")
 
+    def host(t):
+        t = t.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    # ---- parity against the oracle (CPU leg), before anything is timed
+    par = None
+    if cpu:
+        step(0)
+        rq(0)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(7)
+        nrow = min(M, 64)
+        rows = np.sort(rng.choice(M, nrow, replace=False))
+        if w.zero_row_frac > 0:    # the workload's planted zero rows join the sample
+            zr = np.flatnonzero((inp["x"] == 0).all(axis=1))[:4]
+            rows = np.unique(np.concatenate([rows, zr]))
+        par = cpu_leg_parity(w, inp, host(outs[0]), host(qbufs[0][0]), host(qbufs[0][1]), rows, np)
+
+    # ---- timed steps: exactly `steps` calls after `warmup` untimed ones,
+    # synchronised on both sides
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(st)
+    for i in range(steps):
+        step(i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / steps
+
+    nk = max(steps, MIN_KERNEL_LAUNCHES)
     for i in range(warmup):
         rq(i)
-    ms_rq = _time_loop(rq, steps, torch)
+    t_rq = _time_each(rq, nk, torch, np)
     rq_bytes = M * K * base["x"].element_size() + M * K + 4 * M + 4 * g * g
     if w.smooth:
         rq_bytes += K * base["x"].element_size()
@@ -163,52 +276,54 @@ def measure(name, steps, warmup, torch, np, w4, workloads):
         c, sc = qbufs[i % 4]
         w4.w4a4_gemm_from_codes(c, sc, s["w_packed"], s["w_scale"], w_scale_group=w.sw_group,
                                 bias=s["bias"], out_dtype=outs[i % 4].dtype)
-    if rank:
-        gemm_note = "low-rank term excluded from the GEMM-alone timing"
-    else:
-        gemm_note = None
     for i in range(warmup):
         gemm(i)
-    ms_gemm = _time_loop(gemm, steps, torch)
+    t_gemm = _time_each(gemm, nk, torch, np)
     ops = 2.0 * M * N * K
     # bytes the GEMM must move: codes, packed weights, scales, bias, output
     gemm_bytes = (M * K + N * K // 2 + 4 * M + base["w_scale"].numel() * base["w_scale"].element_size()
                   + (N * base["bias"].element_size() if base["bias"] is not None else 0)
                   + M * N * outs[0].element_size())
+    ms_rq, ms_gemm = t_rq["ms_mean"], t_gemm["ms_mean"]
     res = {
         "workload": f"{name}: M={M} K={K} N={N} g={g} {w.dtype}"
                     + (" transposed-view input" if w.transposed else "")
                     + (f" smooth+rank{rank}" if rank else "")
                     + (" per-64-group scales" if w.sw_group else ""),
         "ms_per_step": ms_step,
+        "wall_s_timed_steps": wall,
         "tops": ops / (ms_step * 1e-3) / 1e12,
-        "rotate_quant": {"ms": ms_rq, "GB_s": rq_bytes / (ms_rq * 1e-3) / 1e9,
+        "rotate_quant": {"kernel": RQ_NAMES.get(rq_kernel, rq_kernel), **t_rq,
+                         "GB_s": rq_bytes / (ms_rq * 1e-3) / 1e9,
                          "frac_hbm": rq_bytes / (ms_rq * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "algorithmic_bytes": rq_bytes},
-        "gemm": {"ms": ms_gemm, "TOPS": ops / (ms_gemm * 1e-3) / 1e12,
+        "gemm": {"kernel": GEMM_NAMES.get(gemm_kernel, gemm_kernel), **t_gemm,
+                 "TOPS": ops / (ms_gemm * 1e-3) / 1e12,
                  "frac_int8": ops / (ms_gemm * 1e-3) / 1e12 / INT8_PEAK_TOPS, "ops": ops,
                  "GB_s": gemm_bytes / (ms_gemm * 1e-3) / 1e9, "algorithmic_bytes": gemm_bytes},
     }
-    if gemm_note:
-        res["gemm"]["note"] = gemm_note
+    if par is not None:
+        res["parity"] = par
     if rank:
+        res["gemm"]["note"] = "low-rank term excluded from the GEMM-alone timing"
         # low-rank down projection alone (the first kernel of a low-rank step)
         lbufs = [torch.empty((M, rank), dtype=torch.float32, device="cuda") for _ in sets]
 
         def lrd(i):
             s = sets[i % 4]
             x = s["x"]
-            lib.w4a4_lowrank_down(
-                ctypes.c_void_p(x.data_ptr()), {torch.bfloat16: 2, torch.float16: 1, torch.float32: 0}[x.dtype],
-                M, K, x.stride(0), x.stride(1), ctypes.c_void_p(s["proj_down"].data_ptr()), rank,
-                ctypes.c_void_p(lbufs[i % 4].data_ptr()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            rc = lib.w4a4_lowrank_down(x.data_ptr(), _dtcode(torch, x), M, K, x.stride(0), x.stride(1),
+                                       s["proj_down"].data_ptr(), rank, lbufs[i % 4].data_ptr(), stream)
+            if rc:
+                b._check(rc, "w4a4_lowrank_down")
 
         for i in range(warmup):
             lrd(i)
-        ms_lrd = _time_loop(lrd, steps, torch)
+        t_lrd = _time_each(lrd, nk, torch, np)
         lrd_bytes = M * K * base["x"].element_size() + K * rank * base["proj_down"].element_size() + 4 * M * rank
-        res["lowrank_down"] = {"ms": ms_lrd, "GB_s": lrd_bytes / (ms_lrd * 1e-3) / 1e9,
-                               "frac_hbm": lrd_bytes / (ms_lrd * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        res["lowrank_down"] = {"kernel": "lowrank down projection", **t_lrd,
+                               "GB_s": lrd_bytes / (t_lrd["ms_mean"] * 1e-3) / 1e9,
+                               "frac_hbm": lrd_bytes / (t_lrd["ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                "algorithmic_bytes": lrd_bytes}
     return w, inp, res
 
@@ -238,6 +353,11 @@ def cpu_baseline(w, inp, np, target_s=15.0):
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"{what}, {reps} call(s): {dt:.1f} s"}
+
+
+def _rounded(d):
+    return {k: (round(v, 5) if isinstance(v, float) else _rounded(v) if isinstance(v, dict) else v)
+            for k, v in d.items()}
 
 
 def main():
@@ -271,13 +391,18 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    w, inp, main_res = measure(args.workload, args.steps, args.warmup, torch, np, w4, workloads)
+    cpu = not args.no_cpu
+    w, inp, main_res = measure(args.workload, args.steps, args.warmup, torch, np, w4, workloads,
+                               cpu=cpu)
+    print(f"# {args.workload}: {main_res['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
     extras = {}
     if not args.no_extra and args.workload == "prefill":
         for name in ("widek", "decode", "tiny", "lowrank"):
             _, _, extras[name] = measure(name, max(10, args.steps // 2), args.warmup, torch, np, w4,
-                                         workloads)
+                                         workloads, cpu=cpu)
+            print(f"# {name}: {extras[name]['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
     g = main_res["gemm"]
+    rq = main_res["rotate_quant"]
     line = {
         "metric": METRIC,
         "value": round(main_res["tops"], 2),
@@ -293,28 +418,27 @@ def main():
         "data": "synthetic",
         "config": {"workload": main_res["workload"], "M": w.M, "K": w.K, "N": w.N, "g": w.g,
                    "activation_dtype": w.dtype},
-        "rotate_quant": {k: (round(v, 4) if isinstance(v, float) else v)
-                         for k, v in main_res["rotate_quant"].items()},
-        "gemm": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in g.items()},
+        "parity": main_res.get("parity"),
+        "rotate_quant": _rounded(rq),
+        "gemm": _rounded(g),
         "roofline": {"bound": "mfma", "achieved": round(g["TOPS"], 2), "peak": INT8_PEAK_TOPS,
                      "unit": "TOPS", "frac": round(g["frac_int8"], 4),
-                     "traffic": _traffic("gemm", args.workload), "kernel": GEMM_KERNEL},
-        "roofline_rotate_quant": {"bound": "hbm", "achieved": round(main_res["rotate_quant"]["GB_s"], 1),
+                     "traffic": _traffic("gemm", args.workload),
+                     "kernel": g["kernel"] + " (INT8 MFMA GEMM + fused scale/bias/cast epilogue)",
+                     "per_launch_ms": "mean over the timed launches"},
+        "roofline_rotate_quant": {"bound": "hbm", "achieved": round(rq["GB_s"], 1),
                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": round(main_res["rotate_quant"]["frac_hbm"], 4),
+                                  "frac": round(rq["frac_hbm"], 4),
                                   "traffic": _traffic("rotate_quant", args.workload),
-                                  "kernel": "rotate-quant (block rotation on MFMA, row absmax, INT4 codes)"},
+                                  "kernel": rq["kernel"] + " (block rotation on MFMA, row absmax, INT4 codes)"},
     }
     for name, extra in extras.items():
         line[name] = {"workload": extra["workload"], "ms_per_step": round(extra["ms_per_step"], 5),
-                      "tops": round(extra["tops"], 2),
-                      "rotate_quant": {k: (round(v, 4) if isinstance(v, float) else v)
-                                       for k, v in extra["rotate_quant"].items()},
-                      "gemm": {k: (round(v, 4) if isinstance(v, float) else v)
-                               for k, v in extra["gemm"].items()}}
+                      "tops": round(extra["tops"], 2), "parity": extra.get("parity"),
+                      "rotate_quant": _rounded(extra["rotate_quant"]),
+                      "gemm": _rounded(extra["gemm"])}
         if "lowrank_down" in extra:
-            line[name]["lowrank_down"] = {k: (round(v, 4) if isinstance(v, float) else v)
-                                          for k, v in extra["lowrank_down"].items()}
+            line[name]["lowrank_down"] = _rounded(extra["lowrank_down"])
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, inp, np)
     print(json.dumps(line), flush=True)

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a4.so")
-SOURCES = ["api.hip", "rotate_quant.hip", "gemm.hip", "lowrank.hip"]
+SOURCES = ["api.hip", "rotate_quant.hip", "rq_row.hip", "gemm.hip", "lowrank.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -22,7 +22,8 @@ HIPCC_FLAGS = [
 # per-source extra flags: the GEMM kernels' MFMA results live in ordinary
 # VGPRs (the group-scale loop converts every result with VALU instructions,
 # which cannot read accumulation registers)
-SOURCE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "rq_row.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:

@@ -21,6 +21,9 @@ struct RQArgs {
 // The kernel that launch_rotate_quant takes for these arguments (>= 0), or -1
 // when no kernel serves them; host-only, no device access.
 int rotate_quant_path(const RQArgs& a);
+// the row-streaming kernel for many contiguous 16-bit rows with g = 64
+bool row_kernel_ok(const RQArgs& a);
+hipError_t launch_rotate_quant_row(const RQArgs& a, hipStream_t st);
 hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path);
 
 struct GemmArgs {

@@ -1849,7 +1849,8 @@ static bool colmajor_ok(const RQArgs& a)
 
 // Which kernel serves a call (decided on the host from shapes, strides and
 // alignments alone): 0 generic, 1 MFMA with an LDS row buffer, 2 MFMA
-// registers, 3 wave per row block, 4 column-major, 5 g = 256 row-major; -1
+// registers, 3 wave per row block, 4 column-major, 5 g = 256 row-major,
+// 6 row-streaming g = 64 (rq_row.hip); -1
 // when none does (a row too long for the generic kernel's LDS buffer).
 int rotate_quant_path(const RQArgs& a)
 {
@@ -1863,8 +1864,14 @@ int rotate_quant_path(const RQArgs& a)
               (a.yout == nullptr || ((uintptr_t)a.yout % 16) == 0) &&
               (a.smooth == nullptr || ((uintptr_t)a.smooth % 16) == 0);
     if (a.rot && !(a.g == 16 || a.g == 32 || a.g == 64 || a.g == 128 || a.g == 256)) ok = false;
+    // g = 16 would run as 32-wide MFMA groups with R twice on the diagonal of
+    // a zero-padded 32 x 32 operand; an infinite input then meets a padding
+    // zero (Inf * 0 = NaN) and poisons the neighbouring group.  Those calls
+    // take the generic kernel, which sums each group on its own.
+    if (a.rot && a.g == 16) ok = false;
     if (colmajor_ok(a)) return 4;
     if (g256_ok(a)) return 5;
+    if (row_kernel_ok(a)) return 6;
     if (ok && mfma_lds_bytes(GP, a.K, 1) > 160 * 1024) ok = false;
     const bool contig = a.sk == 1 && (a.sm % 8) == 0 && ((uintptr_t)a.x % 16) == 0;
     // The wave-per-row-block kernel needs many row blocks to keep the GPU
@@ -1901,6 +1908,7 @@ hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path)
     switch (p) {
     case 4: return bf ? launch_colmajor_dt<BF16>(a, st) : launch_colmajor_dt<F16>(a, st);
     case 5: return bf ? launch_g256_dt<BF16>(a, st) : launch_g256_dt<F16>(a, st);
+    case 6: return launch_rotate_quant_row(a, st);
     case 3: return bf ? launch_wave_dt<BF16>(a, GP, st) : launch_wave_dt<F16>(a, GP, st);
     case 2: return bf ? launch_reg_dt<BF16>(a, GP, st) : launch_reg_dt<F16>(a, GP, st);
     case 1: return bf ? launch_mfma_dt<BF16>(a, GP, contig, st) : launch_mfma_dt<F16>(a, GP, contig, st);

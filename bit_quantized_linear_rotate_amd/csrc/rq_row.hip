@@ -1,0 +1,365 @@
+// Row-streaming rotate + quantize for many contiguous 16-bit rows, g = 64
+// (gfx950).  Same arithmetic as every rotate-quant kernel of this library
+// (web page "[Feat][Ascend] Consolidate INT8, RotateQuant, RoPE and ConvRot
+// W4A4 backends", section "W4A4 correctness and performance scope";
+// "[Feat][Ascend] Add fused RotateQuant backend", section "What this PR
+// does"; codes in int8 storage: "[Perf][Ascend] Avoid activation pack/unpack
+// in ConvRot W4A4", section "Summary"):
+//   y = T(x_group . T(R)),  s = max(absmax(y) / 7, 2^-126),
+//   c = clamp(round_half_even(fp32(y) / s), -7, 7).
+//
+// Design (a wave owns one whole row at a time, at most 64 groups of 64):
+//   * R's MFMA fragments (A operand, rounded to T; 8 KB) sit in LDS, built
+//     once per workgroup; a row is up to four tiles of 16 group-rows, each
+//     rotated by eight v_mfma_f32_16x16x32 (B = the tile's x, two 16-byte
+//     loads a lane), column tile by column tile so that each R fragment is
+//     read from LDS once per row and used for every tile.
+//   * The rotated values are rounded to T in pairs (v_cvt_pk) and kept packed:
+//     eight VGPRs a tile.  The row absmax is a packed 16-bit integer max over
+//     the sign-cleared patterns (monotone in |y|; a NaN pattern exceeds every
+//     other) and one wave reduction: no second rotation, no LDS.
+//   * As soon as a row's tiles are rotated, the next row's loads go into the
+//     freed x registers, so each wave keeps one row in flight while it
+//     quantizes the previous one; under 128 VGPRs leave room for four waves a
+//     SIMD.
+//   * Codes: with rinv = 1/s (IEEE), the integers RNE(y * rinv * (1 + 2^-21))
+//     and RNE(y * rinv * (1 - 2^-21)), each one fma against 1.5 * 2^23 (the
+//     add rounds the exact product to an integer and leaves it in the low
+//     byte), bracket the correctly rounded quotient fl(y / s): when they agree
+//     that integer IS the code (rounding is monotone).  They disagree only
+//     when y / s lies within 2^-18 of a half-integer, which for 16-bit y and a
+//     scale taken from the row's own 16-bit absmax happens only at exact ties
+//     (14 y = (2k + 1) absmax): those elements, flagged by a per-element
+//     ballot, are redone with an IEEE division in an out-of-line pass.
+//     Rows whose scale is Inf or NaN take the division for every element.
+//   * Each lane holds four codes of each of four column tiles; two
+//     v_permlane32_swap and two v_permlane16_swap transpose them so that every
+//     lane stores 16 consecutive codes (one 1 KB store per tile and wave).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace w4a4 {
+
+namespace {
+
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
+typedef unsigned v2u32 __attribute__((ext_vector_type(2)));
+
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+
+template <int DT>
+__device__ __forceinline__ uint32_t cvt_pair(float a, float b)
+{
+    if constexpr (DT == BF16) return __builtin_bit_cast(uint32_t, (v2bf){(__bf16)a, (__bf16)b});
+    else return __builtin_bit_cast(uint32_t, (v2h){(_Float16)a, (_Float16)b});
+}
+
+// value r (0: low half, 1: high half) of a packed pair, as fp32
+template <int DT>
+__device__ __forceinline__ float unpack_half(uint32_t p, int r)
+{
+    if constexpr (DT == BF16) return __uint_as_float(r ? (p & 0xffff0000u) : (p << 16));
+    else return f16_to_f32((uint16_t)(r ? (p >> 16) : (p & 0xffffu)));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+// low byte of each of four fp32 magic sums -> four codes in one dword
+__device__ __forceinline__ uint32_t pack_low_bytes(float t0, float t1, float t2, float t3)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(t3), __float_as_uint(t2), 0x0c0c0400u);
+    return lo | (hi << 16);
+}
+
+// buffer resource over `bytes` bytes at `base`: accesses whose per-lane
+// offset falls outside read zeros / are dropped
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+// correctly rounded code for a finite or non-finite quotient (NaN -> 0)
+__device__ __forceinline__ int code_of_quotient(float qv)
+{
+    if (qv != qv) return 0;
+    return (int)__builtin_amdgcn_fmed3f(rintf(qv), -7.0f, 7.0f);
+}
+
+}  // namespace
+
+template <int DT, bool SMOOTH, bool YOUT, int TW>
+__global__ __launch_bounds__(256, 4) void rq_row_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t sm,
+    const float* __restrict__ rot, const uint16_t* __restrict__ smooth,
+    int8_t* __restrict__ codes, float* __restrict__ scales, uint16_t* __restrict__ yout)
+{
+    constexpr int GP = 64, CT = 4, NKS = 2, LPL = 16;
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15, q = lane >> 4;
+    const int gpr = (int)(K / GP);
+    const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
+    // the wave's row is uniform: row pointers live in SGPRs and every load
+    // and store is a scalar base plus a 32-bit lane offset
+    const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + wid;
+
+    // R's MFMA fragments in LDS, built once per workgroup: fragment
+    // f = ct*2 + ks, lane (j, q) reads 16 bytes at (f*64 + lane)*16 holding
+    // T(R[q*16 + ks*8 + e][ct*16 + j]) for e = 0..7
+    __shared__ __align__(16) uint16_t rl[CT * NKS * 64 * 8];
+    for (int i = threadIdx.x; i < CT * NKS * 64 * 8; i += blockDim.x) {
+        const int f = i >> 9, l = (i >> 3) & 63, e = i & 7;
+        const int ct = f >> 1, ks = f & 1, jj = l & 15, qq = l >> 4;
+        rl[i] = f32_to_h<DT>(rot[(qq * LPL + ks * 8 + e) * GP + ct * 16 + jj]);
+    }
+    __syncthreads();
+    const v8s* rfrag = (const v8s*)rl + lane;
+
+    // this lane's byte offsets in tile u (x, codes); lanes past the row's
+    // last group-row get an offset past the row, so their loads read zeros
+    // (no effect on the absmax) and their stores are dropped
+    int xoff[TW], coff[TW];
+#pragma unroll
+    for (int u = 0; u < TW; ++u) {
+        const int b = u * 16 + j;
+        const bool live = b < gpr;
+        xoff[u] = live ? (b * GP + q * LPL) * 2 : (int)(2 * K);
+        coff[u] = live ? b * GP + q * 16 : (int)K;
+    }
+
+    v8s xf[TW][NKS];
+    auto load_row = [&](int64_t r) {
+        const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + r * sm, (uint32_t)(2 * K));
+#pragma unroll
+        for (int u = 0; u < TW; ++u)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                xf[u][ks] = __builtin_bit_cast(v8s, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[u] + 16 * ks, 0, 0));
+    };
+    if (row < M) load_row(row);
+
+    for (; row < M; row += nw) {
+        if constexpr (SMOOTH) {
+            // x' = T(fp32(x) / fp32(smooth)), one IEEE division per value
+            // (lanes past the row keep their zeros)
+#pragma unroll
+            for (int u = 0; u < TW; ++u) {
+                if (xoff[u] < (int)(2 * K)) {
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int k = xoff[u] / 2 + ks * 8 + e;
+                            xf[u][ks][e] = (short)f32_to_h<DT>(h_to_f32<DT>((uint16_t)xf[u][ks][e]) /
+                                                              h_to_f32<DT>(smooth[k]));
+                        }
+                }
+            }
+        }
+        // rotate every tile, one column tile of R at a time (its two
+        // fragments read from LDS once per row); keep the rounded values
+        // packed; packed absmax per tile
+        uint32_t yp[TW][CT][2];
+        v2u16 um[TW];
+#pragma unroll
+        for (int u = 0; u < TW; ++u) um[u] = (v2u16){0, 0};
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const v8s a0 = rfrag[(ct * NKS + 0) * 64], a1 = rfrag[(ct * NKS + 1) * 64];
+#pragma unroll
+            for (int u = 0; u < TW; ++u) {
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (DT == BF16) {
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a0),
+                                                                 __builtin_bit_cast(v8bf, xf[u][0]), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a1),
+                                                                 __builtin_bit_cast(v8bf, xf[u][1]), acc, 0, 0, 0);
+                } else {
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a0),
+                                                                __builtin_bit_cast(v8h, xf[u][0]), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a1),
+                                                                __builtin_bit_cast(v8h, xf[u][1]), acc, 0, 0, 0);
+                }
+                yp[u][ct][0] = cvt_pair<DT>(acc[0], acc[1]);
+                yp[u][ct][1] = cvt_pair<DT>(acc[2], acc[3]);
+                um[u] = __builtin_elementwise_max(um[u], __builtin_bit_cast(v2u16, yp[u][ct][0] & 0x7fff7fffu));
+                um[u] = __builtin_elementwise_max(um[u], __builtin_bit_cast(v2u16, yp[u][ct][1] & 0x7fff7fffu));
+            }
+            // convert each column tile as soon as it is rotated: only its
+            // MFMA results are live at a time
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        v2u16 amax = um[0];
+#pragma unroll
+        for (int u = 1; u < TW; ++u) amax = __builtin_elementwise_max(amax, um[u]);
+        // the next row's loads go into the x registers the rotation freed
+        const int64_t next = row + nw;
+        if (next < M) load_row(next);
+
+        // row scale: IEEE a / 7, clamped up to the smallest normal
+        const uint32_t a16 = wave_max_u32(max((uint32_t)amax[0], (uint32_t)amax[1]));
+        const float a = DT == BF16 ? __uint_as_float(a16 << 16) : f16_to_f32((uint16_t)a16);
+        float s = a / 7.0f;
+        if (s < 0x1p-126f) s = 0x1p-126f;  // NaN compares false and stays NaN
+        if (lane == 0) scales[row] = s;
+        const bool finite = fabsf(s) < 3.0e38f;
+        const __amdgpu_buffer_rsrc_t rc = row_rsrc(codes + row * K, (uint32_t)K);
+
+        // transpose the codes of tile u (4 x 4 dwords across the lane groups:
+        // lane group q then holds bytes q*16 .. q*16+15 of its group-row) and
+        // store them; the rotated values too when they are exported
+        auto store_tile = [&](int u, const uint32_t (&P)[CT]) {
+            auto s02 = __builtin_amdgcn_permlane32_swap(P[0], P[2], false, false);
+            auto s13 = __builtin_amdgcn_permlane32_swap(P[1], P[3], false, false);
+            auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+            auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+            __builtin_amdgcn_raw_buffer_store_b128((v4u32){s01[0], s01[1], s23[0], s23[1]}, rc, coff[u], 0, 0);
+            if constexpr (YOUT) {
+                // rotated values of columns ct*16 + 4q .. +3: byte offset
+                // 2*(b*64) + 32*ct + 8q
+                const __amdgpu_buffer_rsrc_t ry = row_rsrc(yout + row * K, (uint32_t)(2 * K));
+                const int yo = coff[u] < (int)K ? 2 * (coff[u] - q * 16) + 8 * q : (int)(2 * K);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    __builtin_amdgcn_raw_buffer_store_b64((v2u32){yp[u][ct][0], yp[u][ct][1]}, ry,
+                                                          yo + 32 * ct, 0, 0);
+            }
+        };
+
+        if (__builtin_expect(finite, 1)) {
+            const float rinv = 1.0f / s;
+            const float rh = rinv * (1.0f + 0x1p-21f), rl = rinv * (1.0f - 0x1p-21f);
+#pragma unroll
+            for (int u = 0; u < TW; ++u) {
+                uint32_t P[CT];
+                uint64_t nearm[CT][4];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    float th[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float y = unpack_half<DT>(yp[u][ct][r >> 1], r & 1);
+                        th[r] = __builtin_fmaf(y, rh, kMagic);
+                        const float tl = __builtin_fmaf(y, rl, kMagic);
+                        nearm[ct][r] = __builtin_amdgcn_ballot_w64(__float_as_uint(th[r]) != __float_as_uint(tl));
+                    }
+                    P[ct] = pack_low_bytes(th[0], th[1], th[2], th[3]);
+                }
+                uint64_t any = 0;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) any |= nearm[ct][r];
+                if (__builtin_expect(any != 0, 0)) {
+                    // exact ties: the correctly rounded quotient for the
+                    // flagged elements only
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (nearm[ct][r] != 0 && ((nearm[ct][r] >> lane) & 1)) {
+                                const float y = unpack_half<DT>(yp[u][ct][r >> 1], r & 1);
+                                const uint32_t c = (uint32_t)(code_of_quotient(y / s) & 0xff);
+                                P[ct] = (P[ct] & ~(0xffu << (8 * r))) | (c << (8 * r));
+                            }
+                }
+                store_tile(u, P);
+            }
+        } else {
+            // an Inf or NaN scale: every quotient by IEEE division
+#pragma unroll
+            for (int u = 0; u < TW; ++u) {
+                uint32_t P[CT];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float y = unpack_half<DT>(yp[u][ct][r >> 1], r & 1);
+                        w |= (uint32_t)(code_of_quotient(y / s) & 0xff) << (8 * r);
+                    }
+                    P[ct] = w;
+                }
+                store_tile(u, P);
+            }
+        }
+    }
+}
+
+// Contiguous 16-bit rows, g = 64, 32 < K/64 <= 64 group-rows (four tiles) or
+// 16 < K/64 <= 32 (two tiles), 16-byte aligned rows, codes and smoothing
+// factors, 8-byte aligned rotated export, enough rows to fill the GPU.
+bool row_kernel_ok(const RQArgs& a)
+{
+    const bool sixteen = a.dtype == F16 || a.dtype == BF16;
+    if (!sixteen || !a.rot || a.g != 64 || a.sk != 1 || a.M < 2048) return false;
+    if ((a.K % 64) != 0) return false;
+    const int64_t gpr = a.K / 64;
+    if (gpr <= 16 || gpr > 64) return false;
+    if ((a.sm % 8) != 0 || ((uintptr_t)a.x % 16) != 0 || ((uintptr_t)a.codes % 16) != 0) return false;
+    if ((a.K % 16) != 0) return false;
+    if (a.smooth && ((uintptr_t)a.smooth % 16) != 0) return false;
+    if (a.yout && ((uintptr_t)a.yout % 8) != 0) return false;
+    return true;
+}
+
+template <int DT, bool SMOOTH, bool YOUT, int TW>
+static hipError_t launch_row_t(const RQArgs& a, hipStream_t st)
+{
+    auto kern = rq_row_kernel<DT, SMOOTH, YOUT, TW>;
+    static int per_cu = 0, n_cu = 0;
+    if (per_cu == 0) {
+        int dev = 0;
+        hipDeviceProp_t p;
+        if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&p, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess || per_cu < 1) {
+            per_cu = 2;
+            n_cu = 256;
+        } else {
+            n_cu = p.multiProcessorCount;
+        }
+    }
+    int64_t grid = (int64_t)per_cu * n_cu;
+    const int64_t need = (a.M + 3) / 4;   // four waves (rows) per workgroup
+    if (grid > need) grid = need;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.x, a.M, a.K,
+                       a.sm, a.rot, (const uint16_t*)a.smooth, a.codes, a.scales, (uint16_t*)a.yout);
+    return hipGetLastError();
+}
+
+template <int DT, bool SMOOTH, bool YOUT>
+static hipError_t launch_row_tw(const RQArgs& a, hipStream_t st)
+{
+    const int64_t gpr = a.K / 64;
+    return gpr > 32 ? launch_row_t<DT, SMOOTH, YOUT, 4>(a, st) : launch_row_t<DT, SMOOTH, YOUT, 2>(a, st);
+}
+
+template <int DT>
+static hipError_t launch_row_dt(const RQArgs& a, hipStream_t st)
+{
+    if (a.smooth)
+        return a.yout ? launch_row_tw<DT, true, true>(a, st) : launch_row_tw<DT, true, false>(a, st);
+    return a.yout ? launch_row_tw<DT, false, true>(a, st) : launch_row_tw<DT, false, false>(a, st);
+}
+
+hipError_t launch_rotate_quant_row(const RQArgs& a, hipStream_t st)
+{
+    return a.dtype == BF16 ? launch_row_dt<BF16>(a, st) : launch_row_dt<F16>(a, st);
+}
+
+}  // namespace w4a4

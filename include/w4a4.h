@@ -164,6 +164,7 @@ int w4a4_int32_guard(int64_t K, int64_t* k_chunk);
  *   3 one wave per row block (many contiguous rows, g <= 64)
  *   4 column-major (unit row stride, i.e. a transposed view; M % 8 == 0)
  *   5 g = 256 on contiguous rows
+ *   6 one wave per contiguous row, g = 64, 16 < K/64 <= 64 (many rows)
  * w4a4_gemm_plan, *kernel (has_lowrank: a low-rank term will be added):
  *   0 128 x 128 tiles          1 128 x 128 tiles over K chunks (int64 combine)
  *   2 persistent 256 x 256 ring (prefill-sized M)     3 skinny M (M <= 64)

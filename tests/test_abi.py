@@ -115,7 +115,8 @@ def test_plan_queries_name_the_config_kernels(L):
     import torch
     from bit_quantized_linear_rotate_amd import _binding as b
     bf, h = torch.bfloat16, torch.float16
-    assert b.w4a4_rotate_quant_plan(torch.zeros(8192, 3840, dtype=bf), torch.zeros(64, 64), 64) == "wave"
+    assert b.w4a4_rotate_quant_plan(torch.zeros(8192, 3840, dtype=bf), torch.zeros(64, 64), 64) == "row"
+    assert b.w4a4_rotate_quant_plan(torch.zeros(1600, 3840, dtype=bf), torch.zeros(64, 64), 64) == "wave"
     xt = torch.zeros(10240, 8192, dtype=h).t()
     assert b.w4a4_rotate_quant_plan(xt, torch.zeros(256, 256), 256) == "colmajor"
     assert b.w4a4_rotate_quant_plan(torch.zeros(4096, 16384, dtype=bf), torch.zeros(256, 256), 256,

@@ -261,3 +261,57 @@ def test_skinny_m_equals_large_m_rows():
     small = w4.w4a4_gemm_from_codes(dev(codes[:40]), dev(sa[:40]), dev(wp), dev(sw, "bf16"),
                                     bias=dev(b, "bf16"))
     assert torch.equal(big[:40].view(torch.int16), small.view(torch.int16))
+
+
+def _full_range_weights(rng, N, K):
+    """Packed weights over all 16 nibble patterns, -8 (0x8) included."""
+    w = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
+    w[:, ::7] = -8
+    return w, oracle.pack(w)
+
+
+@pytest.mark.parametrize("M,K,N,kernel", [
+    (300, 1024, 260, "ring3"), (4100, 256, 300, "ring3"),
+    (100, 192, 130, "tile128"), (77, 1024, 40, "tile128"),
+    (32, 3840, 384, "skinny"), (5, 160, 17, "tile128")])
+def test_minus_eight_nibble_every_kernel(M, K, N, kernel):
+    need_gpu()
+    assert w4.w4a4_gemm_plan(M, K, N) == kernel
+    rng = np.random.default_rng(M + N)
+    codes = rng.integers(-7, 8, size=(M, K)).astype(np.int8)
+    wq, wp = _full_range_weights(rng, N, K)
+    sa = rng.uniform(0.01, 0.5, size=M).astype(np.float32)
+    sw = workloads.f32_to_storage(rng.uniform(0.005, 0.02, size=N), "bf16")
+    out = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, "bf16"),
+                                  out_dtype=torch.float32)
+    oacc = oracle.gemm(codes, wq)
+    assert np.array_equal(bits(host(out)), bits(oracle.epilogue(oacc, sa, sw, "bf16", "f32")))
+    # per-64-group scales (the 128 x 128 kernel's group loop)
+    if K % 64 == 0:
+        swg = workloads.f32_to_storage(rng.uniform(0.005, 0.02, size=(K // 64, N)), "bf16")
+        assert w4.w4a4_gemm_plan(M, K, N, 64) == "tile128"
+        outg = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(swg, "bf16"), w_scale_group=64,
+                                       out_dtype=torch.float32)
+        parts = oracle.gemm(codes, wq, group=64)
+        assert np.array_equal(bits(host(outg)), bits(oracle.epilogue(parts, sa, swg, "bf16", "f32",
+                                                                     group=64)))
+
+
+def test_extreme_codes_ring_kernel():
+    # +-7 codes against -8 / 7 weights at K = 16384 through the persistent ring
+    # (no INT32 export there): unit scales and fp32 output give f32(acc), exact
+    # below 2^24
+    need_gpu()
+    M, N, K = 512, 256, 16384
+    assert w4.w4a4_gemm_plan(M, K, N) == "ring3"
+    codes = np.full((M, K), 7, dtype=np.int8)
+    codes[1::2] = -7
+    codes[2::5, ::3] = 0
+    wq = np.full((N, K), -8, dtype=np.int8)
+    wq[::3] = 7
+    wp = oracle.pack(wq)
+    out = w4.w4a4_gemm_from_codes(dev(codes), dev(np.ones(M, np.float32)), dev(wp),
+                                  dev(np.ones(N, np.float32)), out_dtype=torch.float32)
+    oacc = oracle.gemm(codes, wq)
+    assert np.abs(oacc).max() == 56 * K
+    assert np.array_equal(host(out), oacc.astype(np.float32))

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_util import bits, dev, host, need_gpu, same_values, ulp_distance
+from tests.gpu_util import bits, dev, host, need_gpu, rotated_close, same_values, ulp_distance
 
 pytestmark = pytest.mark.gpu
 
@@ -75,10 +75,9 @@ def test_rotated_values_within_tolerance(dt, M, K, g):
         ref = np.abs(a).max(axis=2)
         assert (err <= 1e-5 * ref).all()
     else:
-        d = ulp_distance(yo, yg, dt)
-        assert d.max() <= 1
-        frac = (d > 0).mean()
-        print(f"{dt} M={M} K={K} g={g}: {frac:.2e} of rotated values 1 ulp from the oracle")
+        frac, beyond = rotated_close(yg, yo, x, R, g, dt)
+        print(f"{dt} M={M} K={K} g={g}: {frac:.2e} of rotated values differ from the oracle, "
+              f"{beyond} by more than 1 ulp (within the fp32 summation bound)")
 
 
 @pytest.mark.parametrize("dt,M,K,g", CASES)
@@ -86,14 +85,24 @@ def test_end_to_end_code_flips(dt, M, K, g):
     need_gpu()
     x = _draw(dt, M, K, seed=3 * M + K)
     R = workloads.hadamard(g)
-    _, oc, os_ = oracle.rotate_quant(x, R, g, dt)
+    yo, oc, os_ = oracle.rotate_quant(x, R, g, dt)
     c, s = w4.w4a4_rotate_quant_rowwise(dev(x, dt), _rot_dev(R), g)
     c, s = host(c), host(s)
+    _, _, yg = w4.w4a4_rotate_quant_rowwise(dev(x, dt), _rot_dev(R), g, return_rotated=True)
+    yg = host(yg)
     same_scale = bits(s) == bits(os_)
+    # a row with another scale must be the oracle quantizer's result on the
+    # GPU's own rotated row, whose values are within 1 ulp of the oracle's
+    # (or the fp32 summation bound)
+    other = np.flatnonzero(~same_scale)
+    if other.size:
+        qc, qs = oracle.quantize(yg[other], dt)
+        assert np.array_equal(qc, c[other]) and np.array_equal(bits(qs), bits(s[other]))
+        if dt != "f32":
+            rotated_close(yg[other], yo[other], x[other], R, g, dt)
     d = np.abs(c.astype(np.int32) - oc)
-    assert d[same_scale].max(initial=0) <= 1
-    assert (d[same_scale] > 0).mean() <= 1e-4 if same_scale.any() else True
-    assert (~same_scale).sum() <= max(1, 0.05 * M)
+    assert d.max(initial=0) <= 1
+    assert (d > 0).sum() <= 1e-4 * M * K
 
 
 @pytest.mark.parametrize("dt,M,K,g", [("bf16", 7, 48, 16), ("f16", 5, 80, 16), ("f32", 9, 272, 16),
@@ -165,8 +174,9 @@ def test_smoothing(dt):
     assert np.array_equal(bits(host(y0)), bits(oracle.smooth(x, sm, dt)))
     c, s, yg = w4.w4a4_rotate_quant_rowwise(dev(x, dt), _rot_dev(R), g, smooth=dev(sm, dt),
                                             return_rotated=True)
-    yo = oracle.rotate(oracle.smooth(x, sm, dt), R, g, dt)
-    assert ulp_distance(yo, host(yg), dt).max() <= 1
+    xs = oracle.smooth(x, sm, dt)
+    yo = oracle.rotate(xs, R, g, dt)
+    rotated_close(host(yg), yo, xs, R, g, dt)
 
 
 def test_empty_and_rejections():
@@ -245,7 +255,10 @@ def test_column_major_with_smoothing(dt, M, K, edge):
     ("bf16", 67, 1024, 1024),     # 16 groups per row: TW 1, one row per block
     ("f16", 33, 1536, 1536),      # TW 2
     ("bf16", 130, 4096, 4096),    # 64 groups per row: every lane of TW 4
-    ("bf16", 2600, 3840, 3840),   # more row blocks than waves: each wave takes several
+    ("bf16", 1600, 3840, 3840),   # more row blocks than waves: each wave takes several
+    ("bf16", 2600, 3840, 3840),   # the row-streaming kernel (one wave per row)
+    ("f16", 4100, 2560, 2560),    # row-streaming, two tiles a row, ragged last wave
+    ("bf16", 2048, 3840, 4096),   # row-streaming with strided rows
     ("f16", 300, 3840, 4160),     # strided rows (a column slice of a wider buffer)
 ])
 def test_row_major_g64_shapes(dt, M, K, sm):
@@ -262,22 +275,25 @@ def test_row_major_g64_shapes(dt, M, K, sm):
     c, s, yg = w4.w4a4_rotate_quant_rowwise(x, _rot_dev(R), g, return_rotated=True)
     oc, os2 = oracle.quantize(host(yg), dt)
     assert np.array_equal(host(c), oc) and np.array_equal(bits(host(s)), bits(os2))
-    yo = oracle.rotate(np.ascontiguousarray(buf[:, :K]), R, g, dt)
-    assert ulp_distance(yo, host(yg), dt).max() <= 1
+    xk = np.ascontiguousarray(buf[:, :K])
+    yo = oracle.rotate(xk, R, g, dt)
+    frac, beyond = rotated_close(host(yg), yo, xk, R, g, dt)
+    print(f"{dt} M={M} K={K}: {frac:.2e} of rotated values differ, {beyond} beyond 1 ulp")
     c2, s2 = w4.w4a4_rotate_quant_rowwise(x, _rot_dev(R), g)
     assert np.array_equal(host(c2), host(c)) and np.array_equal(bits(host(s2)), bits(host(s)))
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f16"])
-def test_row_major_g64_with_smoothing(dt):
+@pytest.mark.parametrize("dt,M", [("bf16", 50), ("f16", 50), ("bf16", 2100), ("f16", 2100)])
+def test_row_major_g64_with_smoothing(dt, M):
     need_gpu()
-    M, K, g = 50, 2048, 64
+    K, g = 2048, 64
     x = _draw(dt, M, K, seed=13)
     sm = workloads.f32_to_storage(np.random.default_rng(6).uniform(0.5, 2.0, size=K), dt)
     R = workloads.hadamard(g)
     c, s, yg = w4.w4a4_rotate_quant_rowwise(dev(x, dt), _rot_dev(R), g, smooth=dev(sm, dt),
                                             return_rotated=True)
-    yo = oracle.rotate(oracle.smooth(x, sm, dt), R, g, dt)
-    assert ulp_distance(yo, host(yg), dt).max() <= 1
+    xs = oracle.smooth(x, sm, dt)
+    yo = oracle.rotate(xs, R, g, dt)
+    rotated_close(host(yg), yo, xs, R, g, dt)
     oc, os2 = oracle.quantize(host(yg), dt)
     assert np.array_equal(host(c), oc) and np.array_equal(bits(host(s)), bits(os2))
