@@ -18,10 +18,11 @@ mismatch ends the run with an error.  The statistics go into the line.
 --no-cpu skips the whole CPU leg (parity and baseline).
 
 Each kernel is then timed alone on the stream it runs on, over max(steps, 50)
-launches: the mean launch duration from one HIP event pair around the
-back-to-back launches (the figure rocprofv3's kernel statistics average, and
-the one `roofline.achieved` divides the kernel's algorithmic work by), and
-median, p10 and p90 from a second pass with an event pair around every launch.
+launches with a HIP event pair around every launch: their mean (the figure
+rocprofv3's kernel statistics average, and the one `roofline.achieved`
+divides the kernel's algorithmic work by), median, p10 and p90; plus the
+average over one event pair around the back-to-back launches (ms_loop,
+which includes the gaps between kernels).
 
 The line also carries the other four workloads (wide-K transposed-view fp16,
 decode-like M=32, tiny fp32, large-K with smoothing, per-64-group scales and a
@@ -118,20 +119,13 @@ def _variant(d, i, torch):
 def _time_each(fn, n, torch, np):
     """Two passes of n calls each, HIP events on the current stream (the
     stream the binding launches on):
-      * ms_mean: one event pair around n back-to-back launches, divided by n:
-        the kernel's average launch duration as rocprofv3 reports it (the
-        roofline figures use this);
-      * ms_median / ms_p10 / ms_p90: an event pair around every launch (each
-        event adds a few microseconds of its own)."""
+      * an event pair around every launch: ms_mean (their mean: the kernel's
+        average launch duration, the figure rocprofv3's kernel statistics
+        average and the one the roofline figures divide by), ms_median,
+        ms_p10, ms_p90;
+      * ms_loop: one event pair around n back-to-back launches, divided by n
+        (includes the gaps between consecutive kernels)."""
     st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(st)
-    for i in range(n):
-        fn(i)
-    e1.record(st)
-    e1.synchronize()
-    mean = e0.elapsed_time(e1) / n
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n)]
     torch.cuda.synchronize()
@@ -141,9 +135,16 @@ def _time_each(fn, n, torch, np):
         ev[i][1].record(st)
     ev[-1][1].synchronize()
     a = np.asarray([x.elapsed_time(y) for x, y in ev], dtype=np.float64)
-    return {"ms_mean": float(mean), "launches": int(n),
-            "per_launch_events": {"ms_median": float(np.median(a)), "ms_p10": float(np.percentile(a, 10)),
-                                  "ms_p90": float(np.percentile(a, 90))}}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for i in range(n):
+        fn(i)
+    e1.record(st)
+    e1.synchronize()
+    loop = e0.elapsed_time(e1) / n
+    return {"ms_mean": float(a.mean()), "ms_median": float(np.median(a)), "ms_p10": float(np.percentile(a, 10)),
+            "ms_p90": float(np.percentile(a, 90)), "ms_loop": float(loop), "launches": int(n)}
 
 
 def _dtcode(torch, t):
@@ -270,12 +271,24 @@ def measure(name, steps, warmup, torch, np, w4, workloads, cpu=True):
     if w.smooth:
         rq_bytes += K * base["x"].element_size()
 
-    # GEMM + epilogue alone, on the codes just produced
+    # GEMM + epilogue alone, on the codes just produced, through the C ABI
+    # with prepared arguments (the binding's own host time would otherwise
+    # show in the loop average of a ~0.1 ms kernel)
+    gws = w4.w4a4_gemm_workspace_size(M, N, K, 0)
+    assert gws == 0, "the timed GEMM configurations need no workspace"
+    odt = _dtcode(torch, outs[0])
+
     def gemm(i):
         s = sets[i % 4]
         c, sc = qbufs[i % 4]
-        w4.w4a4_gemm_from_codes(c, sc, s["w_packed"], s["w_scale"], w_scale_group=w.sw_group,
-                                bias=s["bias"], out_dtype=outs[i % 4].dtype)
+        b_ = s["bias"]
+        rc = lib.w4a4_gemm_from_codes(
+            c.data_ptr(), sc.data_ptr(), M, K, s["w_packed"].data_ptr(), N, s["w_scale"].data_ptr(),
+            _dtcode(torch, s["w_scale"]), w.sw_group, b_.data_ptr() if b_ is not None else None,
+            _dtcode(torch, b_) if b_ is not None else 0, None, None, 0, 0, outs[i % 4].data_ptr(), odt,
+            None, 0, None, 0, stream)
+        if rc:
+            b._check(rc, "w4a4_gemm_from_codes")
     for i in range(warmup):
         gemm(i)
     t_gemm = _time_each(gemm, nk, torch, np)
@@ -326,6 +339,47 @@ def measure(name, steps, warmup, torch, np, w4, workloads, cpu=True):
                                "frac_hbm": lrd_bytes / (t_lrd["ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                "algorithmic_bytes": lrd_bytes}
     return w, inp, res
+
+
+def stream_ceiling(w, steps, torch, np):
+    """The HBM ceiling for rotate-quant's traffic on this device: a plain
+    streaming kernel of this repository (bit_quantized_linear_rotate_amd/
+    csrc/stream_probe.hip, no rotation, no quantizer) that reads the same M*K
+    16-bit values and writes the same M*K + 4*M bytes, over four cycled
+    buffer sets, at several grid sizes, with ordinary and with non-temporal
+    stores; the best mean per launch counts."""
+    import ctypes
+    from bit_quantized_linear_rotate_amd import build as bld
+    if not os.path.exists(bld.PROBE_LIB):
+        return None
+    L = ctypes.CDLL(bld.PROBE_LIB)
+    L.w4a4_stream_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.w4a4_stream_probe.restype = ctypes.c_int
+    M, K = w.M, w.K
+    xs = [torch.empty((M, K), dtype=torch.bfloat16, device="cuda").normal_() for _ in range(4)]
+    cs = [torch.empty((M, K), dtype=torch.int8, device="cuda") for _ in range(4)]
+    ss = [torch.empty((M,), dtype=torch.float32, device="cuda") for _ in range(4)]
+    stream = torch.cuda.current_stream().cuda_stream
+    nbytes = M * K * 2 + M * K + 4 * M
+    best = None
+    for nt in (0, 1):
+        for grid in (2048, 4096, 8192, 16384):
+            def run(i):
+                rc = L.w4a4_stream_probe(xs[i % 4].data_ptr(), M * K, cs[i % 4].data_ptr(), ss[i % 4].data_ptr(),
+                                         M, grid, nt, stream)
+                if rc:
+                    raise RuntimeError(f"stream probe: hip error {rc}")
+            for i in range(5):
+                run(i)
+            t = _time_each(run, max(steps, MIN_KERNEL_LAUNCHES), torch, np)
+            if best is None or t["ms_mean"] < best[0]["ms_mean"]:
+                best = (t, grid, nt)
+    t, grid, nt = best
+    return {"kernel": "stream_probe_kernel (same bytes as rotate-quant, no arithmetic)",
+            **t, "grid": grid, "nontemporal_stores": bool(nt), "bytes": nbytes,
+            "GB_s": nbytes / (t["ms_mean"] * 1e-3) / 1e9,
+            "frac_hbm_peak": nbytes / (t["ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def cpu_baseline(w, inp, np, target_s=15.0):
@@ -401,6 +455,7 @@ def main():
             _, _, extras[name] = measure(name, max(10, args.steps // 2), args.warmup, torch, np, w4,
                                          workloads, cpu=cpu)
             print(f"# {name}: {extras[name]['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+    ceiling = stream_ceiling(w, args.steps, torch, np) if w.dtype == "bf16" else None
     g = main_res["gemm"]
     rq = main_res["rotate_quant"]
     line = {
@@ -425,12 +480,16 @@ def main():
                      "unit": "TOPS", "frac": round(g["frac_int8"], 4),
                      "traffic": _traffic("gemm", args.workload),
                      "kernel": g["kernel"] + " (INT8 MFMA GEMM + fused scale/bias/cast epilogue)",
-                     "per_launch_ms": "mean over the timed launches"},
+                     "per_launch_ms": "mean of per-launch HIP event pairs"},
         "roofline_rotate_quant": {"bound": "hbm", "achieved": round(rq["GB_s"], 1),
                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": round(rq["frac_hbm"], 4),
                                   "traffic": _traffic("rotate_quant", args.workload),
-                                  "kernel": rq["kernel"] + " (block rotation on MFMA, row absmax, INT4 codes)"},
+                                  "kernel": rq["kernel"] + " (block rotation on MFMA, row absmax, INT4 codes)",
+                                  "measured_stream_ceiling_GB_s": round(ceiling["GB_s"], 1) if ceiling else None,
+                                  "frac_of_measured_ceiling": round(rq["GB_s"] / ceiling["GB_s"], 4)
+                                  if ceiling else None},
+        "stream_ceiling": _rounded(ceiling) if ceiling else None,
     }
     for name, extra in extras.items():
         line[name] = {"workload": extra["workload"], "ms_per_step": round(extra["ms_per_step"], 5),

@@ -74,6 +74,22 @@ __device__ __forceinline__ void store_any(int dt, void* p, int64_t i, float v)
 }
 
 // IEEE-exact fp32 multiply and add (never contracted into an FMA).
+// Non-temporal (streaming) stores for outputs that no later kernel of the
+// same call reads back soon: codes and exported rotated values are written
+// once and would otherwise displace the input rows still to be read from the
+// caches.  Only for stores that fill whole 64-byte pieces of a line across a
+// wave: scattered 4-byte streaming stores measured slower than plain ones.
+typedef unsigned v4u_st __attribute__((ext_vector_type(4)));
+typedef unsigned v2u_st __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_stream16(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    __builtin_nontemporal_store((v4u_st){a, b, c, d}, (v4u_st*)p);
+}
+__device__ __forceinline__ void st_stream8(void* p, uint32_t a, uint32_t b)
+{
+    __builtin_nontemporal_store((v2u_st){a, b}, (v2u_st*)p);
+}
+
 __device__ __forceinline__ float mul_rn(float a, float b) { return __fmul_rn(a, b); }
 __device__ __forceinline__ float add_rn(float a, float b) { return __fadd_rn(a, b); }
 

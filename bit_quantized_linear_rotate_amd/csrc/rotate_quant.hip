@@ -338,12 +338,12 @@ __global__ __launch_bounds__(256) void rq_mfma_kernel(
             }
             w[d] = packed;
         }
-        uint4 out = {w[0], w[1], w[2], w[3]};
-        *(uint4*)(codes + (m0 + r) * K + k0) = out;
+        st_stream16(codes + (m0 + r) * K + k0, w[0], w[1], w[2], w[3]);
         if (yout) {
-            uint4* yo = (uint4*)(yout + (m0 + r) * K + k0);
-            yo[0] = __builtin_bit_cast(uint4, y0);
-            yo[1] = __builtin_bit_cast(uint4, y1);
+            uint16_t* yo = yout + (m0 + r) * K + k0;
+            const uint4 a0 = __builtin_bit_cast(uint4, y0), a1 = __builtin_bit_cast(uint4, y1);
+            st_stream16(yo, a0.x, a0.y, a0.z, a0.w);
+            st_stream16(yo + 8, a1.x, a1.y, a1.z, a1.w);
         }
     }
 }
@@ -662,7 +662,7 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
             const int row = c / (GP / 16), ch = c % (GP / 16);
             const v4i v = lds_read16(ct + (c < CCH ? row * GP + ch * 16 : 0));
             const int off = c < CCH ? (int)((m0 + row) * K + (int64_t)bs * GP + ch * 16) : CM_OOB;
-            __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 2);  // non-temporal
         }
         if constexpr (YOUT) {
             const uint16_t* yt = ytile[st & 1];
@@ -672,7 +672,7 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
                 const int row = c / (GP / 8), ch = c % (GP / 8);
                 const v4i v = lds_read16(yt + (c < YCH ? row * GP + ch * 8 : 0));
                 const int off = c < YCH ? (int)(((m0 + row) * K + (int64_t)bs * GP + ch * 8) * 2) : CM_OOB;
-                __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 2);
             }
         }
     };
@@ -1046,7 +1046,7 @@ __global__ __launch_bounds__(256) void rq_reg_kernel(
                 uint32_t w0 = o4[0], w1 = o4[1], w2 = o4[2], w3 = o4[3];
                 if (live) {
                     int8_t* crow = codes + (m0 + rl) * K + (int64_t)b * GP;
-                    *(uint4*)(crow + q * 16) = make_uint4(w0, w1, w2, w3);
+                    st_stream16(crow + q * 16, w0, w1, w2, w3);
                 }
             } else {
                 if (live) {
@@ -1058,8 +1058,7 @@ __global__ __launch_bounds__(256) void rq_reg_kernel(
             if (live && yout) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    uint2 yy = make_uint2(yv[u][ct][0], yv[u][ct][1]);
-                    *(uint2*)(yout + (m0 + rl) * K + (int64_t)b * GP + ct * 16 + 4 * q) = yy;
+                    st_stream8(yout + (m0 + rl) * K + (int64_t)b * GP + ct * 16 + 4 * q, yv[u][ct][0], yv[u][ct][1]);
                 }
             }
         }
@@ -1310,7 +1309,7 @@ __global__ __launch_bounds__(256, TW >= 4 ? 2 : 3) void rq_wave_kernel(
                     v = send == 3 ? pk[3] : v;
                     o4[(q + t) & 3] = (uint32_t)__shfl((int)v, j + 16 * ((q + t) & 3));
                 }
-                if (live) *(uint4*)(cb + t_coff[u] + q * 16) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+                if (live) st_stream16(cb + t_coff[u] + q * 16, o4[0], o4[1], o4[2], o4[3]);
             } else {
                 if (live) {
 #pragma unroll
@@ -1320,7 +1319,7 @@ __global__ __launch_bounds__(256, TW >= 4 ? 2 : 3) void rq_wave_kernel(
             if (live && yb) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
-                    *(uint2*)(yb + t_coff[u] + ct * 16 + 4 * q) = make_uint2(yv[ct][0], yv[ct][1]);
+                    st_stream8(yb + t_coff[u] + ct * 16 + 4 * q, yv[ct][0], yv[ct][1]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }

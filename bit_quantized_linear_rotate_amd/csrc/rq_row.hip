@@ -27,10 +27,13 @@
 //     add rounds the exact product to an integer and leaves it in the low
 //     byte), bracket the correctly rounded quotient fl(y / s): when they agree
 //     that integer IS the code (rounding is monotone).  They disagree only
-//     when y / s lies within 2^-18 of a half-integer, which for 16-bit y and a
-//     scale taken from the row's own 16-bit absmax happens only at exact ties
-//     (14 y = (2k + 1) absmax): those elements, flagged by a per-element
-//     ballot, are redone with an IEEE division in an out-of-line pass.
+//     when y / s lies within 2^-20 of a half-integer, which for 16-bit y and a
+//     scale taken from the row's own 16-bit absmax a happens only at exact
+//     ties 7 y = (k + 1/2) a, k = 0..6.  All elements of a row that tie at
+//     the same k have the same |y|, so seven IEEE divisions per row (one per
+//     lane) decide, once, whether each k rounds away from zero; every element
+//     then takes its code from the two integers and that 7-bit table with
+//     three integer operations, with no branch and no per-element division.
 //     Rows whose scale is Inf or NaN take the division for every element.
 //   * Each lane holds four codes of each of four column tiles; two
 //     v_permlane32_swap and two v_permlane16_swap transpose them so that every
@@ -78,19 +81,57 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return max(max(r0, r1), max(r2, r3));
 }
 
-// low byte of each of four fp32 magic sums -> four codes in one dword
-__device__ __forceinline__ uint32_t pack_low_bytes(float t0, float t1, float t2, float t3)
-{
-    const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x0c0c0400u);
-    const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(t3), __float_as_uint(t2), 0x0c0c0400u);
-    return lo | (hi << 16);
-}
-
 // buffer resource over `bytes` bytes at `base`: accesses whose per-lane
 // offset falls outside read zeros / are dropped
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+// Tie table of a row with absmax a and finite scale s.  An element whose
+// two bracketing roundings differ is an exact tie y = h * a / 7, h = k + 1/2
+// (k = 0..6), whose code is either k or k + 1 in magnitude; bit k of the
+// result says "k + 1".  Lane k < 7 divides exactly as the quantizer does for
+// that y: y_h = fl(fl(h * a) / 7) is exact whenever h * a / 7 is a 16-bit
+// value at all (otherwise no element can tie at h), computed at a 2^-64
+// scale for large a so that h * a cannot overflow; q_h = fl(y_h / s).  When
+// the scale was clamped to 2^-126, y / s = y * 2^126 exactly and a tie
+// rounds to even.  The returned mask is indexed by the low five bits of the
+// toward-zero code's two's-complement byte: bit k for code k >= 0 and bit
+// 32 - k for code -k.
+__device__ __forceinline__ uint32_t tie_mask(float a, float s, bool clamped, int lane)
+{
+    uint32_t b;
+    if (clamped) {
+        b = 0x2au;  // k odd: h = k + 1/2 rounds to even k + 1
+    } else {
+        const float h = (float)(lane & 7) + 0.5f;
+        const bool big = a > 0x1p64f;
+        const float ah = big ? a * 0x1p-64f : a;
+        float yh = (h * ah) / 7.0f;
+        if (big) yh *= 0x1p64f;
+        const float qh = yh / s;
+        const bool up = lane < 7 && rintf(qh) > h;
+        b = (uint32_t)__builtin_amdgcn_ballot_w64(up) & 0x7fu;
+    }
+    return b | (__builtin_bitreverse32(b) << 1);
+}
+
+// code byte of y from its two bracketing roundings (magic sums) and the tie
+// mask: t_dn when they agree (then t_up == t_dn), else the tie's outcome
+__device__ __forceinline__ uint32_t tie_select(float t_up, float t_dn, uint32_t mask)
+{
+    const uint32_t u = __float_as_uint(t_up), d = __float_as_uint(t_dn);
+    const uint32_t up = __builtin_amdgcn_ubfe(mask, d & 31u, 1u);
+    return d + up * (u - d);
+}
+
+// four code bytes (in the low byte of each value) in one dword
+__device__ __forceinline__ uint32_t pack_bytes(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(c1, c0, 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(c3, c2, 0x0c0c0400u);
+    return lo | (hi << 16);
 }
 
 // correctly rounded code for a finite or non-finite quotient (NaN -> 0)
@@ -102,13 +143,14 @@ __device__ __forceinline__ int code_of_quotient(float qv)
 
 }  // namespace
 
-template <int DT, bool SMOOTH, bool YOUT, int TW>
-__global__ __launch_bounds__(256, 4) void rq_row_kernel(
+template <int DT, bool SMOOTH, bool YOUT, int TW, int PF>
+__global__ __launch_bounds__(256, 2) void rq_row_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t sm,
     const float* __restrict__ rot, const uint16_t* __restrict__ smooth,
     int8_t* __restrict__ codes, float* __restrict__ scales, uint16_t* __restrict__ yout)
 {
     constexpr int GP = 64, CT = 4, NKS = 2, LPL = 16;
+    constexpr int kNT = 2;  // cache policy of the output stores: non-temporal
     const int lane = threadIdx.x & 63;
     const int j = lane & 15, q = lane >> 4;
     const int gpr = (int)(K / GP);
@@ -117,18 +159,6 @@ __global__ __launch_bounds__(256, 4) void rq_row_kernel(
     // and store is a scalar base plus a 32-bit lane offset
     const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + wid;
-
-    // R's MFMA fragments in LDS, built once per workgroup: fragment
-    // f = ct*2 + ks, lane (j, q) reads 16 bytes at (f*64 + lane)*16 holding
-    // T(R[q*16 + ks*8 + e][ct*16 + j]) for e = 0..7
-    __shared__ __align__(16) uint16_t rl[CT * NKS * 64 * 8];
-    for (int i = threadIdx.x; i < CT * NKS * 64 * 8; i += blockDim.x) {
-        const int f = i >> 9, l = (i >> 3) & 63, e = i & 7;
-        const int ct = f >> 1, ks = f & 1, jj = l & 15, qq = l >> 4;
-        rl[i] = f32_to_h<DT>(rot[(qq * LPL + ks * 8 + e) * GP + ct * 16 + jj]);
-    }
-    __syncthreads();
-    const v8s* rfrag = (const v8s*)rl + lane;
 
     // this lane's byte offsets in tile u (x, codes); lanes past the row's
     // last group-row get an offset past the row, so their loads read zeros
@@ -142,18 +172,36 @@ __global__ __launch_bounds__(256, 4) void rq_row_kernel(
         coff[u] = live ? b * GP + q * 16 : (int)K;
     }
 
-    v8s xf[TW][NKS];
-    auto load_row = [&](int64_t r) {
-        const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + r * sm, (uint32_t)(2 * K));
+    // PF rows in flight per wave, each in its own set of x registers.  Rows
+    // past M get a zero-sized resource: their loads read zeros and touch no
+    // memory, so the loads need no branch (and the compiler's wait counts
+    // stay exact)
+    v8s xf[PF][TW][NKS];
+    auto load_row = [&](v8s (&buf)[TW][NKS], int64_t r) {
+        const __amdgpu_buffer_rsrc_t rx = r < M ? row_rsrc(x + r * sm, (uint32_t)(2 * K)) : row_rsrc(x, 0u);
 #pragma unroll
         for (int u = 0; u < TW; ++u)
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                xf[u][ks] = __builtin_bit_cast(v8s, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[u] + 16 * ks, 0, 0));
+                buf[u][ks] = __builtin_bit_cast(v8s, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[u] + 16 * ks, 0, 0));
     };
-    if (row < M) load_row(row);
+#pragma unroll
+    for (int p = 0; p < PF; ++p) load_row(xf[p], row + p * nw);
 
-    for (; row < M; row += nw) {
+    // R's MFMA fragments (A operand) in registers, rounded to T: fragment
+    // f = ct*2 + ks of lane (j, q) holds T(R[q*16 + ks*8 + e][ct*16 + j]),
+    // e = 0..7 (read once per wave from the fp32 matrix, after the first
+    // rows' loads are on their way)
+    v8s rf[CT * NKS];
+#pragma unroll
+    for (int f = 0; f < CT * NKS; ++f)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            rf[f][e] = (short)f32_to_h<DT>(rot[(q * LPL + (f & 1) * 8 + e) * GP + (f >> 1) * 16 + j]);
+
+    // one row: rotate, absmax, refill this buffer with the row PF*nw ahead,
+    // scale, codes
+    auto process = [&](v8s (&buf)[TW][NKS], int64_t r) {
         if constexpr (SMOOTH) {
             // x' = T(fp32(x) / fp32(smooth)), one IEEE division per value
             // (lanes past the row keep their zeros)
@@ -165,35 +213,34 @@ __global__ __launch_bounds__(256, 4) void rq_row_kernel(
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const int k = xoff[u] / 2 + ks * 8 + e;
-                            xf[u][ks][e] = (short)f32_to_h<DT>(h_to_f32<DT>((uint16_t)xf[u][ks][e]) /
-                                                              h_to_f32<DT>(smooth[k]));
+                            buf[u][ks][e] = (short)f32_to_h<DT>(h_to_f32<DT>((uint16_t)buf[u][ks][e]) /
+                                                               h_to_f32<DT>(smooth[k]));
                         }
                 }
             }
         }
-        // rotate every tile, one column tile of R at a time (its two
-        // fragments read from LDS once per row); keep the rounded values
-        // packed; packed absmax per tile
+        // rotate every tile, one column tile of R at a time; keep the rounded
+        // values packed; packed absmax per tile
         uint32_t yp[TW][CT][2];
         v2u16 um[TW];
 #pragma unroll
         for (int u = 0; u < TW; ++u) um[u] = (v2u16){0, 0};
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-            const v8s a0 = rfrag[(ct * NKS + 0) * 64], a1 = rfrag[(ct * NKS + 1) * 64];
+            const v8s a0 = rf[ct * NKS + 0], a1 = rf[ct * NKS + 1];
 #pragma unroll
             for (int u = 0; u < TW; ++u) {
                 v4f acc = {0.f, 0.f, 0.f, 0.f};
                 if constexpr (DT == BF16) {
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a0),
-                                                                 __builtin_bit_cast(v8bf, xf[u][0]), acc, 0, 0, 0);
+                                                                 __builtin_bit_cast(v8bf, buf[u][0]), acc, 0, 0, 0);
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a1),
-                                                                 __builtin_bit_cast(v8bf, xf[u][1]), acc, 0, 0, 0);
+                                                                 __builtin_bit_cast(v8bf, buf[u][1]), acc, 0, 0, 0);
                 } else {
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a0),
-                                                                __builtin_bit_cast(v8h, xf[u][0]), acc, 0, 0, 0);
+                                                                __builtin_bit_cast(v8h, buf[u][0]), acc, 0, 0, 0);
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a1),
-                                                                __builtin_bit_cast(v8h, xf[u][1]), acc, 0, 0, 0);
+                                                                __builtin_bit_cast(v8h, buf[u][1]), acc, 0, 0, 0);
                 }
                 yp[u][ct][0] = cvt_pair<DT>(acc[0], acc[1]);
                 yp[u][ct][1] = cvt_pair<DT>(acc[2], acc[3]);
@@ -207,18 +254,17 @@ __global__ __launch_bounds__(256, 4) void rq_row_kernel(
         v2u16 amax = um[0];
 #pragma unroll
         for (int u = 1; u < TW; ++u) amax = __builtin_elementwise_max(amax, um[u]);
-        // the next row's loads go into the x registers the rotation freed
-        const int64_t next = row + nw;
-        if (next < M) load_row(next);
+        // the row PF*nw ahead goes into the x registers the rotation freed
+        load_row(buf, r + PF * nw);
 
         // row scale: IEEE a / 7, clamped up to the smallest normal
         const uint32_t a16 = wave_max_u32(max((uint32_t)amax[0], (uint32_t)amax[1]));
         const float a = DT == BF16 ? __uint_as_float(a16 << 16) : f16_to_f32((uint16_t)a16);
         float s = a / 7.0f;
         if (s < 0x1p-126f) s = 0x1p-126f;  // NaN compares false and stays NaN
-        if (lane == 0) scales[row] = s;
+        if (lane == 0 && r < M) scales[r] = s;
         const bool finite = fabsf(s) < 3.0e38f;
-        const __amdgpu_buffer_rsrc_t rc = row_rsrc(codes + row * K, (uint32_t)K);
+        const __amdgpu_buffer_rsrc_t rc = r < M ? row_rsrc(codes + r * K, (uint32_t)K) : row_rsrc(codes, 0u);
 
         // transpose the codes of tile u (4 x 4 dwords across the lane groups:
         // lane group q then holds bytes q*16 .. q*16+15 of its group-row) and
@@ -228,55 +274,36 @@ __global__ __launch_bounds__(256, 4) void rq_row_kernel(
             auto s13 = __builtin_amdgcn_permlane32_swap(P[1], P[3], false, false);
             auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
             auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
-            __builtin_amdgcn_raw_buffer_store_b128((v4u32){s01[0], s01[1], s23[0], s23[1]}, rc, coff[u], 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128((v4u32){s01[0], s01[1], s23[0], s23[1]}, rc, coff[u], 0, kNT);
             if constexpr (YOUT) {
                 // rotated values of columns ct*16 + 4q .. +3: byte offset
                 // 2*(b*64) + 32*ct + 8q
-                const __amdgpu_buffer_rsrc_t ry = row_rsrc(yout + row * K, (uint32_t)(2 * K));
+                const __amdgpu_buffer_rsrc_t ry =
+                    r < M ? row_rsrc(yout + r * K, (uint32_t)(2 * K)) : row_rsrc(yout, 0u);
                 const int yo = coff[u] < (int)K ? 2 * (coff[u] - q * 16) + 8 * q : (int)(2 * K);
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
                     __builtin_amdgcn_raw_buffer_store_b64((v2u32){yp[u][ct][0], yp[u][ct][1]}, ry,
-                                                          yo + 32 * ct, 0, 0);
+                                                          yo + 32 * ct, 0, kNT);
             }
         };
 
         if (__builtin_expect(finite, 1)) {
             const float rinv = 1.0f / s;
             const float rh = rinv * (1.0f + 0x1p-21f), rl = rinv * (1.0f - 0x1p-21f);
+            const uint32_t tmask = tie_mask(a, s, s == 0x1p-126f, lane);
 #pragma unroll
             for (int u = 0; u < TW; ++u) {
                 uint32_t P[CT];
-                uint64_t nearm[CT][4];
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    float th[4];
+                    uint32_t c[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float y = unpack_half<DT>(yp[u][ct][r >> 1], r & 1);
-                        th[r] = __builtin_fmaf(y, rh, kMagic);
-                        const float tl = __builtin_fmaf(y, rl, kMagic);
-                        nearm[ct][r] = __builtin_amdgcn_ballot_w64(__float_as_uint(th[r]) != __float_as_uint(tl));
+                    for (int i = 0; i < 4; ++i) {
+                        const float y = unpack_half<DT>(yp[u][ct][i >> 1], i & 1);
+                        c[i] = tie_select(__builtin_fmaf(y, rh, kMagic), __builtin_fmaf(y, rl, kMagic), tmask);
                     }
-                    P[ct] = pack_low_bytes(th[0], th[1], th[2], th[3]);
-                }
-                uint64_t any = 0;
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) any |= nearm[ct][r];
-                if (__builtin_expect(any != 0, 0)) {
-                    // exact ties: the correctly rounded quotient for the
-                    // flagged elements only
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (nearm[ct][r] != 0 && ((nearm[ct][r] >> lane) & 1)) {
-                                const float y = unpack_half<DT>(yp[u][ct][r >> 1], r & 1);
-                                const uint32_t c = (uint32_t)(code_of_quotient(y / s) & 0xff);
-                                P[ct] = (P[ct] & ~(0xffu << (8 * r))) | (c << (8 * r));
-                            }
+                    P[ct] = pack_bytes(c[0], c[1], c[2], c[3]);
                 }
                 store_tile(u, P);
             }
@@ -289,16 +316,28 @@ __global__ __launch_bounds__(256, 4) void rq_row_kernel(
                 for (int ct = 0; ct < CT; ++ct) {
                     uint32_t w = 0;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float y = unpack_half<DT>(yp[u][ct][r >> 1], r & 1);
-                        w |= (uint32_t)(code_of_quotient(y / s) & 0xff) << (8 * r);
+                    for (int i = 0; i < 4; ++i) {
+                        const float y = unpack_half<DT>(yp[u][ct][i >> 1], i & 1);
+                        w |= (uint32_t)(code_of_quotient(y / s) & 0xff) << (8 * i);
                     }
                     P[ct] = w;
                 }
                 store_tile(u, P);
             }
         }
-    }
+    };
+
+    // every wave takes at least one pass (a row past M is all zeros in and
+    // nothing out), so no branch guards the loop and the first rows' loads
+    // stay where they are issued, ahead of R's
+    do {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            process(xf[p], row);
+            row += nw;
+            if (p + 1 < PF && row >= M) break;
+        }
+    } while (row < M);
 }
 
 // Contiguous 16-bit rows, g = 64, 32 < K/64 <= 64 group-rows (four tiles) or
@@ -318,10 +357,14 @@ bool row_kernel_ok(const RQArgs& a)
     return true;
 }
 
+// rows in flight per wave (two measured no faster than one: the extra
+// registers cost a wave per SIMD)
+constexpr int kRowPF = 1;
+
 template <int DT, bool SMOOTH, bool YOUT, int TW>
 static hipError_t launch_row_t(const RQArgs& a, hipStream_t st)
 {
-    auto kern = rq_row_kernel<DT, SMOOTH, YOUT, TW>;
+    auto kern = rq_row_kernel<DT, SMOOTH, YOUT, TW, kRowPF>;
     static int per_cu = 0, n_cu = 0;
     if (per_cu == 0) {
         int dev = 0;

@@ -1,0 +1,98 @@
+"""CPU model of the row-streaming kernel's code rounding, checked against the
+oracle's quantizer on every 16-bit value of a row.
+
+The kernel never divides per element.  With rinv = 1/s it forms two fp32
+products that bracket the IEEE quotient, y * rinv * (1 + 2^-21) and
+y * rinv * (1 - 2^-21), each rounded to an integer by one fused
+multiply-add with 1.5 * 2^23.  Where the two integers agree they are
+round-half-even(fl(y / s)).  Where they differ the quotient is within
+2^-20 of a half-integer h = k + 1/2, which for 16-bit y and absmax a only
+happens at an exact tie 7 y = h a; every element of the row that ties at h
+has the same |y|, so one IEEE division per h (seven per row, one per lane)
+gives the outcome for all of them.  The model below takes exactly these
+steps in fp32 (numpy's float32 arithmetic is IEEE round-to-nearest-even;
+the fused multiply-add is exact because the fp64 product of a 16-bit value
+and an fp32 value is exact) and must reproduce the oracle's codes for
+every y with |y| <= a, for absmax values spread over the whole range:
+subnormal, clamped scale (a / 7 below 2^-126), around 2^64 (where the tie
+values are formed at a 2^-64 scale) and the largest finite value."""
+import numpy as np
+import pytest
+
+import oracle
+
+F32 = np.float32
+
+
+def _mask_bits(a, s, clamped, dtype):
+    """Bit k (k = 0..6): a tie at h = k + 1/2 rounds away from zero."""
+    if clamped:
+        return 0x2A
+    b = 0
+    big = a > F32(2.0 ** 64)
+    ah = F32(a * F32(2.0 ** -64)) if big else a
+    for k in range(7):
+        h = F32(k + 0.5)
+        yh = F32(F32(h * ah) / F32(7.0))
+        if big:
+            yh = F32(yh * F32(2.0 ** 64))
+        qh = F32(yh / s)
+        if np.rint(qh) > h:
+            b |= 1 << k
+    return b
+
+
+def _bitrev32(v):
+    return int(f"{v & 0xFFFFFFFF:032b}"[::-1], 2)
+
+
+def model_codes(y, a, dtype):
+    """Codes of the values y (fp32 array) in a row whose absmax is a."""
+    a = F32(a)
+    s = F32(a / F32(7.0))
+    if s < F32(2.0 ** -126):
+        s = F32(2.0 ** -126)
+    rinv = F32(F32(1.0) / s)
+    rh = F32(rinv * F32(1.0 + 2.0 ** -21))
+    rl = F32(rinv * F32(1.0 - 2.0 ** -21))
+    u = np.rint(y.astype(np.float64) * np.float64(rh)).astype(np.int64)
+    d = np.rint(y.astype(np.float64) * np.float64(rl)).astype(np.int64)
+    b = _mask_bits(a, s, s == F32(2.0 ** -126), dtype)
+    mask = (b | (_bitrev32(b) << 1)) & 0xFFFFFFFF
+    up = (mask >> (d & 31)) & 1
+    code = d + up * (u - d)
+    return code.astype(np.int8), int((u != d).sum()), int(((u != d) & (up == 1)).sum())
+
+
+def _patterns(dtype, rng):
+    """Positive finite absmax bit patterns covering the range."""
+    if dtype == "bf16":
+        fixed = [0x0001, 0x0002, 0x007F, 0x0080, 0x0081, 0x00E0, 0x0380, 0x03B0, 0x03C0, 0x03FF,
+                 0x0400, 0x3F80, 0x40E0, 0x4100, 0x5F7F, 0x5F80, 0x5F81, 0x5FD0, 0x7F7F, 0x7F00]
+        top = 0x7F7F
+    else:
+        fixed = [0x0001, 0x0002, 0x0007, 0x000E, 0x03FF, 0x0400, 0x0401, 0x3C00, 0x4700, 0x4B00,
+                 0x4B80, 0x7BFF, 0x7800]
+        top = 0x7BFF
+    extra = rng.integers(1, top + 1, size=60).tolist()
+    return sorted(set(fixed + extra))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_bracket_and_tie_table_reproduce_the_quantizer(dtype):
+    rng = np.random.default_rng(17)
+    ties = ups = 0
+    for ap in _patterns(dtype, rng):
+        pos = np.arange(0, ap + 1, dtype=np.uint32)
+        bits = np.concatenate([pos, pos | 0x8000]).astype(np.uint16)
+        vals = oracle.decode(dtype, bits)
+        a = float(oracle.decode(dtype, np.array([ap], np.uint16))[0])
+        ref_codes, ref_s = oracle.quantize(bits[None, :], dtype)
+        got, nt, nu = model_codes(vals.astype(np.float32), a, dtype)
+        bad = np.flatnonzero(got != ref_codes[0])
+        assert bad.size == 0, (hex(ap), [(hex(int(bits[i])), int(got[i]), int(ref_codes[0][i])) for i in bad[:5]])
+        ties += nt
+        ups += nu
+    # both outcomes of a tie occur (a rule that always rounds half to even,
+    # or always away from zero, would fail above)
+    assert ties > 0 and 0 < ups < ties, (ties, ups)
