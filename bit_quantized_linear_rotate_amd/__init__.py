@@ -12,6 +12,8 @@ from ._binding import (  # noqa: F401
     w4a4_gemm_workspace_size,
     w4a4_int32_guard,
     w4a4_linear,
+    w4a4_linear_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     w4a4_linear_workspace_size,
     w4a4_lowrank_down,
     w4a4_rotate_quant_plan,

@@ -38,6 +38,9 @@ _SIGNATURES = {
                      ctypes.c_int, _i32, _vp, _vp, _vp, _i32, _vp, ctypes.c_int, _vp, _sz, _vp],
                     ctypes.c_int),
     "w4a4_linear_workspace_size": ([_i64, _i64, _i64, _i32], _sz),
+    "w4a4_linear_noalloc": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _i64,
+                             _vp, ctypes.c_int, _i32, _vp, _vp, _vp, _i32, _vp, ctypes.c_int, _vp],
+                            ctypes.c_int),
     "w4a4_int32_guard": ([_i64, ctypes.POINTER(_i64)], ctypes.c_int),
     "w4a4_rotate_quant_plan": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp,
                                 ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
@@ -296,14 +299,10 @@ def w4a4_gemm_from_codes(codes: torch.Tensor, scales: torch.Tensor, w_packed: to
     return (out, acc) if return_acc else out
 
 
-def w4a4_linear(x: torch.Tensor, rot: Optional[torch.Tensor], g: int, w_packed: torch.Tensor,
-                w_scale: torch.Tensor, w_scale_group: int = 0,
-                bias: Optional[torch.Tensor] = None, smooth: Optional[torch.Tensor] = None,
-                proj_down: Optional[torch.Tensor] = None, proj_up: Optional[torch.Tensor] = None,
-                out_dtype: Optional[torch.dtype] = None,
-                workspace: Optional[torch.Tensor] = None,
-                out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """The whole W4A4 linear: y = layer(x) of shape (..., N)."""
+def _linear_checks(x, rot, g, w_packed, w_scale, w_scale_group, bias, smooth, proj_down, proj_up,
+                   out_dtype, out):
+    """Validation shared by w4a4_linear and w4a4_linear_noalloc; returns
+    (lead shape, x as (M, K), rot, g, N, rank, out dtype)."""
     lead = _need(x, "x", contiguous=False).shape[:-1]
     x2 = _as_2d(x)
     M, K = x2.shape
@@ -333,6 +332,20 @@ def w4a4_linear(x: torch.Tensor, rot: Optional[torch.Tensor], g: int, w_packed: 
         raise ValueError(f"out_dtype {out_dtype} is not float32/float16/bfloat16")
     if out is not None:
         _need(out, "out", (M, N), (out_dtype,))
+    return lead, x2, rot, g, N, rank, out_dtype
+
+
+def w4a4_linear(x: torch.Tensor, rot: Optional[torch.Tensor], g: int, w_packed: torch.Tensor,
+                w_scale: torch.Tensor, w_scale_group: int = 0,
+                bias: Optional[torch.Tensor] = None, smooth: Optional[torch.Tensor] = None,
+                proj_down: Optional[torch.Tensor] = None, proj_up: Optional[torch.Tensor] = None,
+                out_dtype: Optional[torch.dtype] = None,
+                workspace: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The whole W4A4 linear: y = layer(x) of shape (..., N)."""
+    lead, x2, rot, g, N, rank, out_dtype = _linear_checks(
+        x, rot, g, w_packed, w_scale, w_scale_group, bias, smooth, proj_down, proj_up, out_dtype, out)
+    M, K = x2.shape
     need = w4a4_linear_workspace_size(M, K, N, rank)
     if workspace is not None:
         _need(workspace, "workspace", dtypes=(torch.uint8,))
@@ -351,4 +364,33 @@ def w4a4_linear(x: torch.Tensor, rot: Optional[torch.Tensor], g: int, w_packed: 
         _ptr(proj_down), _ptr(proj_up), rank, _ptr(out), _DT[out.dtype], _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(dev))
     _check(rc, "w4a4_linear")
+    return out.view(*lead, N)
+
+
+# size of the library's per-GPU scratch (W4A4_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def w4a4_linear_noalloc(x: torch.Tensor, rot: Optional[torch.Tensor], g: int,
+                        w_packed: torch.Tensor, w_scale: torch.Tensor, out: torch.Tensor,
+                        w_scale_group: int = 0, bias: Optional[torch.Tensor] = None,
+                        smooth: Optional[torch.Tensor] = None,
+                        proj_down: Optional[torch.Tensor] = None,
+                        proj_up: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """w4a4_linear without a workspace and without any allocation: the
+    library's per-GPU scratch holds the intermediates (calls that overlap on
+    one GPU race).  `out` (M, N) is required; layers needing more than
+    NOALLOC_SCRATCH_BYTES of scratch are refused (ValueError)."""
+    if not isinstance(out, torch.Tensor):
+        raise ValueError("out must be a torch.Tensor (the no-allocation call allocates nothing)")
+    lead, x2, rot, g, N, rank, out_dtype = _linear_checks(
+        x, rot, g, w_packed, w_scale, w_scale_group, bias, smooth, proj_down, proj_up, None, out)
+    M, K = x2.shape
+    _same_device(x2, rot=rot, w_packed=w_packed, w_scale=w_scale, bias=bias, smooth=smooth,
+                 proj_down=proj_down, proj_up=proj_up, out=out)
+    rc = lib().w4a4_linear_noalloc(
+        _ptr(x2), _dt(x2), M, K, x2.stride(0), x2.stride(1), _ptr(rot), g, _ptr(smooth),
+        _ptr(w_packed), N, _ptr(w_scale), _dt(w_scale), w_scale_group, _ptr(bias),
+        _ptr(proj_down), _ptr(proj_up), rank, _ptr(out), _DT[out.dtype], _stream(x2.device))
+    _check(rc, "w4a4_linear_noalloc")
     return out.view(*lead, N)

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/w4a4.h"
 #include "kernels.hpp"
 
@@ -103,6 +105,37 @@ int gemm_validate(const int8_t* codes, const float* scales, int64_t M, int64_t K
         if (!scales || !wp || !sw || !out || (K > 0 && !codes))
             return fail(W4A4_INVALID, "a required pointer is NULL");
     }
+    return W4A4_OK;
+}
+
+// Scratch of w4a4_linear_noalloc: the codes, scales, low-rank activations
+// and (for very long K) int64 partial sums of one call.  Each GPU the library
+// runs on holds its own copy, allocated with the code object and kept until
+// the process ends; host code reaches it only through the device address
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[W4A4_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_dev[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch, looked up once per device
+// (with that device current) and kept.
+int scratch_address(void** ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(W4A4_UNSUPPORTED, "device index %d", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(W4A4_HIP_ERROR, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_dev[dev] = p;
+    }
+    *ptr = g_scratch_dev[dev];
     return W4A4_OK;
 }
 
@@ -294,6 +327,32 @@ int w4a4_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride
     e = launch_gemm(ga, st);
     if (e != hipSuccess) return hip_fail(e, "gemm launch");
     return W4A4_OK;
+}
+
+int w4a4_linear_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                        int64_t stride_k, const float* rot, int32_t g, const void* smooth,
+                        const uint8_t* w_packed, int64_t N, const void* w_scale, int w_scale_dtype,
+                        int32_t w_scale_group, const void* bias, const void* proj_down,
+                        const void* proj_up, int32_t rank, void* out, int out_dtype, void* stream)
+{
+    if (M < 0 || K < 0 || N < 0) return fail(W4A4_INVALID, "negative size");
+    if (proj_down && (rank < 1 || rank > 64)) return fail(W4A4_INVALID, "rank=%d outside [1, 64]", rank);
+    const size_t need = w4a4_linear_workspace_size(M, K, N, proj_down ? rank : 0);
+    if (need > (size_t)W4A4_NOALLOC_SCRATCH_BYTES)
+        return fail(W4A4_INVALID,
+                    "this layer needs %zu bytes of scratch, more than the %zu bytes w4a4_linear_noalloc "
+                    "holds; call w4a4_linear with a workspace",
+                    need, (size_t)W4A4_NOALLOC_SCRATCH_BYTES);
+    if (M == 0 || N == 0)
+        return w4a4_linear(x, x_dtype, M, K, stride_m, stride_k, rot, g, smooth, w_packed, N, w_scale,
+                           w_scale_dtype, w_scale_group, bias, proj_down, proj_up, rank, out, out_dtype,
+                           nullptr, 0, stream);
+    void* ws = nullptr;
+    const int rc = scratch_address(&ws);
+    if (rc) return rc;
+    return w4a4_linear(x, x_dtype, M, K, stride_m, stride_k, rot, g, smooth, w_packed, N, w_scale,
+                       w_scale_dtype, w_scale_group, bias, proj_down, proj_up, rank, out, out_dtype, ws,
+                       (size_t)W4A4_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

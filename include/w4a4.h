@@ -140,6 +140,27 @@ int w4a4_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride
 size_t w4a4_linear_workspace_size(int64_t M, int64_t K, int64_t N, int32_t rank);
 
 /*
+ * w4a4_linear for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, and the same kernels, which work
+ * in a scratch array the library holds per GPU (W4A4_NOALLOC_SCRATCH_BYTES,
+ * allocated with the code object and kept until the process ends).  The
+ * call allocates nothing.  A layer whose w4a4_linear_workspace_size exceeds
+ * that size is refused with W4A4_INVALID before anything is enqueued.
+ * Every call on a GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (other streams, other threads) race and must be serialised by the
+ * caller; calls in order on one stream are safe.  The caller still passes x
+ * and out.  The first call on a device looks up that device's scratch
+ * address (no allocation).
+ */
+#define W4A4_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int w4a4_linear_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                        int64_t stride_k, const float* rot, int32_t g, const void* smooth,
+                        const uint8_t* w_packed, int64_t N, const void* w_scale, int w_scale_dtype,
+                        int32_t w_scale_group, const void* bias, const void* proj_down,
+                        const void* proj_up, int32_t rank, void* out, int out_dtype, void* stream);
+
+/*
  * INT32 overflow guard (W4A4 page, section "W4A4 correctness and performance
  * scope").  Returns 1 if a K-long accumulation could overflow the GEMM's INT32
  * registers (which hold 16 * c * w, |c| <= 7, |w| <= 8), else 0; *k_chunk (if
