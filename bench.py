@@ -28,7 +28,7 @@ The line also carries the other four workloads (wide-K transposed-view fp16,
 decode-like M=32, tiny fp32, large-K with smoothing, per-64-group scales and a
 rank-32 term), each as a step and per kernel.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload prefill]
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload prefill]
                        [--no-cpu] [--no-extra] [--copy-calibration]
 
 `roofline.traffic` is the HBM traffic of one launch of the kernel as measured
@@ -417,8 +417,8 @@ def _rounded(d):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
