@@ -453,10 +453,20 @@ constexpr int R3_ASTAGE = BBM * R3_BK;       // 32 KB of codes
 constexpr int R3_WSTAGE = BBN * R3_BK / 2;   // 16 KB of packed weights
 constexpr int R3_SLOT = R3_ASTAGE + R3_WSTAGE;
 constexpr int R3_WAVES = 8;
-constexpr int R3_ALOADS = R3_ASTAGE / 1024 / R3_WAVES;  // 1 KB per load: 4 per wave
-constexpr int R3_WLOADS = R3_WSTAGE / 1024 / R3_WAVES;  // 2 per wave
-constexpr int R3_EPR = 68;  // epilogue strip row in words (64 + 4 pad)
-static_assert(R3_WAVES * 16 * R3_EPR * 4 + 2 * BBN * 4 + BBM * 4 <= R3_SLOT, "epilogue must fit in one slot");
+constexpr int R3_LOADERS = 4;                             // waves 0-3 issue every operand load
+constexpr int R3_ALOADS = R3_ASTAGE / 1024 / R3_LOADERS;  // 1 KB per load: 8 per loader wave
+constexpr int R3_WLOADS = R3_WSTAGE / 1024 / R3_LOADERS;  // 4 per loader wave
+// epilogue strip (16 output rows x 64 columns of one wave) row stride in
+// bytes: 64 values + 16 bytes, so that the four 16-lane groups of a 2- or
+// 4-byte strip write hit distinct banks and 16-byte reads stay aligned
+template <int ODT> constexpr int r3_srb() { return ODT == F32 ? 64 * 4 + 16 : 64 * 2 + 16; }
+// strips per wave in flight: two (double-buffered) for 16-bit outputs
+template <int ODT> constexpr int r3_nbuf() { return ODT == F32 ? 1 : 2; }
+template <int ODT> constexpr int r3_epi_bytes()
+{
+    return r3_nbuf<ODT>() * R3_WAVES * 16 * r3_srb<ODT>() + 2 * BBN * 4 + BBM * 4;
+}
+static_assert(r3_epi_bytes<F32>() <= R3_SLOT && r3_epi_bytes<BF16>() <= R3_SLOT, "epilogue must fit in one slot");
 
 __device__ __forceinline__ v4i r3_half(v4u p, int t)
 {
@@ -464,6 +474,27 @@ __device__ __forceinline__ v4i r3_half(v4u p, int t)
     unpack16(t ? p.z : p.x, a, b);
     unpack16(t ? p.w : p.y, c, d);
     return (v4i){(int)a, (int)b, (int)c, (int)d};
+}
+
+// Element i of an n-element fp32/fp16/bf16 vector, with no control flow on
+// the dtype, so that several such loads issue before one wait: the dword
+// that holds it (r3_scalar_word), then its value (r3_scalar_value).  A
+// 16-bit element comes from the aligned dword that holds it; the range check
+// covers the vector rounded up to whole dwords (an allocation always spans
+// the dword that holds its last 16-bit element).
+__device__ __forceinline__ uint32_t r3_scalar_word(const void* base, int dt, int64_t n, int64_t i)
+{
+    const bool w32 = dt == F32;
+    const uint64_t bytes = w32 ? (uint64_t)n * 4 : (((uint64_t)n * 2 + 3) & ~(uint64_t)3);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, bytes);
+    const int off = w32 ? (int)(i * 4) : (int)((i * 2) & ~(int64_t)3);
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ float r3_scalar_value(uint32_t w, int dt, int64_t i)
+{
+    const uint32_t h = (i & 1) ? (w >> 16) : (w & 0xffffu);
+    const float hf = dt == BF16 ? __uint_as_float(h << 16) : f16_to_f32((uint16_t)h);
+    return dt == F32 ? __uint_as_float(w) : hf;
 }
 
 // chunk permutation of code row r in LDS (depends on bits 1 and 2 of r)
@@ -503,7 +534,7 @@ template <int ODT>
 __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int tiles_m, int tiles_n)
 {
     __shared__ __align__(16) int8_t smem[3 * R3_SLOT];
-    static_assert(R3_ALOADS + R3_WLOADS == 6, "vmcnt immediates below assume 6 loads per stage");
+    static_assert(R3_ALOADS + R3_WLOADS == 12, "vmcnt immediates below assume 12 loads per stage");
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -516,28 +547,34 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
     int t = blockIdx.x;
     const int G = gridDim.x;
 
-    // codes: wave w fills tile rows w*32 .. w*32+31, eight rows per load;
-    // lane l writes chunk (l & 7) of row (l >> 3), i.e. logical chunk
+    // Waves 0-3 (one per SIMD) issue every operand load and are the only
+    // waves that wait on vmcnt; waves 4-7 issue the output stores, so a
+    // tile's stores never hold up the next tile's loads.
+    const bool loader = wave < R3_LOADERS;
+    const int lw = wave & (R3_LOADERS - 1);
+    // codes: loader lw fills tile rows lw*64 .. lw*64+63, eight rows per
+    // load; lane l writes chunk (l & 7) of row (l >> 3), i.e. logical chunk
     // (l & 7) ^ r3_swz(row) (the row's low three bits are l >> 3).
     const int a_vo = (int)((lane >> 3) * K + (((lane & 7) ^ r3_swz(lane >> 3)) * 16));
     const int a_row8 = (int)(8 * K);
-    // weights: wave w fills tile columns w*32 .. w*32+31, sixteen per load;
-    // lane l writes chunk (l & 3) of column (l >> 2).
-    const int w_vo = (int)((wave * 32 + (lane >> 2)) * (K >> 1) + (((lane & 3) ^ ((lane >> 3) & 3)) * 16));
+    // weights: loader lw fills tile columns lw*64 .. lw*64+63, sixteen per
+    // load; lane l writes chunk (l & 3) of column (l >> 2).
+    const int w_vo = (int)((lw * 64 + (lane >> 2)) * (K >> 1) + (((lane & 3) ^ ((lane >> 3) & 3)) * 16));
     const int w_col16 = (int)(16 * (K >> 1));
     auto issue = [&](int slot, const __amdgpu_buffer_rsrc_t& ra, const __amdgpu_buffer_rsrc_t& rw, int st) {
+        if (!loader) return;
         int8_t* as = smem + slot * R3_SLOT;
         int8_t* ws = as + R3_ASTAGE;
         const int ka = st * R3_BK, kw = st * (R3_BK / 2);
 #pragma unroll
         for (int i = 0; i < R3_ALOADS; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (__attribute__((address_space(3))) void*)(as + (wave * 32 + i * 8) * R3_BK), 16,
-                a_vo + (wave * 4 + i) * a_row8 + ka, 0, 0, 0);
+                ra, (__attribute__((address_space(3))) void*)(as + (lw * 64 + i * 8) * R3_BK), 16,
+                a_vo + (lw * 8 + i) * a_row8 + ka, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < R3_WLOADS; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw, (__attribute__((address_space(3))) void*)(ws + (wave * 32 + i * 16) * (R3_BK / 2)), 16,
+                rw, (__attribute__((address_space(3))) void*)(ws + (lw * 64 + i * 16) * (R3_BK / 2)), 16,
                 w_vo + i * w_col16 + kw, 0, 0, 0);
     };
 
@@ -585,7 +622,7 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = (v4i){0, 0, 0, 0};
         for (int s = 0; s < nsteps; ++s) {
-            __builtin_amdgcn_s_waitcnt(0x0f76);  // vmcnt(6): stage s has landed
+            if (loader) __builtin_amdgcn_s_waitcnt(0x0f7c);  // vmcnt(12): stage s has landed
             __builtin_amdgcn_s_barrier();
             const bool same = s + 2 < nsteps;
             issue(nxt2, same ? cur_t.ra : nxt_t.ra, same ? cur_t.rw : nxt_t.rw,
@@ -598,112 +635,147 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
 
         // ---- epilogue in the slot the last step used (every wave has left it
         // after the barrier below); the next tile's first two stages are
-        // already in flight into the other two.  Scales and bias are widened
-        // in LDS; each wave passes its accumulators through LDS as 16 x 64
-        // strips so that every store instruction writes whole output rows.
+        // already in flight into the other two.  The storer waves stage the
+        // column scales, bias and row scales in LDS.  Every wave then applies
+        // the epilogue to its own accumulators in registers and writes the
+        // rounded outputs as 16 x 64 strips; each storer wave writes two
+        // strips (its own and loader wave w-4's) to global memory with
+        // 16-byte row-contiguous stores.
         int8_t* eslot = smem + nxt2 * R3_SLOT;  // == slot of the step just computed
         __builtin_amdgcn_s_barrier();
-        float* scol = (float*)(eslot + R3_WAVES * 16 * R3_EPR * 4);
+        constexpr int SRB = r3_srb<ODT>(), NBUF = r3_nbuf<ODT>();
+        constexpr int ESZ = ODT == F32 ? 4 : 2;
+        int8_t* strips = eslot;
+        float* scol = (float*)(eslot + NBUF * R3_WAVES * 16 * SRB);
         float* bcol = scol + BBN;
         float* srow = bcol + BBN;
         const int64_t m0 = cur_t.m0, n0 = cur_t.n0;
-        {
+        const bool has_bias = a.bias != nullptr;
+        if (!loader) {
             // one round trip per tile for the column scales, the bias and the
-            // row scales
-            const int c = tid & (BBN - 1);
+            // row scales (storer waves only: their vmcnt holds no operand
+            // load); three branch-free loads, then one wait
+            const int c = tid - R3_LOADERS * 64;
             const int64_t col = n0 + c, row = m0 + c;
             const int64_t cc = col < N ? col : N - 1;
-            if (tid < BBN) {
-                scol[c] = load_any_f32(a.sw_dtype, a.sw, cc);
-                srow[c] = a.sa[row < M ? row : M - 1];
-            } else {
-                bcol[c] = a.bias ? load_any_f32(a.bias_dtype, a.bias, cc) : 0.0f;
-            }
+            const int bdt = has_bias ? a.bias_dtype : a.sw_dtype;
+            const uint32_t ws = r3_scalar_word(a.sw, a.sw_dtype, N, cc);
+            const uint32_t wb = r3_scalar_word(has_bias ? a.bias : a.sw, bdt, N, cc);
+            const uint32_t wr = r3_scalar_word(a.sa, F32, M, row < M ? row : M - 1);
+            scol[c] = r3_scalar_value(ws, a.sw_dtype, cc);
+            bcol[c] = has_bias ? r3_scalar_value(wb, bdt, cc) : 0.0f;
+            srow[c] = __uint_as_float(wr);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS writes done
         __builtin_amdgcn_s_barrier();
-        int* strip = (int*)eslot + wave * 16 * R3_EPR;
-        // store mapping: each store instruction writes whole rows of the
-        // 16 x 64 strip (128 bytes for 16-bit outputs, 256 for fp32): VPR
-        // outputs per lane and store, LPR lanes per row, RPI rows per store
-        constexpr int VPR = ODT == F32 ? 4 : 8;
-        constexpr int LPR = 64 / VPR;
-        constexpr int RPI = 64 / LPR;
-        const int sr = lane / LPR;            // first strip row of this lane
-        const int cb = (lane % LPR) * VPR;    // column offset inside the 64
-        const int64_t col0 = n0 + wn * 64 + cb;
-        const bool has_bias = a.bias != nullptr;
+        float scl[4], bia[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            scl[nt] = scol[wn * 64 + nt * 16 + j];
+            bia[nt] = bcol[wn * 64 + nt * 16 + j];
+        }
         // a full tile with 16-byte aligned rows stores with no per-lane checks
         const bool full = m0 + BBM <= M && n0 + BBN <= N && (N % 8) == 0;
-        const float* scl = scol + wn * 64 + cb;
-        const float* bia = bcol + wn * 64 + cb;
+        // storer mapping: 16-byte chunk `ch` of strip row `rr`; VPC outputs
+        // per chunk, CPR chunks per strip row
+        constexpr int VPC = 16 / ESZ, CPR = 64 / VPC, CHUNKS = 16 * CPR, PER_LANE = CHUNKS / 64;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
+            int8_t* sbuf = strips + (mt % NBUF) * R3_WAVES * 16 * SRB;
+            // this wave's 16 x 64 outputs of row tile mt, rounded, into its strip
+            const float* sr = srow + wm * 128 + mt * 16 + 4 * q;
+            const float sa[4] = {sr[0], sr[1], sr[2], sr[3]};
+            int8_t* mine = sbuf + wave * 16 * SRB;
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) strip[(4 * q + r) * R3_EPR + nt * 16 + j] = acc[mt][nt][r] >> 4;
-            __builtin_amdgcn_s_waitcnt(0xc07f);
-            __builtin_amdgcn_wave_barrier();
-            int iv[16 / RPI][VPR];
-#pragma unroll
-            for (int i = 0; i < 16 / RPI; ++i)
-#pragma unroll
-                for (int c4 = 0; c4 < VPR / 4; ++c4) {
-                    const int4 v = *(const int4*)(strip + (sr + i * RPI) * R3_EPR + cb + 4 * c4);
-                    iv[i][4 * c4] = v.x; iv[i][4 * c4 + 1] = v.y; iv[i][4 * c4 + 2] = v.z; iv[i][4 * c4 + 3] = v.w;
+                for (int r = 0; r < 4; ++r) {
+                    const float tv = mul_rn(mul_rn((float)(acc[mt][nt][r] >> 4), sa[r]), scl[nt]);
+                    const float o = has_bias ? add_rn(tv, bia[nt]) : tv;
+                    int8_t* dst = mine + (4 * q + r) * SRB + (nt * 16 + j) * ESZ;
+                    if constexpr (ODT == F32)
+                        *(float*)dst = o;
+                    else
+                        *(uint16_t*)dst = f32_to_h<ODT>(o);
                 }
             __builtin_amdgcn_s_waitcnt(0xc07f);
-            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_s_barrier();
+            if (!loader) {
+                // every chunk of both strips in one asm block that also waits
+                // for them: the compiler would otherwise put a vmcnt(0) in
+                // front of the first LDS read (it cannot tell these reads from
+                // the loader waves' LDS-DMA targets), which would stall on this
+                // wave's own output stores of the previous row tile
+                using lds_ptr = const __attribute__((address_space(3))) int8_t*;
+                v4u vv[2][PER_LANE];
+                lds_ptr la[2][PER_LANE];
 #pragma unroll
-            for (int i = 0; i < 16 / RPI; ++i) {
-                const int tr = wm * 128 + mt * 16 + sr + i * RPI;  // row inside the tile
-                const int64_t row = m0 + tr;
-                const float sa = srow[tr];
-                float o[VPR];
+                for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int c = 0; c < VPR; ++c) {
-                    const float tv = mul_rn(mul_rn((float)iv[i][c], sa), scl[c]);
-                    const float tb = add_rn(tv, bia[c]);
-                    o[c] = has_bias ? tb : tv;
-                }
-                if constexpr (ODT == F32) {
-                    float* dst = (float*)a.out + row * N + col0;
-                    if (full) {
-                        *(float4*)dst = make_float4(o[0], o[1], o[2], o[3]);
-                    } else if (row < M) {
-#pragma unroll
-                        for (int c = 0; c < VPR; ++c)
-                            if (col0 + c < N) dst[c] = o[c];
+                    for (int i = 0; i < PER_LANE; ++i) {
+                        const int sw = h ? wave : wave - R3_LOADERS;
+                        const int c = lane + 64 * i;
+                        la[h][i] = (lds_ptr)(sbuf + sw * 16 * SRB + (c / CPR) * SRB + (c % CPR) * 16);
                     }
+                if constexpr (PER_LANE == 2) {
+                    asm volatile(
+                        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
+                        "ds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+                        : "=v"(vv[0][0]), "=v"(vv[0][1]), "=v"(vv[1][0]), "=v"(vv[1][1])
+                        : "v"(la[0][0]), "v"(la[0][1]), "v"(la[1][0]), "v"(la[1][1])
+                        : "memory");
                 } else {
-                    uint16_t* dst = (uint16_t*)a.out + row * N + col0;
-                    uint32_t pk[4];
 #pragma unroll
-                    for (int c2 = 0; c2 < 4; ++c2)
-                        pk[c2] = (uint32_t)f32_to_h<ODT>(o[2 * c2]) |
-                                 ((uint32_t)f32_to_h<ODT>(o[2 * c2 + 1]) << 16);
-                    if (full) {
-                        *(uint4*)dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-                    } else if (row < M) {
-                        if (col0 + VPR <= N && (N % 8) == 0) {
-                            *(uint4*)dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-                        } else {
+                    for (int h = 0; h < 2; ++h)
+                        asm volatile(
+                            "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
+                            "ds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+                            : "=v"(vv[h][0]), "=v"(vv[h][1]), "=v"(vv[h][2]), "=v"(vv[h][3])
+                            : "v"(la[h][0]), "v"(la[h][1]), "v"(la[h][2]), "v"(la[h][3])
+                            : "memory");
+                }
 #pragma unroll
-                            for (int c = 0; c < VPR; ++c)
-                                if (col0 + c < N) dst[c] = (uint16_t)(pk[c >> 1] >> (16 * (c & 1)));
+                for (int h = 0; h < 2; ++h) {
+                    const int sw = h ? wave : wave - R3_LOADERS;   // strip's owner wave
+                    const int swm = sw & 1, swn = sw >> 1;
+#pragma unroll
+                    for (int i = 0; i < PER_LANE; ++i) {
+                        const int c = lane + 64 * i;
+                        const int rr = c / CPR, ch = c % CPR;
+                        const uint4 v = make_uint4(vv[h][i][0], vv[h][i][1], vv[h][i][2], vv[h][i][3]);
+                        const int64_t row = m0 + swm * 128 + mt * 16 + rr;
+                        const int64_t col0 = n0 + swn * 64 + ch * VPC;
+                        int8_t* dst = (int8_t*)a.out + (row * N + col0) * ESZ;
+                        if (full) {
+                            *(uint4*)dst = v;
+                        } else if (row < M) {
+                            if (col0 + VPC <= N && (N % 8) == 0) {
+                                *(uint4*)dst = v;
+                            } else {
+                                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                                for (int e = 0; e < VPC; ++e) {
+                                    if (col0 + e >= N) break;
+                                    if constexpr (ODT == F32)
+                                        ((uint32_t*)dst)[e] = w4[e];
+                                    else
+                                        ((uint16_t*)dst)[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+                                }
+                            }
                         }
                     }
                 }
+            }
+            if constexpr (NBUF == 1) {
+                // single strip buffer: every storer has read it before it is reused
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                __builtin_amdgcn_s_barrier();
             }
         }
         t += G;
         if (t >= ntiles) break;
         cur_t = nxt_t;
         nxt_t = r3_tile(a, t + G, ntiles, tiles_n);
-        // the output stores are counted by vmcnt ahead of nothing the next
-        // step needs, but the first wait below counts only loads: drain them
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     }
     __builtin_amdgcn_s_waitcnt(0x0070);
 }
