@@ -432,10 +432,17 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 //   * Every byte offset, row and k included, travels in the per-lane voffset,
 //     so the buffer range check covers it: rows past M or N and k past K read
 //     as zero, and a missing next tile is a zero-sized buffer.
-//   * Every step waits only for its own stage (vmcnt leaves the next stage's
-//     loads in flight), meets the other waves at a bare s_barrier
+//   * Waves 0-3 issue all operand loads (twelve 1 KB loads per stage each).
+//     Every step they wait only for its own stage (vmcnt leaves the next
+//     stage's loads in flight), meet the other waves at a bare s_barrier
 //     (__syncthreads would also wait for the loads still in flight) and then
-//     puts stage s+2 in flight before computing stage s.
+//     put stage s+2 in flight before computing stage s.
+//   * Epilogue: each wave rounds its own outputs in registers and stores
+//     them through a per-wave LDS strip as 16-byte row-contiguous stores.
+//     vmcnt retires in issue order on gfx9, so a loader's output stores,
+//     issued after the next tile's first two stages, only delay that tile's
+//     first two waits, which count them (a partial tile, whose store count
+//     varies, drains them and issues dropped stand-ins instead).
 //   * Two waves per SIMD keep the matrix core busy while the other waits on
 //     LDS or the barrier; with at most 256 registers per lane the compiler
 //     keeps the accumulators in VGPRs, where every MFMA updates its
@@ -460,12 +467,16 @@ constexpr int R3_WLOADS = R3_WSTAGE / 1024 / R3_LOADERS;  // 4 per loader wave
 // bytes: 64 values + 16 bytes, so that the four 16-lane groups of a 2- or
 // 4-byte strip write hit distinct banks and 16-byte reads stay aligned
 template <int ODT> constexpr int r3_srb() { return ODT == F32 ? 64 * 4 + 16 : 64 * 2 + 16; }
-// strips per wave in flight: two (double-buffered) for 16-bit outputs
-template <int ODT> constexpr int r3_nbuf() { return ODT == F32 ? 1 : 2; }
+// one strip per wave, then the column scales, the bias and the row scales
 template <int ODT> constexpr int r3_epi_bytes()
 {
-    return r3_nbuf<ODT>() * R3_WAVES * 16 * r3_srb<ODT>() + 2 * BBN * 4 + BBM * 4;
+    return R3_WAVES * 16 * r3_srb<ODT>() + 2 * BBN * 4 + BBM * 4;
 }
+// output store instructions per wave in a full tile's epilogue (8 row tiles,
+// 16 x 64 outputs each, 16 bytes per lane and store)
+template <int ODT> constexpr int r3_stores() { return 8 * (16 * 64 * (ODT == F32 ? 4 : 2)) / (64 * 16); }
+// s_waitcnt immediate for vmcnt(n), expcnt and lgkmcnt not waited on (gfx9)
+constexpr int r3_vmcnt(int n) { return ((n >> 4) << 14) | 0x0f70 | (n & 15); }
 static_assert(r3_epi_bytes<F32>() <= R3_SLOT && r3_epi_bytes<BF16>() <= R3_SLOT, "epilogue must fit in one slot");
 
 __device__ __forceinline__ v4i r3_half(v4u p, int t)
@@ -548,8 +559,9 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
     const int G = gridDim.x;
 
     // Waves 0-3 (one per SIMD) issue every operand load and are the only
-    // waves that wait on vmcnt; waves 4-7 issue the output stores, so a
-    // tile's stores never hold up the next tile's loads.
+    // waves that wait on vmcnt in the K loop; waves 4-7 load the epilogue's
+    // scales (their vmcnt never holds an operand load, so that wait does not
+    // drain the next tile's stages).
     const bool loader = wave < R3_LOADERS;
     const int lw = wave & (R3_LOADERS - 1);
     // codes: loader lw fills tile rows lw*64 .. lw*64+63, eight rows per
@@ -616,13 +628,44 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
     issue(0, cur_t.ra, cur_t.rw, 0);
     issue(1, cur_t.ra, cur_t.rw, 1);
     int cur = 0, nxt2 = 2;
+    // vmcnt retires in issue order (gfx9): after a full tile's epilogue the
+    // loader's own r3_stores() output stores sit behind the next tile's first
+    // two stages, so steps 0 and 1 may leave them in flight
+    static_assert(12 + r3_stores<ODT>() <= 63, "vmcnt range");
+    // exactly r3_stores() stores behind the first two stages, as after every
+    // full tile: dropped stores through a zero-sized buffer
+    auto pad_stores = [&]() {
+        if (!loader) return;
+        const __amdgpu_buffer_rsrc_t none = make_rsrc(a.out, 0);
+        // distinct offsets and the volatile bit: none of them may be merged
+        // or dropped by the compiler (the hardware drops them all)
+#pragma unroll
+        for (int i = 0; i < r3_stores<ODT>(); ++i)
+            __builtin_amdgcn_raw_buffer_store_b32(0u, none, 4 * i, 0, (int)0x80000000);
+    };
+    pad_stores();
     for (;;) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = (v4i){0, 0, 0, 0};
         for (int s = 0; s < nsteps; ++s) {
-            if (loader) __builtin_amdgcn_s_waitcnt(0x0f7c);  // vmcnt(12): stage s has landed
+            if (loader) {
+                // Stage s has landed once vmcnt drops to 12 (the next stage's
+                // loads may still be in flight); in steps 0 and 1 the previous
+                // tile's r3_stores() output stores (or as many dropped stand-ins),
+                // issued after this tile's first two stages, may be in flight
+                // too.  One asm block with its own scalar branch, so that the
+                // loop body keeps a single basic block around the MFMAs.
+                asm volatile(
+                    "s_cmp_lt_u32 %0, 2\n\t"
+                    "s_cbranch_scc0 1f\n\t"
+                    "s_waitcnt vmcnt(%1)\n\t"
+                    "s_branch 2f\n"
+                    "1:\n\t"
+                    "s_waitcnt vmcnt(12)\n"
+                    "2:" ::"s"(s), "n"(12 + r3_stores<ODT>()) : "memory", "scc");
+            }
             __builtin_amdgcn_s_barrier();
             const bool same = s + 2 < nsteps;
             issue(nxt2, same ? cur_t.ra : nxt_t.ra, same ? cur_t.rw : nxt_t.rw,
@@ -635,25 +678,26 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
 
         // ---- epilogue in the slot the last step used (every wave has left it
         // after the barrier below); the next tile's first two stages are
-        // already in flight into the other two.  The storer waves stage the
-        // column scales, bias and row scales in LDS.  Every wave then applies
-        // the epilogue to its own accumulators in registers and writes the
-        // rounded outputs as 16 x 64 strips; each storer wave writes two
-        // strips (its own and loader wave w-4's) to global memory with
-        // 16-byte row-contiguous stores.
+        // already in flight into the other two.  Waves 4-7 stage the column
+        // scales, bias and row scales in LDS.  Every wave then applies the
+        // epilogue to its own accumulators in registers, writes each row
+        // tile's rounded 16 x 64 outputs as a strip in LDS, reads it back
+        // row-contiguous and stores it with 16-byte stores.  A loader wave's
+        // stores stay in flight into the next tile's first two steps (the
+        // wait there counts them).
         int8_t* eslot = smem + nxt2 * R3_SLOT;  // == slot of the step just computed
         __builtin_amdgcn_s_barrier();
-        constexpr int SRB = r3_srb<ODT>(), NBUF = r3_nbuf<ODT>();
+        constexpr int SRB = r3_srb<ODT>();
         constexpr int ESZ = ODT == F32 ? 4 : 2;
         int8_t* strips = eslot;
-        float* scol = (float*)(eslot + NBUF * R3_WAVES * 16 * SRB);
+        float* scol = (float*)(eslot + R3_WAVES * 16 * SRB);
         float* bcol = scol + BBN;
         float* srow = bcol + BBN;
         const int64_t m0 = cur_t.m0, n0 = cur_t.n0;
         const bool has_bias = a.bias != nullptr;
         if (!loader) {
             // one round trip per tile for the column scales, the bias and the
-            // row scales (storer waves only: their vmcnt holds no operand
+            // row scales (waves 4-7 only: their vmcnt holds no operand
             // load); three branch-free loads, then one wait
             const int c = tid - R3_LOADERS * 64;
             const int64_t col = n0 + c, row = m0 + c;
@@ -676,16 +720,17 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
         }
         // a full tile with 16-byte aligned rows stores with no per-lane checks
         const bool full = m0 + BBM <= M && n0 + BBN <= N && (N % 8) == 0;
-        // storer mapping: 16-byte chunk `ch` of strip row `rr`; VPC outputs
-        // per chunk, CPR chunks per strip row
+        // each wave writes its own strip: 16-byte chunk `ch` of strip row `rr`;
+        // VPC outputs per chunk, CPR chunks per strip row
         constexpr int VPC = 16 / ESZ, CPR = 64 / VPC, CHUNKS = 16 * CPR, PER_LANE = CHUNKS / 64;
+        static_assert(PER_LANE == 2 || PER_LANE == 4, "strip read asm below");
+        int8_t* mine = strips + wave * 16 * SRB;
+        using lds_ptr = const __attribute__((address_space(3))) int8_t*;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-            int8_t* sbuf = strips + (mt % NBUF) * R3_WAVES * 16 * SRB;
             // this wave's 16 x 64 outputs of row tile mt, rounded, into its strip
             const float* sr = srow + wm * 128 + mt * 16 + 4 * q;
             const float sa[4] = {sr[0], sr[1], sr[2], sr[3]};
-            int8_t* mine = sbuf + wave * 16 * SRB;
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -698,79 +743,63 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
                     else
                         *(uint16_t*)dst = f32_to_h<ODT>(o);
                 }
+            // read the strip back row-contiguous: one asm block with its own
+            // wait, since the compiler would otherwise put a vmcnt(0) before
+            // the first read (it cannot tell the strip from the LDS-DMA
+            // targets), which would stall on this wave's stores and loads
+            v4u vv[PER_LANE];
+            lds_ptr la[PER_LANE];
+#pragma unroll
+            for (int i = 0; i < PER_LANE; ++i) {
+                const int c = lane + 64 * i;
+                la[i] = (lds_ptr)(mine + (c / CPR) * SRB + (c % CPR) * 16);
+            }
             __builtin_amdgcn_s_waitcnt(0xc07f);
-            __builtin_amdgcn_s_barrier();
-            if (!loader) {
-                // every chunk of both strips in one asm block that also waits
-                // for them: the compiler would otherwise put a vmcnt(0) in
-                // front of the first LDS read (it cannot tell these reads from
-                // the loader waves' LDS-DMA targets), which would stall on this
-                // wave's own output stores of the previous row tile
-                using lds_ptr = const __attribute__((address_space(3))) int8_t*;
-                v4u vv[2][PER_LANE];
-                lds_ptr la[2][PER_LANE];
+            __builtin_amdgcn_wave_barrier();
+            if constexpr (PER_LANE == 2) {
+                asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                             : "=v"(vv[0]), "=v"(vv[1]) : "v"(la[0]), "v"(la[1]) : "memory");
+            } else {
+                asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
+                             "ds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+                             : "=v"(vv[0]), "=v"(vv[1]), "=v"(vv[2]), "=v"(vv[3])
+                             : "v"(la[0]), "v"(la[1]), "v"(la[2]), "v"(la[3]) : "memory");
+            }
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+            for (int i = 0; i < PER_LANE; ++i) {
+                const int c = lane + 64 * i;
+                const int rr = c / CPR, ch = c % CPR;
+                const uint4 v = make_uint4(vv[i][0], vv[i][1], vv[i][2], vv[i][3]);
+                const int64_t row = m0 + wm * 128 + mt * 16 + rr;
+                const int64_t col0 = n0 + wn * 64 + ch * VPC;
+                int8_t* dst = (int8_t*)a.out + (row * N + col0) * ESZ;
+                if (full) {
+                    *(uint4*)dst = v;
+                } else if (row < M) {
+                    if (col0 + VPC <= N && (N % 8) == 0) {
+                        *(uint4*)dst = v;
+                    } else {
+                        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                    for (int i = 0; i < PER_LANE; ++i) {
-                        const int sw = h ? wave : wave - R3_LOADERS;
-                        const int c = lane + 64 * i;
-                        la[h][i] = (lds_ptr)(sbuf + sw * 16 * SRB + (c / CPR) * SRB + (c % CPR) * 16);
-                    }
-                if constexpr (PER_LANE == 2) {
-                    asm volatile(
-                        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
-                        "ds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
-                        : "=v"(vv[0][0]), "=v"(vv[0][1]), "=v"(vv[1][0]), "=v"(vv[1][1])
-                        : "v"(la[0][0]), "v"(la[0][1]), "v"(la[1][0]), "v"(la[1][1])
-                        : "memory");
-                } else {
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-                        asm volatile(
-                            "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
-                            "ds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
-                            : "=v"(vv[h][0]), "=v"(vv[h][1]), "=v"(vv[h][2]), "=v"(vv[h][3])
-                            : "v"(la[h][0]), "v"(la[h][1]), "v"(la[h][2]), "v"(la[h][3])
-                            : "memory");
-                }
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int sw = h ? wave : wave - R3_LOADERS;   // strip's owner wave
-                    const int swm = sw & 1, swn = sw >> 1;
-#pragma unroll
-                    for (int i = 0; i < PER_LANE; ++i) {
-                        const int c = lane + 64 * i;
-                        const int rr = c / CPR, ch = c % CPR;
-                        const uint4 v = make_uint4(vv[h][i][0], vv[h][i][1], vv[h][i][2], vv[h][i][3]);
-                        const int64_t row = m0 + swm * 128 + mt * 16 + rr;
-                        const int64_t col0 = n0 + swn * 64 + ch * VPC;
-                        int8_t* dst = (int8_t*)a.out + (row * N + col0) * ESZ;
-                        if (full) {
-                            *(uint4*)dst = v;
-                        } else if (row < M) {
-                            if (col0 + VPC <= N && (N % 8) == 0) {
-                                *(uint4*)dst = v;
-                            } else {
-                                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                                for (int e = 0; e < VPC; ++e) {
-                                    if (col0 + e >= N) break;
-                                    if constexpr (ODT == F32)
-                                        ((uint32_t*)dst)[e] = w4[e];
-                                    else
-                                        ((uint16_t*)dst)[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-                                }
-                            }
+                        for (int e = 0; e < VPC; ++e) {
+                            if (col0 + e >= N) break;
+                            if constexpr (ODT == F32)
+                                ((uint32_t*)dst)[e] = w4[e];
+                            else
+                                ((uint16_t*)dst)[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
                         }
                     }
                 }
             }
-            if constexpr (NBUF == 1) {
-                // single strip buffer: every storer has read it before it is reused
-                __builtin_amdgcn_s_waitcnt(0xc07f);
-                __builtin_amdgcn_s_barrier();
-            }
+            // one row tile at a time: only its accumulators and addresses live
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (!full && loader) {
+            // a partial tile's stores vary in number: drain them (and the
+            // next tile's first two stages), then stand in for them
+            __builtin_amdgcn_s_waitcnt(r3_vmcnt(0));
+            pad_stores();
         }
         t += G;
         if (t >= ntiles) break;
