@@ -34,6 +34,9 @@
 //     lane) decide, once, whether each k rounds away from zero; every element
 //     then takes its code from the two integers and that 7-bit table with
 //     three integer operations, with no branch and no per-element division.
+//     When 7 does not divide the integer significand of a, a tie needs
+//     7 | 2k + 1, i.e. k = 3 only: then the one multiplier that rounds that
+//     tie the quantizer's way gives every code with a single fma (most rows).
 //     Rows whose scale is Inf or NaN take the division for every element.
 //   * Each lane holds four codes of each of four column tiles; two
 //     v_permlane32_swap and two v_permlane16_swap transpose them so that every
@@ -288,10 +291,35 @@ __global__ __launch_bounds__(256, 2) void rq_row_kernel(
             }
         };
 
-        if (__builtin_expect(finite, 1)) {
+        // a's integer significand: when 7 does not divide it, the only tie a
+        // 16-bit element can make is y = a / 2 (k = 3)
+        const uint32_t sig = DT == BF16 ? ((a16 >> 7) & 0xffu ? (a16 & 0x7fu) | 0x80u : a16 & 0x7fu)
+                                        : ((a16 >> 10) & 0x1fu ? (a16 & 0x3ffu) | 0x400u : a16 & 0x3ffu);
+        const bool clamped = s == 0x1p-126f;
+        if (__builtin_expect(finite && !clamped && sig % 7u != 0u, 1)) {
+            // one rounding per element: of the two bracketing multipliers,
+            // the one that takes the k = 3 tie the quantizer's way gives every
+            // code (the two agree on every element that is not a tie)
             const float rinv = 1.0f / s;
             const float rh = rinv * (1.0f + 0x1p-21f), rl = rinv * (1.0f - 0x1p-21f);
-            const uint32_t tmask = tie_mask(a, s, s == 0x1p-126f, lane);
+            const float r1 = (tie_mask(a, s, false, lane) & 8u) ? rh : rl;
+#pragma unroll
+            for (int u = 0; u < TW; ++u) {
+                uint32_t P[CT];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    uint32_t c[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        c[i] = __float_as_uint(__builtin_fmaf(unpack_half<DT>(yp[u][ct][i >> 1], i & 1), r1, kMagic));
+                    P[ct] = pack_bytes(c[0], c[1], c[2], c[3]);
+                }
+                store_tile(u, P);
+            }
+        } else if (finite) {
+            const float rinv = 1.0f / s;
+            const float rh = rinv * (1.0f + 0x1p-21f), rl = rinv * (1.0f - 0x1p-21f);
+            const uint32_t tmask = tie_mask(a, s, clamped, lane);
 #pragma unroll
             for (int u = 0; u < TW; ++u) {
                 uint32_t P[CT];

@@ -15,7 +15,12 @@ the fused multiply-add is exact because the fp64 product of a 16-bit value
 and an fp32 value is exact) and must reproduce the oracle's codes for
 every y with |y| <= a, for absmax values spread over the whole range:
 subnormal, clamped scale (a / 7 below 2^-126), around 2^64 (where the tie
-values are formed at a 2^-64 scale) and the largest finite value."""
+values are formed at a 2^-64 scale) and the largest finite value.
+
+Rows whose absmax has an integer significand that 7 does not divide can only
+tie at y = a / 2 (7 y = (k + 1/2) a needs 7 | 2k + 1): there the kernel takes
+one fma per element with the multiplier that rounds that tie the quantizer's
+way, and that single rounding must reproduce the oracle as well."""
 import numpy as np
 import pytest
 
@@ -64,6 +69,27 @@ def model_codes(y, a, dtype):
     return code.astype(np.int8), int((u != d).sum()), int(((u != d) & (up == 1)).sum())
 
 
+def significand(ap, dtype):
+    """Integer significand of a positive finite 16-bit pattern."""
+    if dtype == "bf16":
+        return (ap & 0x7F) | (0x80 if (ap >> 7) & 0xFF else 0)
+    return (ap & 0x3FF) | (0x400 if (ap >> 10) & 0x1F else 0)
+
+
+def model_codes_single(y, a, dtype):
+    """Codes from one fma per element, for rows whose absmax significand 7
+    does not divide: the multiplier that takes the tie y = a / 2 (k = 3) the
+    quantizer's way (bit 3 of the tie table)."""
+    a = F32(a)
+    s = F32(a / F32(7.0))
+    assert s >= F32(2.0 ** -126)
+    rinv = F32(F32(1.0) / s)
+    rh = F32(rinv * F32(1.0 + 2.0 ** -21))
+    rl = F32(rinv * F32(1.0 - 2.0 ** -21))
+    r1 = rh if _mask_bits(a, s, False, dtype) & 8 else rl
+    return np.rint(y.astype(np.float64) * np.float64(r1)).astype(np.int64).astype(np.int8)
+
+
 def _patterns(dtype, rng):
     """Positive finite absmax bit patterns covering the range."""
     if dtype == "bf16":
@@ -81,7 +107,7 @@ def _patterns(dtype, rng):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_bracket_and_tie_table_reproduce_the_quantizer(dtype):
     rng = np.random.default_rng(17)
-    ties = ups = 0
+    ties = ups = single = table = 0
     for ap in _patterns(dtype, rng):
         pos = np.arange(0, ap + 1, dtype=np.uint32)
         bits = np.concatenate([pos, pos | 0x8000]).astype(np.uint16)
@@ -93,6 +119,16 @@ def test_bracket_and_tie_table_reproduce_the_quantizer(dtype):
         assert bad.size == 0, (hex(ap), [(hex(int(bits[i])), int(got[i]), int(ref_codes[0][i])) for i in bad[:5]])
         ties += nt
         ups += nu
+        if significand(ap, dtype) % 7 and F32(F32(a) / F32(7.0)) >= F32(2.0 ** -126):
+            one = model_codes_single(vals.astype(np.float32), a, dtype)
+            bad = np.flatnonzero(one != ref_codes[0])
+            assert bad.size == 0, ("single", hex(ap), [(hex(int(bits[i])), int(one[i]), int(ref_codes[0][i]))
+                                                        for i in bad[:5]])
+            single += 1
+        else:
+            table += 1
     # both outcomes of a tie occur (a rule that always rounds half to even,
     # or always away from zero, would fail above)
     assert ties > 0 and 0 < ups < ties, (ties, ups)
+    # both paths of the kernel are exercised
+    assert single > 10 and table > 3, (single, table)
