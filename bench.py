@@ -18,11 +18,11 @@ mismatch ends the run with an error.  The statistics go into the line.
 --no-cpu skips the whole CPU leg (parity and baseline).
 
 Each kernel is then timed alone on the stream it runs on, over max(steps, 50)
-launches with a HIP event pair around every launch: their mean (the figure
-rocprofv3's kernel statistics average, and the one `roofline.achieved`
-divides the kernel's algorithmic work by), median, p10 and p90; plus the
-average over one event pair around the back-to-back launches (ms_loop,
-which includes the gaps between kernels).
+launches with a HIP event pair around every launch: their median (the figure
+rocprofv3's average kernel duration agrees with, and the one
+`roofline.achieved` divides the kernel's algorithmic work by), mean, p10 and
+p90; plus the average over one event pair around the back-to-back launches
+(ms_loop, which includes the gaps between kernels).
 
 The line also carries the other four workloads (wide-K transposed-view fp16,
 decode-like M=32, tiny fp32, large-K with smoothing, per-64-group scales and a
@@ -54,13 +54,14 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, published
 MIN_KERNEL_LAUNCHES = 50
 TRAFFIC_FILES = {  # kernel source -> committed counter summary
-    "gemm": ("bit_quantized_linear_rotate_amd/csrc/gemm.hip", "profiles/gemm_prefill_m8192_k3840_n3840_traffic.json"),
-    "rotate_quant": ("bit_quantized_linear_rotate_amd/csrc/rotate_quant.hip",
-                     "profiles/rotate_quant_prefill_m8192_k3840_g64_traffic.json"),
+    "gemm": ("bit_quantized_linear_rotate_amd/csrc/gemm.hip",
+             "profiles/gemm_ring3_prefill_m8192_k3840_n3840_traffic.json"),
+    "rotate_quant": ("bit_quantized_linear_rotate_amd/csrc/rq_row.hip",
+                     "profiles/rotate_quant_row_prefill_m8192_k3840_g64_traffic.json"),
 }
 GEMM_NAMES = {"ring3": "w4a4_gemm_ring3_kernel", "skinny": "w4a4_gemm_skinny_kernel",
               "tile128": "w4a4_gemm_kernel", "tile128_splitk": "w4a4_gemm_kernel (K chunks)"}
-RQ_NAMES = {"wave": "rq_wave_kernel", "colmajor": "rq_colmajor_kernel", "g256": "rq_g256_kernel",
+RQ_NAMES = {"row": "rq_row_kernel", "wave": "rq_wave_kernel", "colmajor": "rq_colmajor_kernel", "g256": "rq_g256_kernel",
             "reg": "rq_reg_kernel", "mfma_lds": "rq_mfma_kernel", "generic": "rq_generic_kernel"}
 
 
@@ -119,10 +120,9 @@ def _variant(d, i, torch):
 def _time_each(fn, n, torch, np):
     """Two passes of n calls each, HIP events on the current stream (the
     stream the binding launches on):
-      * an event pair around every launch: ms_mean (their mean: the kernel's
-        average launch duration, the figure rocprofv3's kernel statistics
-        average and the one the roofline figures divide by), ms_median,
-        ms_p10, ms_p90;
+      * an event pair around every launch: ms_median (the figure
+        rocprofv3's average kernel duration agrees with, and the one the
+        roofline figures divide by), ms_mean, ms_p10, ms_p90;
       * ms_loop: one event pair around n back-to-back launches, divided by n
         (includes the gaps between consecutive kernels)."""
     st = torch.cuda.current_stream()
@@ -297,7 +297,9 @@ def measure(name, steps, warmup, torch, np, w4, workloads, cpu=True):
     gemm_bytes = (M * K + N * K // 2 + 4 * M + base["w_scale"].numel() * base["w_scale"].element_size()
                   + (N * base["bias"].element_size() if base["bias"] is not None else 0)
                   + M * N * outs[0].element_size())
-    ms_rq, ms_gemm = t_rq["ms_mean"], t_gemm["ms_mean"]
+    # per-launch medians: the figure rocprofv3's kernel statistics agree
+    # with (the mean carries the event pairs' own occasional delays)
+    ms_rq, ms_gemm = t_rq["ms_median"], t_gemm["ms_median"]
     res = {
         "workload": f"{name}: M={M} K={K} N={N} g={g} {w.dtype}"
                     + (" transposed-view input" if w.transposed else "")
@@ -335,8 +337,8 @@ def measure(name, steps, warmup, torch, np, w4, workloads, cpu=True):
         t_lrd = _time_each(lrd, nk, torch, np)
         lrd_bytes = M * K * base["x"].element_size() + K * rank * base["proj_down"].element_size() + 4 * M * rank
         res["lowrank_down"] = {"kernel": "lowrank down projection", **t_lrd,
-                               "GB_s": lrd_bytes / (t_lrd["ms_mean"] * 1e-3) / 1e9,
-                               "frac_hbm": lrd_bytes / (t_lrd["ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                               "GB_s": lrd_bytes / (t_lrd["ms_median"] * 1e-3) / 1e9,
+                               "frac_hbm": lrd_bytes / (t_lrd["ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                "algorithmic_bytes": lrd_bytes}
     return w, inp, res
 
@@ -373,13 +375,13 @@ def stream_ceiling(w, steps, torch, np):
             for i in range(5):
                 run(i)
             t = _time_each(run, max(steps, MIN_KERNEL_LAUNCHES), torch, np)
-            if best is None or t["ms_mean"] < best[0]["ms_mean"]:
+            if best is None or t["ms_median"] < best[0]["ms_median"]:
                 best = (t, grid, nt)
     t, grid, nt = best
     return {"kernel": "stream_probe_kernel (same bytes as rotate-quant, no arithmetic)",
             **t, "grid": grid, "nontemporal_stores": bool(nt), "bytes": nbytes,
-            "GB_s": nbytes / (t["ms_mean"] * 1e-3) / 1e9,
-            "frac_hbm_peak": nbytes / (t["ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "GB_s": nbytes / (t["ms_median"] * 1e-3) / 1e9,
+            "frac_hbm_peak": nbytes / (t["ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def cpu_baseline(w, inp, np, target_s=15.0):
@@ -409,6 +411,174 @@ def cpu_baseline(w, inp, np, target_s=15.0):
             "sample": f"{what}, {reps} call(s): {dt:.1f} s"}
 
 
+# --- counter summaries (host only): turns the rocprofv3 CSVs of the commands
+# below into the text summaries under profiles/
+PROFILE_COMMANDS = {
+    "stats": "rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof_all -o run "
+             "-- python3 $REPO/bench.py",
+    "FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmcF -o f "
+                  "-- python3 $REPO/bench.py --steps 3 --warmup 1 --no-cpu --copy-calibration",
+    "WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmcW -o w "
+                  "-- python3 $REPO/bench.py --steps 3 --warmup 1 --no-cpu --copy-calibration",
+    "SQ": "rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVES "
+          "SQ_INSTS_LDS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE --output-format csv -d $REPO/gpurun_out/pmcS -o s "
+          "-- python3 $REPO/bench.py --steps 3 --warmup 1 --no-cpu",
+}
+N_XCD, N_SIMD = 8, 1024   # MI355X: GRBM_GUI_ACTIVE sums the 8 XCDs; 256 CUs x 4 SIMDs
+
+
+def _profile_kernels():
+    """(kernel name, summary stem, workload text, algorithmic bytes, ops,
+    source file) of the kernels the summaries cover."""
+    import workloads
+    W = workloads.WORKLOADS
+    es = {"bf16": 2, "f16": 2, "f32": 4}
+
+    def rq_bytes(w):
+        xs = es[w.dtype]
+        return w.M * w.K * xs + w.M * w.K + 4 * w.M + 4 * w.g * w.g + (w.K * xs if w.smooth else 0)
+
+    def gemm_bytes(w):
+        sw = (w.K // 64 if w.sw_group else 1) * w.N * es[w.sw_dtype]
+        return (w.M * w.K + w.N * w.K // 2 + 4 * w.M + sw + (w.N * es[w.dtype] if w.bias else 0)
+                + w.M * w.N * es[w.dtype])
+
+    def text(w):
+        return (f"{w.name}: M={w.M} K={w.K} N={w.N} g={w.g} {w.dtype}"
+                + (" transposed view" if w.transposed else "") + (" smoothing" if w.smooth else "")
+                + (f" rank {w.rank}" if w.rank else "") + (" per-64-group scales" if w.sw_group else ""))
+    p, wk, lr = W["prefill"], W["widek"], W["lowrank"]
+    src = "bit_quantized_linear_rotate_amd/csrc/"
+    return [
+        ("void w4a4::rq_row_kernel<2, false, false, 4, 1>", "rotate_quant_row_prefill_m8192_k3840_g64",
+         text(p), rq_bytes(p), None, src + "rq_row.hip"),
+        ("void w4a4::w4a4_gemm_ring3_kernel<2>", "gemm_ring3_prefill_m8192_k3840_n3840",
+         text(p), gemm_bytes(p), 2.0 * p.M * p.N * p.K, src + "gemm.hip"),
+        ("void w4a4::rq_colmajor_kernel<1, 256, false, false, 6>", "rotate_quant_colmajor_widek_m8192_k10240_g256",
+         text(wk), rq_bytes(wk), None, src + "rotate_quant.hip"),
+        ("void w4a4::w4a4_gemm_ring3_kernel<1>", "gemm_ring3_widek_m8192_k10240_n3840",
+         text(wk), gemm_bytes(wk), 2.0 * wk.M * wk.N * wk.K, src + "gemm.hip"),
+        ("void w4a4::rq_g256_kernel<2, true>", "rotate_quant_g256_lowrank_m4096_k16384",
+         text(lr), rq_bytes(lr), None, src + "rotate_quant.hip"),
+        ("void w4a4::w4a4_gemm_kernel<2, false, true>", "gemm_tile128_lowrank_m4096_k16384_n6144",
+         text(lr), gemm_bytes(lr), 2.0 * lr.M * lr.N * lr.K, src + "gemm.hip"),
+        ("void w4a4::lowrank_wide_kernel<2, 32>", "lowrank_down_lowrank_m4096_k16384_r32",
+         text(lr), lr.M * lr.K * 2 + lr.K * lr.rank * 2 + 4 * lr.M * lr.rank, None, src + "lowrank.hip"),
+        ("void (anonymous namespace)::stream_probe_kernel<true>", "stream_probe_nt_prefill_m8192_k3840",
+         "streaming probe, the prefill rotate-quant's bytes (non-temporal stores)",
+         p.M * p.K * 2 + p.M * p.K + 4 * p.M, None, src + "stream_probe.hip"),
+    ]
+
+
+def _short_name(k):
+    """Kernel name without the return type and the parameter list."""
+    k = k[5:] if k.startswith("void ") else k
+    pre = "(anonymous namespace)::"
+    head = pre if k.startswith(pre) else ""
+    return head + k[len(head):].split("(")[0]
+
+
+def summarize_profiles(d):
+    """profiles/*.md and the two traffic .json files from the CSVs in
+    directory d (prof_all/, pmcF/, pmcW/, pmcS/ as the commands above write
+    them)."""
+    import csv
+    import glob
+    import hashlib
+    import statistics
+
+    def one(pattern):
+        f = glob.glob(os.path.join(d, pattern))
+        if len(f) != 1:
+            raise SystemExit(f"expected one file {pattern} under {d}, found {f}")
+        return list(csv.DictReader(open(f[0])))
+
+    def counters(rows):
+        by = {}
+        for r in rows:
+            by.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        return by
+    F = counters(one("pmcF/f_counter_collection.csv"))
+    Wr = counters(one("pmcW/w_counter_collection.csv"))
+    S = counters(one("pmcS/s_counter_collection.csv"))
+    stats = {r["Name"]: r for r in one("prof_all/run_kernel_stats.csv")}
+    copy = "__amd_rocclr_copyBuffer"
+    cal_bytes = 256 << 20
+    f_copy, w_copy = max(F[copy]["FETCH_SIZE"]), max(Wr[copy]["WRITE_SIZE"])
+    f_scale, w_scale = cal_bytes / (f_copy * 1024), cal_bytes / (w_copy * 1024)
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    med = statistics.median
+    rows_md = []
+    for name, stem, wtext, alg, ops, srcf in _profile_kernels():
+        full = [k for k in S if k.startswith(name)]
+        if not full:
+            continue
+        k = full[0]
+        st = stats.get(k)
+        fb = med(F[k]["FETCH_SIZE"]) * 1024 * f_scale
+        wb = med(Wr[k]["WRITE_SIZE"]) * 1024 * w_scale
+        sq = {c: med(v) for c, v in S[k].items()}
+        cyc = sq["GRBM_GUI_ACTIVE"] / N_XCD
+        avg_ns = float(st["AverageNs"]) if st else None
+        lines = [f"# `{_short_name(k)}` — {wtext}", "",
+                 "Commands (`$REPO` is the repository root, run from `/tmp` with `TMPDIR=/tmp`), "
+                 "then `python bench.py --summarize-profiles gpurun_out` on the host:", "", "```"]
+        lines += [PROFILE_COMMANDS[c] for c in ("stats", "FETCH_SIZE", "WRITE_SIZE", "SQ")]
+        lines += ["```", ""]
+        if st:
+            lines += [f"Kernel statistics (`--kernel-trace --stats`, the default bench run): {st['Calls']} calls, "
+                      f"average {avg_ns / 1000:.2f} us, min {float(st['MinNs']) / 1000:.2f} us, "
+                      f"max {float(st['MaxNs']) / 1000:.2f} us.", ""]
+        lines += ["Counters, median per dispatch:", "", "| Counter | Value |", "|---|---|"]
+        lines += [f"| FETCH_SIZE x 1024 x {f_scale:.4f} (bytes) | {fb:,.0f} |",
+                  f"| WRITE_SIZE x 1024 x {w_scale:.4f} (bytes) | {wb:,.0f} |",
+                  f"| algorithmic bytes | {alg:,} |",
+                  f"| traffic / algorithmic | {(fb + wb) / alg:.3f} |"]
+        for c in ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS",
+                  "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"):
+            lines.append(f"| {c} | {sq[c]:,.0f} |")
+        mfma_busy = sq["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_SIMD)
+        valu_busy = 4 * sq["SQ_INSTS_VALU"] / (cyc * N_SIMD)
+        lines += ["", "Derived (GRBM_GUI_ACTIVE / 8 = cycles of one XCD over the counter run's dispatch, "
+                  "which the profiler serialises and can stretch; 1024 SIMDs):", "",
+                  f"- cycles per XCD {cyc:,.0f}",
+                  f"- MFMA busy {100 * mfma_busy:.1f}% of SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES)",
+                  f"- VALU issue {100 * valu_busy:.1f}% of SIMD cycles (4 cycles per wave64 instruction)"]
+        if avg_ns:
+            lines.append(f"- algorithmic bytes / average duration: {alg / (avg_ns * 1e-9) / 1e9:,.0f} GB/s "
+                         f"({100 * alg / (avg_ns * 1e-9) / 1e9 / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+            if ops:
+                lines.append(f"- ops / average duration: {ops / (avg_ns * 1e-9) / 1e12:,.0f} TOPS "
+                             f"({100 * ops / (avg_ns * 1e-9) / 1e12 / INT8_PEAK_TOPS:.1f}% of the dense INT8 peak)")
+        with open(os.path.join(out_dir, stem + ".md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        rows_md.append((k, wtext, st))
+        if stem in ("rotate_quant_row_prefill_m8192_k3840_g64", "gemm_ring3_prefill_m8192_k3840_n3840"):
+            with open(os.path.join(ROOT, srcf), "rb") as f:
+                digest = hashlib.sha256(f.read()).hexdigest()
+            rec = {"kernel": _short_name(k), "workload": "prefill", "source": srcf,
+                   "source_sha256": digest, "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+                   "traffic_bytes_per_launch": round(fb + wb), "algorithmic_bytes_per_launch": alg,
+                   "launches_counted": len(F[k]["FETCH_SIZE"]),
+                   "calibration": {"copy_bytes": cal_bytes, "fetch_scale": round(f_scale, 4),
+                                   "write_scale": round(w_scale, 4)},
+                   "commands": [PROFILE_COMMANDS["FETCH_SIZE"], PROFILE_COMMANDS["WRITE_SIZE"]]}
+            with open(os.path.join(out_dir, stem + "_traffic.json"), "w") as f:
+                json.dump(rec, f, indent=1)
+    # all kernels of the default run
+    lines = ["# rocprofv3 kernel statistics — the default bench run (all five workloads)", "", "```",
+             PROFILE_COMMANDS["stats"], "```", "",
+             "| Kernel | Calls | Average us | Min us | Max us | Share |", "|---|---|---|---|---|---|"]
+    for r in sorted(stats.values(), key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{_short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1000:.2f} | "
+                     f"{float(r['MinNs']) / 1000:.2f} | {float(r['MaxNs']) / 1000:.2f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    with open(os.path.join(out_dir, "kernel_stats_all_workloads.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {len(rows_md) * 1 + 1} summaries under profiles/")
+
+
 def _rounded(d):
     return {k: (round(v, 5) if isinstance(v, float) else _rounded(v) if isinstance(v, dict) else v)
             for k, v in d.items()}
@@ -423,7 +593,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/ from the rocprofv3 CSVs under DIR (host only) and exit")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the layer's data-parallel split (rows of the "
               f"activation across GPUs, weights replicated) needs no exchange, so N={args.gpus} "
@@ -480,7 +655,7 @@ def main():
                      "unit": "TOPS", "frac": round(g["frac_int8"], 4),
                      "traffic": _traffic("gemm", args.workload),
                      "kernel": g["kernel"] + " (INT8 MFMA GEMM + fused scale/bias/cast epilogue)",
-                     "per_launch_ms": "mean of per-launch HIP event pairs"},
+                     "per_launch_ms": "median of per-launch HIP event pairs"},
         "roofline_rotate_quant": {"bound": "hbm", "achieved": round(rq["GB_s"], 1),
                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": round(rq["frac_hbm"], 4),
