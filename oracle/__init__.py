@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
         L.orc_smooth.argtypes = [i32, vp, i64, i64, vp, vp]
         L.orc_rotate.argtypes = [i32, vp, i64, i64, vp, i32, vp]
         L.orc_quantize.argtypes = [i32, vp, i64, i64, vp, vp]
+        L.orc_quantize_q.argtypes = [i32, vp, i64, i64, i32, vp, vp]
         L.orc_unpack.argtypes = [vp, i64, i64, vp]
         L.orc_pack.argtypes = [vp, i64, i64, vp]
         L.orc_gemm.argtypes = [vp, i64, i64, vp, i64, i32, vp]
@@ -64,7 +65,7 @@ def lib() -> ctypes.CDLL:
         L.orc_epilogue.argtypes = [vp, i64, i64, i64, i32, vp, vp, i32, vp, i32, vp, vp, i32,
                                    i32, vp, i32]
         L.orc_num_threads.argtypes = []
-        for f in ("orc_round_to", "orc_decode", "orc_smooth", "orc_rotate", "orc_quantize",
+        for f in ("orc_round_to", "orc_decode", "orc_smooth", "orc_rotate", "orc_quantize", "orc_quantize_q",
                   "orc_unpack", "orc_pack", "orc_gemm", "orc_lowrank_down", "orc_epilogue",
                   "orc_num_threads"):
             getattr(L, f).restype = ctypes.c_int
@@ -142,13 +143,14 @@ def rotate(x, R, g: int, dtype: str) -> np.ndarray:
     return y
 
 
-def quantize(y, dtype: str) -> tuple:
-    """Per-row absmax INT4 quantizer -> (codes int8 (M,K), scales fp32 (M,))."""
+def quantize(y, dtype: str, qmax: int = 7) -> tuple:
+    """Per-row absmax quantizer -> (codes int8 (M,K), scales fp32 (M,)):
+    INT4 codes for qmax = 7, the INT8 mode for qmax = 127."""
     y = _t(y, dtype)
     M, K = y.shape
     codes = np.empty((M, K), dtype=np.int8)
     scales = np.empty((M,), dtype=np.float32)
-    _check(lib().orc_quantize(DT[dtype], _p(y), M, K, _p(codes), _p(scales)), "quantize")
+    _check(lib().orc_quantize_q(DT[dtype], _p(y), M, K, int(qmax), _p(codes), _p(scales)), "quantize")
     return codes, scales
 
 
@@ -212,13 +214,34 @@ def epilogue(acc, s_a, s_w, sw_dtype: str, out_dtype: str, bias=None, bias_dtype
     return out
 
 
-def rotate_quant(x, R, g, dtype, smooth_factors=None):
+def rotate_quant(x, R, g, dtype, smooth_factors=None, qmax: int = 7):
     """Steps a1..a4: (optional smoothing), rotation, per-row quantization.
     ``R=None`` skips the rotation.  Returns (y, codes, scales)."""
     xs = smooth(x, smooth_factors, dtype) if smooth_factors is not None else _t(x, dtype)
     y = rotate(xs, R, g, dtype) if R is not None else xs
-    codes, scales = quantize(y, dtype)
+    codes, scales = quantize(y, dtype, qmax)
     return y, codes, scales
+
+
+def linear_int8(x, R, g, w, s_w, dtype: str, sw_dtype: str, bias=None, rows=None, cols=None) -> dict:
+    """The dynamic INT8 ConvRot linear ("[Feat][Ascend] Add fused RotateQuant
+    backend", "What this PR does": RotateQuant feeding the INT8 linear):
+    rotation, per-token INT8 codes (qmax = 127), the exact integer product
+    with INT8 weights w (N, K), then the same epilogue as the W4A4 layer
+    (per-token scale, per-channel weight scale, bias), on (optionally) a subset
+    of rows and columns."""
+    if rows is not None:
+        x = _t(x, dtype)[rows]
+    if cols is not None:
+        w = np.asarray(w)[cols]
+        s_w = np.asarray(s_w)[cols]
+        if bias is not None:
+            bias = np.asarray(bias)[cols]
+    y, codes, scales = rotate_quant(x, R, g, dtype, qmax=127)
+    acc = gemm(codes, w)
+    out = epilogue(acc, scales, s_w, sw_dtype, dtype, bias=bias,
+                   bias_dtype=dtype if bias is not None else None)
+    return {"y": y, "codes": codes, "scales": scales, "acc": acc, "out": out}
 
 
 def linear(inputs: dict, dtype: str, g: int, sw_dtype: str, sw_group: int = 0,

@@ -183,18 +183,22 @@ int orc_rotate(int dt, const void *x, int64_t M, int64_t K, const double *R, int
 }
 
 /* ------------------------------------------------------------------------ */
-/* a3/a4  Per-row signed-INT4 quantizer with codes kept in INT8 storage      */
+/* a3/a4  Per-row symmetric quantizer with codes kept in INT8 storage        */
 /* ([P1] W4A4 scope: the reference signed-INT4 quantizer; [P2] Summary: the  */
 /* same codes stay in INT8 storage; [P3] zero scales are replaced by the     */
 /* finite minimum before division, public scales stay positive).             */
 /* Readings R4/R5: a = max |y| over the row in fp32 (a NaN anywhere makes    */
-/* the scale NaN); s = a / 7 in IEEE fp32; s below the smallest normal fp32  */
-/* becomes 2^-126.  q = y / s (IEEE fp32 division, not a reciprocal          */
-/* multiply); code = clamp(round-half-even(q), -7, 7); a NaN quotient gives  */
-/* code 0.                                                                   */
+/* the scale NaN); s = a / qmax in IEEE fp32; s below the smallest normal    */
+/* fp32 becomes 2^-126.  q = y / s (IEEE fp32 division, not a reciprocal     */
+/* multiply); code = clamp(round-half-even(q), -qmax, qmax); a NaN quotient  */
+/* gives code 0.  qmax = 7 for the INT4 codes of the W4A4 layer; qmax = 127  */
+/* for the INT8 mode of the fused RotateQuant of [P3] "What this PR does"    */
+/* (reading R16: the same rule on the symmetric INT8 grid, -128 unused).     */
 /* ------------------------------------------------------------------------ */
-int orc_quantize(int dt, const void *y, int64_t M, int64_t K, int8_t *codes, float *scales)
+int orc_quantize_q(int dt, const void *y, int64_t M, int64_t K, int qmax, int8_t *codes, float *scales)
 {
+    if (qmax != 7 && qmax != 127) return 1;
+    const float fq = (float)qmax;
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         float a = 0.0f;
@@ -207,7 +211,7 @@ int orc_quantize(int dt, const void *y, int64_t M, int64_t K, int8_t *codes, flo
         float s;
         if (nan_row) s = NAN;
         else {
-            s = a / 7.0f;
+            s = a / fq;
             if (s < FLT_MIN) s = FLT_MIN; /* 2^-126 */
         }
         scales[m] = s;
@@ -217,14 +221,19 @@ int orc_quantize(int dt, const void *y, int64_t M, int64_t K, int8_t *codes, flo
             int8_t c = 0;
             if (!isnan(q)) {
                 float r = nearbyintf(q);
-                if (r > 7.0f) r = 7.0f;
-                if (r < -7.0f) r = -7.0f;
+                if (r > fq) r = fq;
+                if (r < -fq) r = -fq;
                 c = (int8_t)r;
             }
             codes[m * K + k] = c;
         }
     }
     return 0;
+}
+
+int orc_quantize(int dt, const void *y, int64_t M, int64_t K, int8_t *codes, float *scales)
+{
+    return orc_quantize_q(dt, y, M, K, 7, codes, scales);
 }
 
 /* ------------------------------------------------------------------------ */
