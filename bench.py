@@ -450,7 +450,7 @@ def _profile_kernels():
     p, wk, lr = W["prefill"], W["widek"], W["lowrank"]
     src = "bit_quantized_linear_rotate_amd/csrc/"
     return [
-        ("void w4a4::rq_row_kernel<2, false, false, 4, 1>", "rotate_quant_row_prefill_m8192_k3840_g64",
+        ("void w4a4::rq_row_kernel<2, false, false, 4, 1, 7>", "rotate_quant_row_prefill_m8192_k3840_g64",
          text(p), rq_bytes(p), None, src + "rq_row.hip"),
         ("void w4a4::w4a4_gemm_ring3_kernel<2>", "gemm_ring3_prefill_m8192_k3840_n3840",
          text(p), gemm_bytes(p), 2.0 * p.M * p.N * p.K, src + "gemm.hip"),
@@ -458,9 +458,9 @@ def _profile_kernels():
          text(wk), rq_bytes(wk), None, src + "rotate_quant.hip"),
         ("void w4a4::w4a4_gemm_ring3_kernel<1>", "gemm_ring3_widek_m8192_k10240_n3840",
          text(wk), gemm_bytes(wk), 2.0 * wk.M * wk.N * wk.K, src + "gemm.hip"),
-        ("void w4a4::rq_g256_kernel<2, true>", "rotate_quant_g256_lowrank_m4096_k16384",
+        ("void w4a4::rq_g256_kernel<2, true, 7>", "rotate_quant_g256_lowrank_m4096_k16384",
          text(lr), rq_bytes(lr), None, src + "rotate_quant.hip"),
-        ("void w4a4::w4a4_gemm_kernel<2, false, true>", "gemm_tile128_lowrank_m4096_k16384_n6144",
+        ("void w4a4::w4a4_gemm_kernel<2, false, true, false>", "gemm_tile128_lowrank_m4096_k16384_n6144",
          text(lr), gemm_bytes(lr), 2.0 * lr.M * lr.N * lr.K, src + "gemm.hip"),
         ("void w4a4::lowrank_wide_kernel<2, 32>", "lowrank_down_lowrank_m4096_k16384_r32",
          text(lr), lr.M * lr.K * 2 + lr.K * lr.rank * 2 + 4 * lr.M * lr.rank, None, src + "lowrank.hip"),

@@ -18,4 +18,10 @@ from ._binding import (  # noqa: F401
     w4a4_lowrank_down,
     w4a4_rotate_quant_plan,
     w4a4_rotate_quant_rowwise,
+    w8a8_gemm_from_codes,
+    w8a8_gemm_workspace_size,
+    w8a8_linear,
+    w8a8_linear_workspace_size,
+    w8a8_rotate_quant_plan,
+    w8a8_rotate_quant_rowwise,
 )

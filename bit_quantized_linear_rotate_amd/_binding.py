@@ -38,6 +38,16 @@ _SIGNATURES = {
                      ctypes.c_int, _i32, _vp, _vp, _vp, _i32, _vp, ctypes.c_int, _vp, _sz, _vp],
                     ctypes.c_int),
     "w4a4_linear_workspace_size": ([_i64, _i64, _i64, _i32], _sz),
+    "w8a8_rotate_quant_rowwise": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp,
+                                   _vp, _vp, _vp], ctypes.c_int),
+    "w8a8_gemm_from_codes": ([_vp, _vp, _i64, _i64, _vp, _i64, _vp, ctypes.c_int, _vp, ctypes.c_int,
+                              _vp, ctypes.c_int, _vp, _sz, _vp], ctypes.c_int),
+    "w8a8_gemm_workspace_size": ([_i64, _i64, _i64], _sz),
+    "w8a8_linear": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _i64, _vp,
+                     ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _sz, _vp], ctypes.c_int),
+    "w8a8_linear_workspace_size": ([_i64, _i64, _i64], _sz),
+    "w8a8_rotate_quant_plan": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp,
+                                ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
     "w4a4_linear_noalloc": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _i64,
                              _vp, ctypes.c_int, _i32, _vp, _vp, _vp, _i32, _vp, ctypes.c_int, _vp],
                             ctypes.c_int),
@@ -393,4 +403,128 @@ def w4a4_linear_noalloc(x: torch.Tensor, rot: Optional[torch.Tensor], g: int,
         _ptr(w_packed), N, _ptr(w_scale), _dt(w_scale), w_scale_group, _ptr(bias),
         _ptr(proj_down), _ptr(proj_up), rank, _ptr(out), _DT[out.dtype], _stream(x2.device))
     _check(rc, "w4a4_linear_noalloc")
+    return out.view(*lead, N)
+
+
+# ---- INT8 mode (qmax = 127) and the dynamic INT8 linear --------------------
+
+def w8a8_rotate_quant_rowwise(x: torch.Tensor, rot: Optional[torch.Tensor], g: int,
+                              smooth: Optional[torch.Tensor] = None,
+                              return_rotated: bool = False):
+    """Rotate + per-row INT8 quantization (codes in [-127, 127]).  Returns
+    (codes int8 (M, K), scales fp32 (M,)) and, if requested, the rotated
+    values (M, K) in x.dtype."""
+    x2 = _as_2d(_need(x, "x", contiguous=False))
+    M, K = x2.shape
+    _dt(x2)
+    rot, g = _rot_arg(rot, g)
+    if smooth is not None:
+        _need(smooth, "smooth", (K,), (x2.dtype,))
+    _same_device(x2, rot=rot, smooth=smooth)
+    dev = x2.device
+    codes = torch.empty((M, K), dtype=torch.int8, device=dev)
+    scales = torch.empty((M,), dtype=torch.float32, device=dev)
+    rotated = torch.empty((M, K), dtype=x2.dtype, device=dev) if return_rotated else None
+    rc = lib().w8a8_rotate_quant_rowwise(
+        _ptr(x2), _dt(x2), M, K, x2.stride(0), x2.stride(1), _ptr(rot), g, _ptr(smooth),
+        _ptr(codes), _ptr(scales), _ptr(rotated), _stream(dev))
+    _check(rc, "w8a8_rotate_quant_rowwise")
+    return (codes, scales, rotated) if return_rotated else (codes, scales)
+
+
+def w8a8_rotate_quant_plan(x: torch.Tensor, rot: Optional[torch.Tensor], g: int,
+                           smooth: Optional[torch.Tensor] = None,
+                           return_rotated: bool = False) -> str:
+    """Name of the kernel w8a8_rotate_quant_rowwise would launch (host-only)."""
+    x2 = _as_2d(x)
+    M, K = x2.shape
+    rot, g = _rot_arg(rot, g)
+    k = ctypes.c_int(-1)
+    rc = lib().w8a8_rotate_quant_plan(_ptr(x2), _dt(x2), M, K, x2.stride(0), x2.stride(1),
+                                      _ptr(rot), g, _ptr(smooth), _ALIGNED,
+                                      _ALIGNED if return_rotated else None, ctypes.byref(k))
+    _check(rc, "w8a8_rotate_quant_plan")
+    return RQ_KERNELS.get(k.value, "none")
+
+
+def w8a8_gemm_workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().w8a8_gemm_workspace_size(M, N, K))
+
+
+def w8a8_linear_workspace_size(M: int, K: int, N: int) -> int:
+    return int(lib().w8a8_linear_workspace_size(M, K, N))
+
+
+def w8a8_gemm_from_codes(codes: torch.Tensor, scales: torch.Tensor, w: torch.Tensor,
+                         w_scale: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                         out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """INT8-code x INT8-weight GEMM (w: (N, K) int8) with the E-B epilogue."""
+    _need(codes, "codes", dtypes=(torch.int8,))
+    if codes.dim() != 2:
+        raise ValueError(f"codes must be (M, K), got shape {tuple(codes.shape)}")
+    M, K = codes.shape
+    _need(w, "w", dtypes=(torch.int8,))
+    if w.dim() != 2 or w.shape[1] != K:
+        raise ValueError(f"w has shape {tuple(w.shape)}, expected (N, {K})")
+    N = w.shape[0]
+    _need(scales, "scales", (M,), (torch.float32,))
+    _need(w_scale, "w_scale", (N,), _FLOAT)
+    if bias is not None:
+        _need(bias, "bias", (N,), _FLOAT)
+    if out_dtype not in _FLOAT:
+        raise ValueError(f"out_dtype {out_dtype} is not float32/float16/bfloat16")
+    _same_device(codes, scales=scales, w=w, w_scale=w_scale, bias=bias)
+    dev = codes.device
+    out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    wsz = w8a8_gemm_workspace_size(M, N, K)
+    ws = torch.empty((max(wsz, 1),), dtype=torch.uint8, device=dev) if wsz else None
+    rc = lib().w8a8_gemm_from_codes(
+        _ptr(codes), _ptr(scales), M, K, _ptr(w), N, _ptr(w_scale), _dt(w_scale), _ptr(bias),
+        _dt(bias) if bias is not None else 0, _ptr(out), _DT[out_dtype], _ptr(ws), wsz, _stream(dev))
+    _check(rc, "w8a8_gemm_from_codes")
+    return out
+
+
+def w8a8_linear(x: torch.Tensor, rot: Optional[torch.Tensor], g: int, w: torch.Tensor,
+                w_scale: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                smooth: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                workspace: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The dynamic INT8 ConvRot linear: y = layer(x) of shape (..., N)."""
+    lead = _need(x, "x", contiguous=False).shape[:-1]
+    x2 = _as_2d(x)
+    M, K = x2.shape
+    _dt(x2)
+    rot, g = _rot_arg(rot, g)
+    _need(w, "w", dtypes=(torch.int8,))
+    if w.dim() != 2 or w.shape[1] != K:
+        raise ValueError(f"w has shape {tuple(w.shape)}, expected (N, {K})")
+    N = w.shape[0]
+    _need(w_scale, "w_scale", (N,), _FLOAT)
+    if bias is not None:
+        _need(bias, "bias", (N,), (x2.dtype,))
+    if smooth is not None:
+        _need(smooth, "smooth", (K,), (x2.dtype,))
+    out_dtype = out_dtype or (out.dtype if out is not None else x2.dtype)
+    if out_dtype not in _FLOAT:
+        raise ValueError(f"out_dtype {out_dtype} is not float32/float16/bfloat16")
+    if out is not None:
+        _need(out, "out", (M, N), (out_dtype,))
+    need = w8a8_linear_workspace_size(M, K, N)
+    if workspace is not None:
+        _need(workspace, "workspace", dtypes=(torch.uint8,))
+        if workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, need {need}")
+    _same_device(x2, rot=rot, w=w, w_scale=w_scale, bias=bias, smooth=smooth, out=out,
+                 workspace=workspace)
+    dev = x2.device
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    rc = lib().w8a8_linear(
+        _ptr(x2), _dt(x2), M, K, x2.stride(0), x2.stride(1), _ptr(rot), g, _ptr(smooth), _ptr(w), N,
+        _ptr(w_scale), _dt(w_scale), _ptr(bias), _ptr(out), _DT[out.dtype], _ptr(workspace),
+        workspace.numel(), _stream(dev))
+    _check(rc, "w8a8_linear")
     return out.view(*lead, N)

@@ -56,20 +56,20 @@ int device_check()
 
 bool pow2_g(int g) { return g == 16 || g == 32 || g == 64 || g == 128 || g == 256; }
 
-int check_activation(const void* x, int dt, int64_t M, int64_t K, int64_t sm, int64_t sk)
+int check_activation(const void* x, int dt, int64_t M, int64_t K, int64_t sm, int64_t sk, bool int4 = true)
 {
     if (M < 0 || K < 0) return fail(W4A4_INVALID, "negative size M=%lld K=%lld", (long long)M, (long long)K);
     if (sm < 0 || sk < 0) return fail(W4A4_INVALID, "negative stride");
     if (!dtype_ok(dt)) return fail(W4A4_UNSUPPORTED, "unknown activation dtype %d", dt);
-    if (K % 2) return fail(W4A4_INVALID, "K=%lld is odd: INT4 rows need an even width", (long long)K);
+    if (int4 && K % 2) return fail(W4A4_INVALID, "K=%lld is odd: INT4 rows need an even width", (long long)K);
     if (M > 0 && K > 0 && !x) return fail(W4A4_INVALID, "x is NULL");
     return W4A4_OK;
 }
 
 int rq_validate(const void* x, int dt, int64_t M, int64_t K, int64_t sm, int64_t sk, const float* rot,
-                int g, int8_t* codes, float* scales)
+                int g, int8_t* codes, float* scales, bool int4 = true)
 {
-    int rc = check_activation(x, dt, M, K, sm, sk);
+    int rc = check_activation(x, dt, M, K, sm, sk, int4);
     if (rc) return rc;
     if (rot) {
         if (g <= 0) return fail(W4A4_INVALID, "group size g=%d", g);
@@ -82,6 +82,7 @@ int rq_validate(const void* x, int dt, int64_t M, int64_t K, int64_t sm, int64_t
 }
 
 int64_t guard_chunk(int64_t K) { return K > kGemmMaxK ? kGemmMaxK : 0; }
+int64_t guard_chunk8(int64_t K) { return K > kGemmMaxK8 ? kGemmMaxK8 : 0; }
 
 int gemm_validate(const int8_t* codes, const float* scales, int64_t M, int64_t K, const uint8_t* wp,
                   int64_t N, const void* sw, int sw_dt, int sw_group, const void* bias, int bias_dt,
@@ -324,6 +325,120 @@ int w4a4_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride
     if (e != hipSuccess) return hip_fail(e, "rotate_quant launch");
     GemmArgs ga{codes, scales, M, K, N, w_packed, w_scale, w_scale_dtype, w_scale_group,
                 bias, x_dtype, lora, proj_up, x_dtype, r, out, out_dtype, nullptr, kc, acc64};
+    e = launch_gemm(ga, st);
+    if (e != hipSuccess) return hip_fail(e, "gemm launch");
+    return W4A4_OK;
+}
+
+// ---- INT8 mode (qmax = 127) and the dynamic INT8 linear ----------------
+
+int w8a8_rotate_quant_rowwise(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                              int64_t stride_k, const float* rot, int32_t g, const void* smooth,
+                              int8_t* codes, float* scales, void* rotated_out, void* stream)
+{
+    int rc = rq_validate(x, x_dtype, M, K, stride_m, stride_k, rot, g, codes, scales, false);
+    if (rc) return rc;
+    if (M == 0) return W4A4_OK;
+    rc = device_check();
+    if (rc) return rc;
+    RQArgs a{x, x_dtype, M, K, stride_m, stride_k, rot, rot ? g : 0, smooth, codes, scales, rotated_out};
+    a.qmax = 127;
+    int path = 0;
+    hipError_t e = launch_rotate_quant(a, (hipStream_t)stream, &path);
+    if (e == hipErrorNotSupported)
+        return fail(W4A4_UNSUPPORTED, "no INT8 rotate_quant kernel for this shape (K=%lld)", (long long)K);
+    if (e != hipSuccess) return hip_fail(e, "rotate_quant launch");
+    return W4A4_OK;
+}
+
+int w8a8_rotate_quant_plan(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                           int64_t stride_k, const float* rot, int32_t g, const void* smooth,
+                           const int8_t* codes, const void* rotated_out, int* kernel)
+{
+    int rc = rq_validate(x, x_dtype, M, K, stride_m, stride_k, rot, g, (int8_t*)codes, (float*)1, false);
+    if (rc) return rc;
+    RQArgs a{x, x_dtype, M, K, stride_m, stride_k, rot, rot ? g : 0, smooth, (int8_t*)codes,
+             nullptr, (void*)rotated_out};
+    a.qmax = 127;
+    const int p = M > 0 ? rotate_quant_path(a) : -1;
+    if (M > 0 && p < 0)
+        return fail(W4A4_UNSUPPORTED, "no INT8 rotate_quant kernel for this shape (K=%lld)", (long long)K);
+    if (kernel) *kernel = p;
+    return W4A4_OK;
+}
+
+size_t w8a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0) return 0;
+    return guard_chunk8(K) > 0 ? align256((size_t)M * (size_t)N * 8) : 0;
+}
+
+int w8a8_gemm_from_codes(const int8_t* codes, const float* scales, int64_t M, int64_t K,
+                         const int8_t* w, int64_t N, const void* w_scale, int w_scale_dtype,
+                         const void* bias, int bias_dtype, void* out, int out_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream)
+{
+    if (M < 0 || K < 0 || N < 0) return fail(W4A4_INVALID, "negative size");
+    if (!dtype_ok(w_scale_dtype) || !dtype_ok(out_dtype) || (bias && !dtype_ok(bias_dtype)))
+        return fail(W4A4_UNSUPPORTED, "unknown dtype code");
+    if (M > 0 && N > 0 && (!scales || !w || !w_scale || !out || (K > 0 && !codes)))
+        return fail(W4A4_INVALID, "a required pointer is NULL");
+    if (M == 0 || N == 0) return W4A4_OK;
+    const int64_t kc = guard_chunk8(K);
+    const size_t need = w8a8_gemm_workspace_size(M, N, K);
+    if (workspace_bytes < need || (need && !workspace))
+        return fail(W4A4_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    int rc = device_check();
+    if (rc) return rc;
+    GemmArgs a{codes, scales, M, K, N, (const uint8_t*)w, w_scale, w_scale_dtype, 0,
+               bias, bias_dtype, nullptr, nullptr, 0, 0, out, out_dtype, nullptr, kc, (int64_t*)workspace};
+    a.w8 = 1;
+    hipError_t e = launch_gemm(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gemm launch");
+    return W4A4_OK;
+}
+
+size_t w8a8_linear_workspace_size(int64_t M, int64_t K, int64_t N)
+{
+    if (M <= 0) return 0;
+    size_t s = align256((size_t)M * (size_t)K) + align256((size_t)M * 4);
+    if (N > 0) s += w8a8_gemm_workspace_size(M, N, K);
+    return s;
+}
+
+int w8a8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m, int64_t stride_k,
+                const float* rot, int32_t g, const void* smooth, const int8_t* w, int64_t N,
+                const void* w_scale, int w_scale_dtype, const void* bias, void* out, int out_dtype,
+                void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc = rq_validate(x, x_dtype, M, K, stride_m, stride_k, rot, g, (int8_t*)1, (float*)1, false);
+    if (rc) return rc;
+    if (N < 0) return fail(W4A4_INVALID, "negative size");
+    if (!dtype_ok(w_scale_dtype) || !dtype_ok(out_dtype)) return fail(W4A4_UNSUPPORTED, "unknown dtype code");
+    if (M > 0 && N > 0 && (!w || !w_scale || !out)) return fail(W4A4_INVALID, "a required pointer is NULL");
+    if (M == 0 || N == 0) return W4A4_OK;
+    const size_t need = w8a8_linear_workspace_size(M, K, N);
+    if (!workspace || workspace_bytes < need)
+        return fail(W4A4_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    rc = device_check();
+    if (rc) return rc;
+    uint8_t* ws = (uint8_t*)workspace;
+    int8_t* codes = (int8_t*)ws;
+    ws += align256((size_t)M * (size_t)K);
+    float* scales = (float*)ws;
+    ws += align256((size_t)M * 4);
+    const int64_t kc = guard_chunk8(K);
+    hipStream_t st = (hipStream_t)stream;
+    RQArgs qa{x, x_dtype, M, K, stride_m, stride_k, rot, rot ? g : 0, smooth, codes, scales, nullptr};
+    qa.qmax = 127;
+    if (rotate_quant_path(qa) < 0)
+        return fail(W4A4_UNSUPPORTED, "no INT8 rotate_quant kernel for this shape (K=%lld)", (long long)K);
+    int path = 0;
+    hipError_t e = launch_rotate_quant(qa, st, &path);
+    if (e != hipSuccess) return hip_fail(e, "rotate_quant launch");
+    GemmArgs ga{codes, scales, M, K, N, (const uint8_t*)w, w_scale, w_scale_dtype, 0,
+                bias, x_dtype, nullptr, nullptr, 0, 0, out, out_dtype, nullptr, kc, kc > 0 ? (int64_t*)ws : nullptr};
+    ga.w8 = 1;
     e = launch_gemm(ga, st);
     if (e != hipSuccess) return hip_fail(e, "gemm launch");
     return W4A4_OK;

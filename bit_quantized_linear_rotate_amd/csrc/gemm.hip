@@ -81,9 +81,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // GSW: -1 for one weight scale per column, else the dtype of the per-64-group
 // weight scales (F32, F16 or BF16)
-template <int GSW, bool SPLIT, bool ALIGNED>
+template <int GSW, bool SPLIT, bool ALIGNED, bool W8 = false>
 __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
 {
+    // W8: INT8 weights (N, K) taken as they are (no unpack, no factor 16)
+    static_assert(!(W8 && GSW >= 0), "INT8 weights come with per-channel scales");
+    constexpr int SHIFT = W8 ? 0 : 4;
     constexpr bool GROUP = GSW >= 0;
     __shared__ __align__(16) int8_t As[2][BM * LDR];
     __shared__ __align__(16) int8_t Bs[2][BN * LDR];
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
 
     // global -> register staging
     uint4 ra[2];
-    uint4 rw;
+    uint4 rw, rw1;
     // ALIGNED without K-chunks (K % 64 == 0): buffer loads over the tile's
     // code rows and weight columns.  The step's k is added to the per-lane
     // offset, never passed as the scalar offset: the range check covers only
@@ -127,8 +130,9 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
     constexpr bool BUF = ALIGNED && !SPLIT;
     const __amdgpu_buffer_rsrc_t rca =
         make_rsrc(a.codes + (m0 < M ? m0 : 0) * K, (uint64_t)(m0 < M ? min(M - m0, (int64_t)BM) : 0) * K);
+    const int64_t wrow = W8 ? K : (K >> 1);   // weight bytes per column
     const __amdgpu_buffer_rsrc_t rcw = make_rsrc(
-        a.wp + (n0 < N ? n0 : 0) * (K >> 1), (uint64_t)(n0 < N ? min(N - n0, (int64_t)BN) : 0) * (K >> 1));
+        a.wp + (n0 < N ? n0 : 0) * wrow, (uint64_t)(n0 < N ? min(N - n0, (int64_t)BN) : 0) * wrow);
     auto gload = [&](int64_t k) {
         if constexpr (BUF) {
 #pragma unroll
@@ -137,8 +141,14 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
                 ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                     rca, (int)((c >> 2) * K + (c & 3) * 16 + k), 0, 0));
             }
-            rw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                rcw, (int)((tid >> 1) * (K >> 1) + (tid & 1) * 16 + (k >> 1)), 0, 0));
+            if constexpr (W8) {
+                const int wo = (int)((tid >> 1) * K + (tid & 1) * 32 + k);
+                rw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rcw, wo, 0, 0));
+                rw1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rcw, wo + 16, 0, 0));
+            } else {
+                rw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rcw, (int)((tid >> 1) * (K >> 1) + (tid & 1) * 16 + (k >> 1)), 0, 0));
+            }
             return;
         }
 #pragma unroll
@@ -160,6 +170,27 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
         }
         const int n = tid >> 1, half = tid & 1;
         const int64_t gn = n0 + n;
+        if constexpr (W8) {
+            const int64_t kw = k + half * 32;   // this thread's 32 weight bytes
+            if constexpr (ALIGNED) {
+                if (gn < N && kw < kend) {
+                    rw = *(const uint4*)(a.wp + gn * K + kw);
+                    rw1 = *(const uint4*)(a.wp + gn * K + kw + 16);
+                } else {
+                    rw = make_uint4(0, 0, 0, 0);
+                    rw1 = make_uint4(0, 0, 0, 0);
+                }
+            } else {
+                uint32_t wv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                if (gn < N)
+                    for (int e = 0; e < 32; ++e)
+                        if (kw + e < kend)
+                            wv[e >> 2] |= (uint32_t)a.wp[gn * K + kw + e] << (8 * (e & 3));
+                rw = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                rw1 = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+            }
+            return;
+        }
         const int64_t kp = (k >> 1) + half * 16;  // packed byte index
         if constexpr (ALIGNED) {
             if (gn < N && 2 * kp < kend) rw = *(const uint4*)(a.wp + gn * (K >> 1) + kp);
@@ -181,6 +212,11 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
             *(uint4*)(&As[buf][row * LDR + c16 * 16]) = ra[i];
         }
         const int n = tid >> 1, half = tid & 1;
+        if constexpr (W8) {
+            *(uint4*)(&Bs[buf][n * LDR + half * 32]) = rw;
+            *(uint4*)(&Bs[buf][n * LDR + half * 32 + 16]) = rw1;
+            return;
+        }
         uint4 u0, u1;
         unpack16(rw.x, u0.x, u0.y);
         unpack16(rw.y, u0.z, u0.w);
@@ -374,13 +410,13 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
                 if (row >= M || col >= N) continue;
                 if constexpr (SPLIT) {
                     atomicAdd((unsigned long long*)(a.acc64 + row * N + col),
-                              (unsigned long long)(int64_t)(acc[mt][nt][r] >> 4));
+                              (unsigned long long)(int64_t)(acc[mt][nt][r] >> SHIFT));
                 } else {
                     float t;
                     if constexpr (GROUP) {
                         t = mul_rn(facc[mt][nt][r], a.sa[row]);
                     } else {
-                        const int32_t iv = acc[mt][nt][r] >> 4;
+                        const int32_t iv = acc[mt][nt][r] >> SHIFT;
                         if (a.acc_out) a.acc_out[row * N + col] = iv;
                         t = (float)iv;
                         t = mul_rn(t, a.sa[row]);
@@ -922,6 +958,8 @@ int gemm_path(const GemmArgs& a)
     const bool aligned = (a.K % 32) == 0 && ((uintptr_t)a.codes % 16) == 0 &&
                          ((uintptr_t)a.wp % 16) == 0;
     const bool group = a.sw_group > 0;
+    // INT8 weights: the 128 x 128 kernel
+    if (a.w8) return a.k_chunk > 0 ? kGemmTileSplitK : kGemmTile;
     // decode-sized M: the skinny kernel (every epilogue variant but group
     // scales and K-chunks)
     if (!group && a.k_chunk == 0 && a.M >= 1 && a.M <= 64 && (a.K % 64) == 0 &&
@@ -983,12 +1021,20 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
         const unsigned gz = (unsigned)((a.K + kc - 1) / kc);
         const int64_t n = a.M * a.N;
         hipLaunchKernelGGL(fill_zero_i64, dim3(1024), dim3(256), 0, st, a.acc64, n);
-        if (aligned)
+        if (a.w8) {
+            if (aligned)
+                hipLaunchKernelGGL((w4a4_gemm_kernel<-1, true, true, true>), dim3(gx, gy, gz), dim3(256), 0,
+                                   st, a, kc);
+            else
+                hipLaunchKernelGGL((w4a4_gemm_kernel<-1, true, false, true>), dim3(gx, gy, gz), dim3(256), 0,
+                                   st, a, kc);
+        } else if (aligned) {
             hipLaunchKernelGGL((w4a4_gemm_kernel<-1, true, true>), dim3(gx, gy, gz), dim3(256), 0,
                                st, a, kc);
-        else
+        } else {
             hipLaunchKernelGGL((w4a4_gemm_kernel<-1, true, false>), dim3(gx, gy, gz), dim3(256), 0,
                                st, a, kc);
+        }
         hipLaunchKernelGGL(split_epilogue_kernel, dim3(2048), dim3(256), 0, st, a);
         return hipGetLastError();
     }
@@ -1010,6 +1056,13 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
         else if (a.sw_dtype == F16) W4A4_GROUP_LAUNCH(F16);
         else W4A4_GROUP_LAUNCH(BF16);
 #undef W4A4_GROUP_LAUNCH
+    } else if (a.w8) {
+        if (aligned_buf)
+            hipLaunchKernelGGL((w4a4_gemm_kernel<-1, false, true, true>), dim3(gx, gy, 1), dim3(256), 0,
+                               st, a, kc);
+        else
+            hipLaunchKernelGGL((w4a4_gemm_kernel<-1, false, false, true>), dim3(gx, gy, 1), dim3(256), 0,
+                               st, a, kc);
     } else {
         if (aligned_buf)
             hipLaunchKernelGGL((w4a4_gemm_kernel<-1, false, true>), dim3(gx, gy, 1), dim3(256), 0,

@@ -16,6 +16,7 @@ struct RQArgs {
     int8_t* codes;          // (M, K)
     float* scales;          // (M,)
     void* yout;             // (M, K) in dtype or nullptr
+    int qmax = 7;           // 7: INT4 codes; 127: the INT8 mode
 };
 
 // The kernel that launch_rotate_quant takes for these arguments (>= 0), or -1
@@ -45,6 +46,7 @@ struct GemmArgs {
     int32_t* acc_out;       // optional (M, N) int32
     int64_t k_chunk;        // > 0: accumulate K in chunks of this many (exact int64 combine)
     int64_t* acc64;         // workspace (M, N) int64 when k_chunk > 0
+    int w8 = 0;             // 1: wp holds INT8 weights (N, K), codes up to +-127
 };
 
 // GEMM kernels, as gemm_path names them (host-only choice, no device access)
@@ -67,5 +69,8 @@ hipError_t launch_lowrank_down(const LowRankArgs& a, hipStream_t st);
 // The kernel accumulates 16 * c * w (weights are unpacked as 16 * w, which
 // needs no per-nibble sign extension), |c| <= 7 and |w| <= 8.
 constexpr int64_t kGemmMaxK = (int64_t)2147483647 / (7 * 8 * 16) / 64 * 64;
+// The same for INT8 codes (|c| <= 127) and INT8 weights (|w| <= 128), which
+// the kernel multiplies as they are.
+constexpr int64_t kGemmMaxK8 = (int64_t)2147483647 / (127 * 128) / 64 * 64;
 
 }  // namespace w4a4

@@ -46,6 +46,28 @@ __device__ __forceinline__ int quant_code(float y, float s, float rinv)
     return (int)r;
 }
 
+// The same for the INT8 mode (|y/s| <= 127 (1 + 2^-23)): y * rinv is within
+// 2^-15 of fl(y/s), so outside a 2^-13 band around a half-integer both round
+// to the same integer.
+__device__ __forceinline__ int quant_code127(float y, float s, float rinv)
+{
+    float q = y * rinv;
+    float aq = fabsf(q);
+    float fr = aq - floorf(aq);
+    if (fabsf(fr - 0.5f) < 0x1p-13f) q = y / s;
+    if (q != q) return 0;
+    float r = rintf(q);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+template <int QMAX>
+__device__ __forceinline__ int quant_code_q(float y, float s, float rinv)
+{
+    if constexpr (QMAX == 7) return quant_code(y, s, rinv);
+    else return quant_code127(y, s, rinv);
+}
+
 // Four codes packed into one dword (code r in byte r).  quant4_fast uses
 // y * (1/s) and raises `near` when any quotient lies within 2^-17 of a
 // half-integer, where only the correctly rounded quotient may be trusted;
@@ -73,13 +95,14 @@ __device__ __forceinline__ uint32_t quant4_fast(const float (&y)[4], float rinv,
     return pack_codes(c);
 }
 
+template <int QMAX = 7>
 __device__ __forceinline__ uint32_t quant4_exact(const float (&y)[4], float s)
 {
     float c[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float q = y[i] / s;
-        const float cl = __builtin_amdgcn_fmed3f(rintf(q), -7.0f, 7.0f);
+        const float cl = __builtin_amdgcn_fmed3f(rintf(q), -(float)QMAX, (float)QMAX);
         c[i] = (q == q) ? cl : 0.0f;
     }
     return pack_codes(c);
@@ -117,6 +140,15 @@ __device__ __forceinline__ float row_scale(uint32_t absmax_bits)
 {
     float a = __uint_as_float(absmax_bits);
     float s = a / 7.0f;
+    if (s < 0x1p-126f) s = 0x1p-126f;  // NaN compares false and stays NaN
+    return s;
+}
+
+template <int QMAX>
+__device__ __forceinline__ float row_scale_q(uint32_t absmax_bits)
+{
+    float a = __uint_as_float(absmax_bits);
+    float s = a / (float)QMAX;
     if (s < 0x1p-126f) s = 0x1p-126f;  // NaN compares false and stays NaN
     return s;
 }
@@ -1356,7 +1388,7 @@ __global__ __launch_bounds__(256, TW >= 4 ? 2 : 3) void rq_wave_kernel(
 // the column-major kernel (lane group q, step ks: k = 64 q + 8 ks + e), so
 // the two give the same rotated bits.
 // -------------------------------------------------------------------------
-template <int DT, bool SMOOTH>
+template <int DT, bool SMOOTH, int QMAX = 7>
 __global__ __launch_bounds__(512) void rq_g256_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t sm,
     const float* __restrict__ rot, const uint16_t* __restrict__ smooth,
@@ -1453,11 +1485,14 @@ __global__ __launch_bounds__(512) void rq_g256_kernel(
         __syncthreads();
         const uint32_t* wm = wmax[par] + 4 * wr;
         const uint32_t v = max(max(wm[0], wm[1]), max(wm[2], wm[3]));
-        const float sv = row_scale(v);
+        const float sv = row_scale_q<QMAX>(v);
         const float ri = 1.0f / sv;
         if (wt == 0 && lane == 0 && row < M) scales[row] = sv;
         // quantize: exact division only where a quotient is near a tie or the
-        // scale is not finite
+        // scale is not finite (|y * ri - fl(y / s)| <= 2 QMAX 2^-24, so the
+        // band is 2^-17 for INT4 codes and 2^-13 in the INT8 mode)
+        constexpr float kBand = QMAX == 7 ? 0x1p-17f : 0x1p-13f;
+        constexpr float kQ = (float)QMAX;
         const bool fin = fabsf(sv) < 3.0e38f;
         int8_t* cb = codes + (live ? row : 0) * K + gr * GP;
 #pragma unroll
@@ -1467,15 +1502,15 @@ __global__ __launch_bounds__(512) void rq_g256_kernel(
             for (int r = 0; r < 4; ++r) yy[r] = h_to_f32<DT>((uint16_t)(yp[ct][r >> 1] >> (16 * (r & 1))));
             uint32_t pk;
             if (!fin) {
-                pk = quant4_exact(yy, sv);
+                pk = quant4_exact<QMAX>(yy, sv);
             } else {
                 float t[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float qv = yy[r] * ri;
-                    t[r] = __builtin_amdgcn_fmed3f(qv, -7.0f, 7.0f) + kRoundMagic;
-                    const bool nr = fabsf(qv - (t[r] - kRoundMagic)) > 0.5f - 0x1p-17f;
-                    if (__any(nr)) t[r] = __builtin_amdgcn_fmed3f(yy[r] / sv, -7.0f, 7.0f) + kRoundMagic;
+                    t[r] = __builtin_amdgcn_fmed3f(qv, -kQ, kQ) + kRoundMagic;
+                    const bool nr = fabsf(qv - (t[r] - kRoundMagic)) > 0.5f - kBand;
+                    if (__any(nr)) t[r] = __builtin_amdgcn_fmed3f(yy[r] / sv, -kQ, kQ) + kRoundMagic;
                 }
                 pk = pack4_magic(t[0], t[1], t[2], t[3]);
             }
@@ -1489,7 +1524,7 @@ __global__ __launch_bounds__(512) void rq_g256_kernel(
     }
 }
 
-template <int DT>
+template <int DT, int QMAX = 7>
 static hipError_t launch_g256_dt(const RQArgs& a, hipStream_t st)
 {
     static int n_cu = 0;
@@ -1504,10 +1539,10 @@ static hipError_t launch_g256_dt(const RQArgs& a, hipStream_t st)
     const int64_t pairs = (a.M + 1) / 2;
     const int64_t grid = pairs < n_cu ? pairs : n_cu;   // one workgroup per CU (128 KB of LDS)
     if (a.smooth)
-        hipLaunchKernelGGL((rq_g256_kernel<DT, true>), dim3((unsigned)grid), dim3(512), 0, st, (const uint16_t*)a.x,
+        hipLaunchKernelGGL((rq_g256_kernel<DT, true, QMAX>), dim3((unsigned)grid), dim3(512), 0, st, (const uint16_t*)a.x,
                            a.M, a.K, a.sm, a.rot, (const uint16_t*)a.smooth, a.codes, a.scales, (uint16_t*)a.yout);
     else
-        hipLaunchKernelGGL((rq_g256_kernel<DT, false>), dim3((unsigned)grid), dim3(512), 0, st, (const uint16_t*)a.x,
+        hipLaunchKernelGGL((rq_g256_kernel<DT, false, QMAX>), dim3((unsigned)grid), dim3(512), 0, st, (const uint16_t*)a.x,
                            a.M, a.K, a.sm, a.rot, (const uint16_t*)a.smooth, a.codes, a.scales, (uint16_t*)a.yout);
     return hipGetLastError();
 }
@@ -1562,7 +1597,7 @@ __device__ __forceinline__ float round_f64_to_T(double v)
     if constexpr (DT == F32) return (float)v;
     else return round_T<DT>(f64_to_f32_odd(v));
 }
-template <int DT, bool ROT, bool SMOOTH>
+template <int DT, bool ROT, bool SMOOTH, int QMAX = 7>
 __global__ __launch_bounds__(256) void rq_generic_kernel(
     const void* __restrict__ x, int64_t M, int64_t K, int64_t sm, int64_t sk,
     const float* __restrict__ rot, int g, const void* __restrict__ smooth,
@@ -1598,12 +1633,12 @@ __global__ __launch_bounds__(256) void rq_generic_kernel(
     if ((tid & 63) == 0) red[tid >> 6] = mx;
     __syncthreads();
     mx = max(max(red[0], red[1]), max(red[2], red[3]));
-    const float s = row_scale(mx);
+    const float s = row_scale_q<QMAX>(mx);
     const float ri = 1.0f / s;
     if (tid == 0) scales[m] = s;
     for (int64_t k = tid; k < K; k += 256) {
         float y = ycalc(k);
-        codes[m * K + k] = (int8_t)quant_code(y, s, ri);
+        codes[m * K + k] = (int8_t)quant_code_q<QMAX>(y, s, ri);
         if (yout) {
             if constexpr (DT == F32) ((float*)yout)[m * K + k] = y;
             else ((uint16_t*)yout)[m * K + k] = f32_to_h<DT>(y);
@@ -1668,7 +1703,7 @@ static hipError_t launch_mfma_dt(const RQArgs& a, int GP, bool contig, hipStream
     }
 }
 
-template <int DT>
+template <int DT, int QMAX = 7>
 static hipError_t launch_generic_dt(const RQArgs& a, hipStream_t st)
 {
     const size_t lds = (size_t)a.K * 4;
@@ -1684,10 +1719,10 @@ static hipError_t launch_generic_dt(const RQArgs& a, hipStream_t st)
                            a.sk, a.rot, a.g, a.smooth, a.codes, a.scales, a.yout);
         return hipGetLastError();
     };
-    if (rot && sm) return go(rq_generic_kernel<DT, true, true>);
-    if (rot) return go(rq_generic_kernel<DT, true, false>);
-    if (sm) return go(rq_generic_kernel<DT, false, true>);
-    return go(rq_generic_kernel<DT, false, false>);
+    if (rot && sm) return go(rq_generic_kernel<DT, true, true, QMAX>);
+    if (rot) return go(rq_generic_kernel<DT, true, false, QMAX>);
+    if (sm) return go(rq_generic_kernel<DT, false, true, QMAX>);
+    return go(rq_generic_kernel<DT, false, false, QMAX>);
 }
 
 
@@ -1853,6 +1888,14 @@ static bool colmajor_ok(const RQArgs& a)
 // when none does (a row too long for the generic kernel's LDS buffer).
 int rotate_quant_path(const RQArgs& a)
 {
+    // INT8 mode: the row-streaming and g = 256 kernels, else the generic one
+    if (a.qmax == 127) {
+        if (g256_ok(a)) return 5;
+        if (row_kernel_ok(a)) return 6;
+        if ((size_t)a.K * 4 > 160 * 1024) return -1;  // row does not fit in LDS
+        return 0;
+    }
+    if (a.qmax != 7) return -1;
     // MFMA path: 16-bit activations, group width 16..256, K a multiple of
     // the MFMA group width, 16-byte aligned operands for the vector loads.
     int GP = 0;
@@ -1904,6 +1947,19 @@ hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path)
     const bool bf = a.dtype == BF16;
     const int GP = a.rot ? (a.g < 32 ? 32 : a.g) : 32;
     const bool contig = a.sk == 1 && (a.sm % 8) == 0 && ((uintptr_t)a.x % 16) == 0;
+    if (a.qmax == 127) {
+        switch (p) {
+        case 5: return bf ? launch_g256_dt<BF16, 127>(a, st) : launch_g256_dt<F16, 127>(a, st);
+        case 6: return launch_rotate_quant_row(a, st);
+        case 0:
+            switch (a.dtype) {
+            case F32: return launch_generic_dt<F32, 127>(a, st);
+            case F16: return launch_generic_dt<F16, 127>(a, st);
+            default: return launch_generic_dt<BF16, 127>(a, st);
+            }
+        default: return hipErrorNotSupported;
+        }
+    }
     switch (p) {
     case 4: return bf ? launch_colmajor_dt<BF16>(a, st) : launch_colmajor_dt<F16>(a, st);
     case 5: return bf ? launch_g256_dt<BF16>(a, st) : launch_g256_dt<F16>(a, st);

@@ -138,15 +138,16 @@ __device__ __forceinline__ uint32_t pack_bytes(uint32_t c0, uint32_t c1, uint32_
 }
 
 // correctly rounded code for a finite or non-finite quotient (NaN -> 0)
+template <int QMAX>
 __device__ __forceinline__ int code_of_quotient(float qv)
 {
     if (qv != qv) return 0;
-    return (int)__builtin_amdgcn_fmed3f(rintf(qv), -7.0f, 7.0f);
+    return (int)__builtin_amdgcn_fmed3f(rintf(qv), -(float)QMAX, (float)QMAX);
 }
 
 }  // namespace
 
-template <int DT, bool SMOOTH, bool YOUT, int TW, int PF>
+template <int DT, bool SMOOTH, bool YOUT, int TW, int PF, int QMAX>
 __global__ __launch_bounds__(256, 2) void rq_row_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t sm,
     const float* __restrict__ rot, const uint16_t* __restrict__ smooth,
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void rq_row_kernel(
         // row scale: IEEE a / 7, clamped up to the smallest normal
         const uint32_t a16 = wave_max_u32(max((uint32_t)amax[0], (uint32_t)amax[1]));
         const float a = DT == BF16 ? __uint_as_float(a16 << 16) : f16_to_f32((uint16_t)a16);
-        float s = a / 7.0f;
+        float s = a / (float)QMAX;
         if (s < 0x1p-126f) s = 0x1p-126f;  // NaN compares false and stays NaN
         if (lane == 0 && r < M) scales[r] = s;
         const bool finite = fabsf(s) < 3.0e38f;
@@ -296,7 +297,37 @@ __global__ __launch_bounds__(256, 2) void rq_row_kernel(
         const uint32_t sig = DT == BF16 ? ((a16 >> 7) & 0xffu ? (a16 & 0x7fu) | 0x80u : a16 & 0x7fu)
                                         : ((a16 >> 10) & 0x1fu ? (a16 & 0x3ffu) | 0x400u : a16 & 0x3ffu);
         const bool clamped = s == 0x1p-126f;
-        if (__builtin_expect(finite && !clamped && sig % 7u != 0u, 1)) {
+        if constexpr (QMAX == 127) {
+            // INT8 mode: one rounding per element (|y / s| <= 127 (1 + 2^-23),
+            // so y * (1/s) is within 2^-15 of fl(y / s)); a quotient within
+            // 2^-13 of a half-integer sends its group of four to the IEEE
+            // division, as does a scale that is not finite
+            const float rinv = 1.0f / s;
+#pragma unroll
+            for (int u = 0; u < TW; ++u) {
+                uint32_t P[CT];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    uint32_t c[4];
+                    bool near = !finite;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float y = unpack_half<DT>(yp[u][ct][i >> 1], i & 1);
+                        const float t = __builtin_fmaf(y, rinv, kMagic);
+                        const float res = __builtin_fmaf(y, rinv, -(t - kMagic));
+                        near |= fabsf(res) > 0.5f - 0x1p-13f;
+                        c[i] = __float_as_uint(t);
+                    }
+                    if (__any(near)) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            c[i] = (uint32_t)code_of_quotient<127>(unpack_half<DT>(yp[u][ct][i >> 1], i & 1) / s);
+                    }
+                    P[ct] = pack_bytes(c[0], c[1], c[2], c[3]);
+                }
+                store_tile(u, P);
+            }
+        } else if (__builtin_expect(finite && !clamped && sig % 7u != 0u, 1)) {
             // one rounding per element: of the two bracketing multipliers,
             // the one that takes the k = 3 tie the quantizer's way gives every
             // code (the two agree on every element that is not a tie)
@@ -346,7 +377,7 @@ __global__ __launch_bounds__(256, 2) void rq_row_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float y = unpack_half<DT>(yp[u][ct][i >> 1], i & 1);
-                        w |= (uint32_t)(code_of_quotient(y / s) & 0xff) << (8 * i);
+                        w |= (uint32_t)(code_of_quotient<QMAX>(y / s) & 0xff) << (8 * i);
                     }
                     P[ct] = w;
                 }
@@ -389,10 +420,10 @@ bool row_kernel_ok(const RQArgs& a)
 // registers cost a wave per SIMD)
 constexpr int kRowPF = 1;
 
-template <int DT, bool SMOOTH, bool YOUT, int TW>
+template <int DT, bool SMOOTH, bool YOUT, int TW, int QMAX>
 static hipError_t launch_row_t(const RQArgs& a, hipStream_t st)
 {
-    auto kern = rq_row_kernel<DT, SMOOTH, YOUT, TW, kRowPF>;
+    auto kern = rq_row_kernel<DT, SMOOTH, YOUT, TW, kRowPF, QMAX>;
     static int per_cu = 0, n_cu = 0;
     if (per_cu == 0) {
         int dev = 0;
@@ -413,24 +444,25 @@ static hipError_t launch_row_t(const RQArgs& a, hipStream_t st)
     return hipGetLastError();
 }
 
-template <int DT, bool SMOOTH, bool YOUT>
+template <int DT, bool SMOOTH, bool YOUT, int QMAX>
 static hipError_t launch_row_tw(const RQArgs& a, hipStream_t st)
 {
     const int64_t gpr = a.K / 64;
-    return gpr > 32 ? launch_row_t<DT, SMOOTH, YOUT, 4>(a, st) : launch_row_t<DT, SMOOTH, YOUT, 2>(a, st);
+    return gpr > 32 ? launch_row_t<DT, SMOOTH, YOUT, 4, QMAX>(a, st) : launch_row_t<DT, SMOOTH, YOUT, 2, QMAX>(a, st);
 }
 
-template <int DT>
+template <int DT, int QMAX>
 static hipError_t launch_row_dt(const RQArgs& a, hipStream_t st)
 {
     if (a.smooth)
-        return a.yout ? launch_row_tw<DT, true, true>(a, st) : launch_row_tw<DT, true, false>(a, st);
-    return a.yout ? launch_row_tw<DT, false, true>(a, st) : launch_row_tw<DT, false, false>(a, st);
+        return a.yout ? launch_row_tw<DT, true, true, QMAX>(a, st) : launch_row_tw<DT, true, false, QMAX>(a, st);
+    return a.yout ? launch_row_tw<DT, false, true, QMAX>(a, st) : launch_row_tw<DT, false, false, QMAX>(a, st);
 }
 
 hipError_t launch_rotate_quant_row(const RQArgs& a, hipStream_t st)
 {
-    return a.dtype == BF16 ? launch_row_dt<BF16>(a, st) : launch_row_dt<F16>(a, st);
+    if (a.qmax == 127) return a.dtype == BF16 ? launch_row_dt<BF16, 127>(a, st) : launch_row_dt<F16, 127>(a, st);
+    return a.dtype == BF16 ? launch_row_dt<BF16, 7>(a, st) : launch_row_dt<F16, 7>(a, st);
 }
 
 }  // namespace w4a4

@@ -140,6 +140,49 @@ int w4a4_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride
 size_t w4a4_linear_workspace_size(int64_t M, int64_t K, int64_t N, int32_t rank);
 
 /*
+ * INT8 mode and the dynamic INT8 ConvRot linear ("[Feat][Ascend] Add fused
+ * RotateQuant backend", section "What this PR does / why we need it": the
+ * fused block rotation + per-row dynamic INT8 quantization that feeds the
+ * ConvRot INT8 linear; positive scales).  Same steps as above with
+ * qmax = 127: s = max(absmax / 127, 2^-126), codes clamp(rne(y / s), -127,
+ * 127) in int8 (-128 never produced).  K may be odd.
+ *
+ * w8a8_rotate_quant_rowwise: the arguments of w4a4_rotate_quant_rowwise.
+ *   Contiguous 16-bit rows with g = 64 (K <= 4096) or g = 256 (K <= 16384)
+ *   take fast kernels; other layouts the exact one-row-per-workgroup kernel
+ *   (K <= 40960, else W4A4_UNSUPPORTED).
+ * w8a8_gemm_from_codes: exact INT32 product of INT8 codes (M, K) with INT8
+ *   weights w (N, K) row-major (any int8 value), then the E-B epilogue with
+ *   per-channel weight scales (N,) and optional bias (N,).  When
+ *   127 * 128 * K could overflow INT32 the sums are taken in K-chunks and
+ *   combined exactly in int64 in a workspace of
+ *   w8a8_gemm_workspace_size(M, N, K) bytes (0 otherwise).
+ * w8a8_linear: rotate-quant (INT8) then the GEMM, enqueued back to back;
+ *   bias in x_dtype; workspace of w8a8_linear_workspace_size(M, K, N) bytes.
+ * Return codes and ownership as for the W4A4 calls; nothing is allocated.
+ */
+int w8a8_rotate_quant_rowwise(const void* x, int x_dtype, int64_t M, int64_t K,
+                              int64_t stride_m, int64_t stride_k, const float* rot, int32_t g,
+                              const void* smooth, int8_t* codes, float* scales,
+                              void* rotated_out, void* stream);
+int w8a8_gemm_from_codes(const int8_t* codes, const float* scales, int64_t M, int64_t K,
+                         const int8_t* w, int64_t N, const void* w_scale, int w_scale_dtype,
+                         const void* bias, int bias_dtype, void* out, int out_dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+size_t w8a8_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+int w8a8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                int64_t stride_k, const float* rot, int32_t g, const void* smooth,
+                const int8_t* w, int64_t N, const void* w_scale, int w_scale_dtype,
+                const void* bias, void* out, int out_dtype, void* workspace,
+                size_t workspace_bytes, void* stream);
+size_t w8a8_linear_workspace_size(int64_t M, int64_t K, int64_t N);
+/* host-only: the kernel w8a8_rotate_quant_rowwise would take (ids as for
+ * w4a4_rotate_quant_plan below: 0 generic, 5 g = 256, 6 row) */
+int w8a8_rotate_quant_plan(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                           int64_t stride_k, const float* rot, int32_t g, const void* smooth,
+                           const int8_t* codes, const void* rotated_out, int* kernel);
+
+/*
  * w4a4_linear for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same arguments without the workspace, and the same kernels, which work
