@@ -26,7 +26,8 @@ p90; plus the average over one event pair around the back-to-back launches
 
 The line also carries the other four workloads (wide-K transposed-view fp16,
 decode-like M=32, tiny fp32, large-K with smoothing, per-64-group scales and a
-rank-32 term), each as a step and per kernel.
+rank-32 term), each as a step and per kernel, and the INT8 mode (qmax = 127,
+INT8 weights) on the prefill and wide-K shapes.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload prefill]
                        [--no-cpu] [--no-extra] [--copy-calibration]
@@ -343,6 +344,142 @@ def measure(name, steps, warmup, torch, np, w4, workloads, cpu=True):
     return w, inp, res
 
 
+def measure_int8(name, steps, warmup, torch, np, w4, workloads, cpu=True):
+    """The INT8 mode on the workload's shape: per-token INT8 codes (qmax =
+    127) and the dynamic INT8 linear with (N, K) INT8 weights, per-channel
+    weight scales in the workload's scale dtype.  The activations are the
+    workload's values in contiguous rows.  Times the w8a8_linear step, the
+    INT8 rotate-quant alone and the INT8 GEMM alone (same protocol as the
+    W4A4 legs); the CPU leg checks sampled rows against the oracle's INT8
+    linear first."""
+    from bit_quantized_linear_rotate_amd import _binding as b
+    w = workloads.WORKLOADS[name]
+    inp = workloads.generate(w)
+    M, K, N, g = w.M, w.K, w.N, w.g
+    rng = np.random.default_rng(w.seed + 77)
+    w8 = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    sw = workloads.f32_to_storage(rng.uniform(0.0005, 0.002, size=N).astype(np.float32), w.sw_dtype)
+    x_host = np.ascontiguousarray(inp["x"])
+
+    def d(a, dt=None):
+        a = np.ascontiguousarray(a)
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+    base = dict(x=d(x_host, w.dtype), rot=torch.from_numpy(inp["rot"].astype(np.float32)).cuda(),
+                w8=d(w8), w_scale=d(sw, w.sw_dtype), bias=d(inp["bias"], w.dtype) if w.bias else None)
+    sets = [base] + [{k: (v.clone() if v is not None and k != "rot" else v) for k, v in base.items()}
+                     for _ in range(3)]
+    xdt = base["x"].dtype
+    outs = [torch.empty((M, N), dtype=xdt, device="cuda") for _ in sets]
+    need = w4.w8a8_linear_workspace_size(M, K, N)
+    wss = [torch.empty((need,), dtype=torch.uint8, device="cuda") for _ in sets]
+    rq_kernel = w4.w8a8_rotate_quant_plan(base["x"], base["rot"], g)
+    lib = w4.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    xc, sc_, oc = _dtcode(torch, base["x"]), _dtcode(torch, base["w_scale"]), _dtcode(torch, outs[0])
+
+    def step(i):
+        s = sets[i % 4]
+        x, b_ = s["x"], s["bias"]
+        rc = lib.w8a8_linear(x.data_ptr(), xc, M, K, x.stride(0), 1, s["rot"].data_ptr(), g, None,
+                             s["w8"].data_ptr(), N, s["w_scale"].data_ptr(), sc_,
+                             b_.data_ptr() if b_ is not None else None, outs[i % 4].data_ptr(), oc,
+                             wss[i % 4].data_ptr(), need, stream)
+        if rc:
+            b._check(rc, "w8a8_linear")
+
+    qbufs = [(torch.empty((M, K), dtype=torch.int8, device="cuda"),
+              torch.empty((M,), dtype=torch.float32, device="cuda")) for _ in sets]
+
+    def rq(i):
+        s = sets[i % 4]
+        c, sc = qbufs[i % 4]
+        x = s["x"]
+        rc = lib.w8a8_rotate_quant_rowwise(x.data_ptr(), xc, M, K, x.stride(0), 1, s["rot"].data_ptr(), g,
+                                           None, c.data_ptr(), sc.data_ptr(), None, stream)
+        if rc:
+            b._check(rc, "w8a8_rotate_quant_rowwise")
+
+    assert w4.w8a8_gemm_workspace_size(M, N, K) == 0
+
+    def gemm(i):
+        s = sets[i % 4]
+        c, sc = qbufs[i % 4]
+        b_ = s["bias"]
+        rc = lib.w8a8_gemm_from_codes(c.data_ptr(), sc.data_ptr(), M, K, s["w8"].data_ptr(), N,
+                                      s["w_scale"].data_ptr(), sc_, b_.data_ptr() if b_ is not None else None,
+                                      _dtcode(torch, b_) if b_ is not None else 0, outs[i % 4].data_ptr(), oc,
+                                      None, 0, stream)
+        if rc:
+            b._check(rc, "w8a8_gemm_from_codes")
+
+    par = None
+    if cpu:
+        import oracle
+        step(0)
+        rq(0)
+        torch.cuda.synchronize()
+        rows = np.sort(np.random.default_rng(7).choice(M, 32, replace=False))
+
+        def host(t):
+            t = t.detach().cpu().contiguous()
+            return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+        out, gc, gs = host(outs[0])[rows], host(qbufs[0][0])[rows], host(qbufs[0][1])[rows]
+        ref = oracle.linear_int8(x_host, inp["rot"], g, w8, sw, w.dtype, w.sw_dtype,
+                                 bias=inp["bias"] if w.bias else None, rows=rows)
+        same = gs.view(np.uint32) == ref["scales"].view(np.uint32)
+        dc = np.abs(gc.astype(np.int32) - ref["codes"])
+        exact = same & (dc.max(axis=1) == 0)
+        ok = dc.max(initial=0) <= 1 and np.array_equal(out[exact].view(np.uint16),
+                                                      ref["out"][exact].view(np.uint16))
+        par = {"rows": int(len(rows)), "cols": int(N), "code_flips": int((dc > 0).sum()),
+               "rows_other_scale": int((~same).sum()), "rows_bit_exact": int(exact.sum()),
+               "rule": "codes within 1; outputs of rows whose codes match bit-exact", "pass": bool(ok)}
+        if not ok:
+            raise SystemExit(f"INT8 parity check failed on {name}: {par}")
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(steps):
+        step(i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    nk = max(steps, MIN_KERNEL_LAUNCHES)
+    for i in range(warmup):
+        rq(i)
+    t_rq = _time_each(rq, nk, torch, np)
+    for i in range(warmup):
+        gemm(i)
+    t_gemm = _time_each(gemm, nk, torch, np)
+    es = base["x"].element_size()
+    rq_bytes = M * K * es + M * K + 4 * M + 4 * g * g
+    ops = 2.0 * M * N * K
+    gemm_bytes = (M * K + N * K + 4 * M + N * base["w_scale"].element_size()
+                  + (N * es if w.bias else 0) + M * N * outs[0].element_size())
+    ms_rq, ms_gemm = t_rq["ms_median"], t_gemm["ms_median"]
+    res = {"workload": f"INT8 mode, {name} shape: M={M} K={K} N={N} g={g} {w.dtype}, contiguous rows, "
+                       f"INT8 weights (N, K), per-channel {w.sw_dtype} weight scales"
+                       + (", bias" if w.bias else ""),
+           "ms_per_step": ms_step, "tops": ops / (ms_step * 1e-3) / 1e12,
+           "rotate_quant": {"kernel": RQ_NAMES.get(rq_kernel, rq_kernel) + " (qmax 127)", **t_rq,
+                            "GB_s": rq_bytes / (ms_rq * 1e-3) / 1e9,
+                            "frac_hbm": rq_bytes / (ms_rq * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                            "algorithmic_bytes": rq_bytes},
+           "gemm": {"kernel": "w4a4_gemm_kernel (INT8 weights)", **t_gemm,
+                    "TOPS": ops / (ms_gemm * 1e-3) / 1e12,
+                    "frac_int8": ops / (ms_gemm * 1e-3) / 1e12 / INT8_PEAK_TOPS, "ops": ops,
+                    "GB_s": gemm_bytes / (ms_gemm * 1e-3) / 1e9, "algorithmic_bytes": gemm_bytes}}
+    if par is not None:
+        res["parity"] = par
+    return res
+
+
 def stream_ceiling(w, steps, torch, np):
     """The HBM ceiling for rotate-quant's traffic on this device: a plain
     streaming kernel of this repository (bit_quantized_linear_rotate_amd/
@@ -630,6 +767,11 @@ def main():
             _, _, extras[name] = measure(name, max(10, args.steps // 2), args.warmup, torch, np, w4,
                                          workloads, cpu=cpu)
             print(f"# {name}: {extras[name]['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+        for name in ("prefill", "widek"):
+            extras["int8_" + name] = measure_int8(name, max(10, args.steps // 2), args.warmup, torch, np, w4,
+                                                  workloads, cpu=cpu)
+            print(f"# int8 {name}: {extras['int8_' + name]['ms_per_step']:.4f} ms/step", file=sys.stderr,
+                  flush=True)
     ceiling = stream_ceiling(w, args.steps, torch, np) if w.dtype == "bf16" else None
     g = main_res["gemm"]
     rq = main_res["rotate_quant"]

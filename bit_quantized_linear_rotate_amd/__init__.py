@@ -23,5 +23,6 @@ from ._binding import (  # noqa: F401
     w8a8_linear,
     w8a8_linear_workspace_size,
     w8a8_rotate_quant_plan,
+    w8a8_gemm_plan,
     w8a8_rotate_quant_rowwise,
 )

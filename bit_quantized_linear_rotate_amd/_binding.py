@@ -48,6 +48,7 @@ _SIGNATURES = {
     "w8a8_linear_workspace_size": ([_i64, _i64, _i64], _sz),
     "w8a8_rotate_quant_plan": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp,
                                 ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
+    "w8a8_gemm_plan": ([_vp, _i64, _i64, _vp, _i64, _vp, ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
     "w4a4_linear_noalloc": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _i64,
                              _vp, ctypes.c_int, _i32, _vp, _vp, _vp, _i32, _vp, ctypes.c_int, _vp],
                             ctypes.c_int),
@@ -449,6 +450,15 @@ def w8a8_rotate_quant_plan(x: torch.Tensor, rot: Optional[torch.Tensor], g: int,
 
 def w8a8_gemm_workspace_size(M: int, N: int, K: int) -> int:
     return int(lib().w8a8_gemm_workspace_size(M, N, K))
+
+
+def w8a8_gemm_plan(M: int, K: int, N: int) -> str:
+    """Name of the GEMM kernel w8a8_gemm_from_codes (or w8a8_linear) would
+    launch for operands the binding allocates (host-only; nothing runs)."""
+    k = ctypes.c_int(-1)
+    rc = lib().w8a8_gemm_plan(_ALIGNED, M, K, _ALIGNED, N, _ALIGNED, ctypes.byref(k))
+    _check(rc, "w8a8_gemm_plan")
+    return GEMM_KERNELS.get(k.value, "none")
 
 
 def w8a8_linear_workspace_size(M: int, K: int, N: int) -> int:

@@ -398,6 +398,17 @@ int w8a8_gemm_from_codes(const int8_t* codes, const float* scales, int64_t M, in
     return W4A4_OK;
 }
 
+int w8a8_gemm_plan(const int8_t* codes, int64_t M, int64_t K, const int8_t* w, int64_t N,
+                   const void* out, int* kernel)
+{
+    if (M < 0 || K < 0 || N < 0) return fail(W4A4_INVALID, "negative size");
+    GemmArgs a{codes, nullptr, M, K, N, (const uint8_t*)w, nullptr, W4A4_F32, 0,
+               nullptr, 0, nullptr, nullptr, 0, 0, (void*)out, W4A4_F32, nullptr, guard_chunk8(K), nullptr};
+    a.w8 = 1;
+    if (kernel) *kernel = (M > 0 && N > 0) ? gemm_path(a) : -1;
+    return W4A4_OK;
+}
+
 size_t w8a8_linear_workspace_size(int64_t M, int64_t K, int64_t N)
 {
     if (M <= 0) return 0;

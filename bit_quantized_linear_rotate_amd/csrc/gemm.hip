@@ -490,15 +490,30 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 // Lane (j, q) covers k = q*32 .. q*32+31 of a step: k-substep t uses
 // k = q*32 + t*16 .. +15 for both operands (low / high half of the lane's 16
 // packed weight bytes).
+//
+// INT8 weights (W8) take the same kernel with K advancing 64 per step: codes
+// and weights then both keep 64-byte rows (16 KB each per stage, 32 KB
+// slots), 16-byte chunk c of row r at c ^ r3_swz8(r) (with the lane pairing
+// above, the 16 lanes of every read cycle hit 16 distinct bank groups), one
+// k-substep of 16 bytes per lane, the weights used as they are (no unpack, no
+// factor 16), and the epilogue in an LDS area of its own after the three
+// slots (an fp32 epilogue does not fit in a 32 KB slot).
 // -------------------------------------------------------------------------
 constexpr int R3_BK = 128;
-constexpr int R3_ASTAGE = BBM * R3_BK;       // 32 KB of codes
-constexpr int R3_WSTAGE = BBN * R3_BK / 2;   // 16 KB of packed weights
-constexpr int R3_SLOT = R3_ASTAGE + R3_WSTAGE;
 constexpr int R3_WAVES = 8;
 constexpr int R3_LOADERS = 4;                             // waves 0-3 issue every operand load
-constexpr int R3_ALOADS = R3_ASTAGE / 1024 / R3_LOADERS;  // 1 KB per load: 8 per loader wave
-constexpr int R3_WLOADS = R3_WSTAGE / 1024 / R3_LOADERS;  // 4 per loader wave
+// per-variant stage geometry (W8: INT8 weights)
+template <bool W8> struct R3Geo {
+    static constexpr int BK = W8 ? 64 : R3_BK;                    // K per step
+    static constexpr int ASTAGE = BBM * BK;                       // codes: 32 KB / 16 KB
+    static constexpr int WSTAGE = W8 ? BBN * BK : BBN * BK / 2;   // weights: 16 KB either way
+    static constexpr int SLOT = ASTAGE + WSTAGE;
+    static constexpr int ALOADS = ASTAGE / 1024 / R3_LOADERS;     // 1 KB per load: 8 / 4 per loader
+    static constexpr int WLOADS = WSTAGE / 1024 / R3_LOADERS;     // 4 per loader
+    static constexpr int LPS = ALOADS + WLOADS;                   // loads per stage per loader
+    static constexpr int RPL = 1024 / BK;                         // code rows per load
+};
+constexpr int R3_SLOT = R3Geo<false>::SLOT;
 // epilogue strip (16 output rows x 64 columns of one wave) row stride in
 // bytes: 64 values + 16 bytes, so that the four 16-lane groups of a 2- or
 // 4-byte strip write hit distinct banks and 16-byte reads stay aligned
@@ -514,6 +529,11 @@ template <int ODT> constexpr int r3_stores() { return 8 * (16 * 64 * (ODT == F32
 // s_waitcnt immediate for vmcnt(n), expcnt and lgkmcnt not waited on (gfx9)
 constexpr int r3_vmcnt(int n) { return ((n >> 4) << 14) | 0x0f70 | (n & 15); }
 static_assert(r3_epi_bytes<F32>() <= R3_SLOT && r3_epi_bytes<BF16>() <= R3_SLOT, "epilogue must fit in one slot");
+template <int ODT, bool W8> constexpr int r3_lds_bytes()
+{
+    return 3 * R3Geo<W8>::SLOT + (W8 ? r3_epi_bytes<ODT>() : 0);
+}
+static_assert(r3_lds_bytes<F32, true>() <= 160 * 1024 && r3_lds_bytes<F32, false>() <= 160 * 1024, "LDS");
 
 __device__ __forceinline__ v4i r3_half(v4u p, int t)
 {
@@ -546,12 +566,15 @@ __device__ __forceinline__ float r3_scalar_value(uint32_t w, int dt, int64_t i)
 
 // chunk permutation of code row r in LDS (depends on bits 1 and 2 of r)
 __device__ __forceinline__ int r3_swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 1); }
+// the same for the 64-byte rows of the INT8 variant: 0, 3, 2, 1 by bits 2-3
+__device__ __forceinline__ int r3_swz8(int r) { return (4 - ((r >> 2) & 3)) & 3; }
 
 struct R3Tile {
     int64_t m0, n0;
     __amdgpu_buffer_rsrc_t ra, rw;
 };
 
+template <bool W8>
 __device__ __forceinline__ R3Tile r3_tile(const GemmArgs& a, int t, int ntiles, int tiles_n)
 {
     R3Tile r;
@@ -573,15 +596,18 @@ __device__ __forceinline__ R3Tile r3_tile(const GemmArgs& a, int t, int ntiles, 
     r.m0 = (int64_t)(first_m + in_g % gsize) * BBM;
     r.n0 = (int64_t)(in_g / gsize) * BBN;
     r.ra = make_rsrc(a.codes + r.m0 * a.K, (uint64_t)(a.M - r.m0) * a.K);
-    r.rw = make_rsrc(a.wp + r.n0 * (a.K >> 1), (uint64_t)(a.N - r.n0) * (a.K >> 1));
+    const int64_t wrow = W8 ? a.K : (a.K >> 1);   // weight bytes per column
+    r.rw = make_rsrc(a.wp + r.n0 * wrow, (uint64_t)(a.N - r.n0) * wrow);
     return r;
 }
 
-template <int ODT>
+template <int ODT, bool W8 = false>
 __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int tiles_m, int tiles_n)
 {
-    __shared__ __align__(16) int8_t smem[3 * R3_SLOT];
-    static_assert(R3_ALOADS + R3_WLOADS == 12, "vmcnt immediates below assume 12 loads per stage");
+    using G3 = R3Geo<W8>;
+    constexpr int BK = G3::BK, SLOT = G3::SLOT, ASTAGE = G3::ASTAGE, LPS = G3::LPS, RPL = G3::RPL;
+    constexpr int SHIFT = W8 ? 0 : 4;   // INT4 weights are unpacked as 16 * w
+    __shared__ __align__(16) int8_t smem[r3_lds_bytes<ODT, W8>()];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -590,7 +616,7 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
 
     const int ntiles = tiles_m * tiles_n;
     const int64_t K = a.K, M = a.M, N = a.N;
-    const int nsteps = (int)(K / R3_BK);
+    const int nsteps = (int)(K / BK);
     int t = blockIdx.x;
     const int G = gridDim.x;
 
@@ -600,42 +626,61 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
     // drain the next tile's stages).
     const bool loader = wave < R3_LOADERS;
     const int lw = wave & (R3_LOADERS - 1);
-    // codes: loader lw fills tile rows lw*64 .. lw*64+63, eight rows per
-    // load; lane l writes chunk (l & 7) of row (l >> 3), i.e. logical chunk
-    // (l & 7) ^ r3_swz(row) (the row's low three bits are l >> 3).
-    const int a_vo = (int)((lane >> 3) * K + (((lane & 7) ^ r3_swz(lane >> 3)) * 16));
-    const int a_row8 = (int)(8 * K);
+    // codes: loader lw fills tile rows lw*64 .. lw*64+63, RPL rows per
+    // load; lane l writes chunk (l % CPR) of row (l / CPR), i.e. logical
+    // chunk (l % CPR) ^ swizzle(row) (the row's low bits are l / CPR).
+    constexpr int CPR = BK / 16;   // 16-byte chunks per code row
+    const int arow = lane / CPR;
+    const int a_vo = (int)(arow * K + (((lane % CPR) ^ (W8 ? r3_swz8(arow) : r3_swz(arow))) * 16));
+    const int a_rowl = (int)(RPL * K);
     // weights: loader lw fills tile columns lw*64 .. lw*64+63, sixteen per
     // load; lane l writes chunk (l & 3) of column (l >> 2).
-    const int w_vo = (int)((lw * 64 + (lane >> 2)) * (K >> 1) + (((lane & 3) ^ ((lane >> 3) & 3)) * 16));
-    const int w_col16 = (int)(16 * (K >> 1));
+    const int64_t wrow = W8 ? K : (K >> 1);
+    const int wsw = W8 ? r3_swz8(lane >> 2) : ((lane >> 3) & 3);
+    const int w_vo = (int)((lw * 64 + (lane >> 2)) * wrow + (((lane & 3) ^ wsw) * 16));
+    const int w_col16 = (int)(16 * wrow);
+    constexpr int WB = W8 ? BK : BK / 2;   // weight bytes per column and step
     auto issue = [&](int slot, const __amdgpu_buffer_rsrc_t& ra, const __amdgpu_buffer_rsrc_t& rw, int st) {
         if (!loader) return;
-        int8_t* as = smem + slot * R3_SLOT;
-        int8_t* ws = as + R3_ASTAGE;
-        const int ka = st * R3_BK, kw = st * (R3_BK / 2);
+        int8_t* as = smem + slot * SLOT;
+        int8_t* ws = as + ASTAGE;
+        const int ka = st * BK, kw = st * WB;
 #pragma unroll
-        for (int i = 0; i < R3_ALOADS; ++i)
+        for (int i = 0; i < G3::ALOADS; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (__attribute__((address_space(3))) void*)(as + (lw * 64 + i * 8) * R3_BK), 16,
-                a_vo + (lw * 8 + i) * a_row8 + ka, 0, 0, 0);
+                ra, (__attribute__((address_space(3))) void*)(as + (lw * 64 + i * RPL) * BK), 16,
+                a_vo + (lw * (64 / RPL) + i) * a_rowl + ka, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < R3_WLOADS; ++i)
+        for (int i = 0; i < G3::WLOADS; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw, (__attribute__((address_space(3))) void*)(ws + (lw * 64 + i * 16) * (R3_BK / 2)), 16,
+                rw, (__attribute__((address_space(3))) void*)(ws + (lw * 64 + i * 16) * WB), 16,
                 w_vo + i * w_col16 + kw, 0, 0, 0);
     };
 
     v4i acc[8][4];
     // fragment offsets inside a slot
-    const int w_ro = R3_ASTAGE + (wn * 64 + j) * (R3_BK / 2) + ((q ^ ((j >> 1) & 3)) * 16);
-    const int a_ro = (wm * 128 + j) * R3_BK;
+    const int w_ro = W8 ? ASTAGE + (wn * 64 + j) * BK + ((q ^ r3_swz8(j)) * 16)
+                        : ASTAGE + (wn * 64 + j) * (BK / 2) + ((q ^ ((j >> 1) & 3)) * 16);
+    const int a_ro = (wm * 128 + j) * BK + (W8 ? ((q ^ r3_swz8(j)) * 16) : 0);
     const int a_c0 = ((q * 2) ^ r3_swz(j)) * 16, a_c1 = ((q * 2 + 1) ^ r3_swz(j)) * 16;
     // One step: the weight fragments and the code fragments of substep 0,
-    // then those of substep 1 while substep 0 multiplies.
+    // then those of substep 1 while substep 0 multiplies (W8: one substep).
     auto compute = [&](int slot) {
-        const int8_t* as = smem + slot * R3_SLOT + a_ro;
-        const int8_t* ws = smem + slot * R3_SLOT + w_ro;
+        const int8_t* as = smem + slot * SLOT + a_ro;
+        const int8_t* ws = smem + slot * SLOT + w_ro;
+        if constexpr (W8) {
+            v4i bf[4], af[8];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) bf[nt] = *(const v4i*)(ws + nt * 16 * BK);
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) af[mt] = *(const v4i*)(as + mt * 16 * BK);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+            return;
+        }
         v4u wp[4];
         v4i af[2][8];
 #pragma unroll
@@ -644,7 +689,7 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
-                af[tt][mt] = *(const v4i*)(as + mt * 16 * R3_BK + (tt ? a_c1 : a_c0));
+                af[tt][mt] = *(const v4i*)(as + mt * 16 * BK + (tt ? a_c1 : a_c0));
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -656,8 +701,8 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
             }
     };
 
-    R3Tile cur_t = r3_tile(a, t, ntiles, tiles_n);
-    R3Tile nxt_t = r3_tile(a, t + G, ntiles, tiles_n);
+    R3Tile cur_t = r3_tile<W8>(a, t, ntiles, tiles_n);
+    R3Tile nxt_t = r3_tile<W8>(a, t + G, ntiles, tiles_n);
     // Loads are issued unconditionally: stages past the end of a tile belong
     // to the next tile (or read zeros when there is none), so the loop carries
     // no control flow around them.
@@ -667,7 +712,7 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
     // vmcnt retires in issue order (gfx9): after a full tile's epilogue the
     // loader's own r3_stores() output stores sit behind the next tile's first
     // two stages, so steps 0 and 1 may leave them in flight
-    static_assert(12 + r3_stores<ODT>() <= 63, "vmcnt range");
+    static_assert(LPS + r3_stores<ODT>() <= 63, "vmcnt range");
     // exactly r3_stores() stores behind the first two stages, as after every
     // full tile: dropped stores through a zero-sized buffer
     auto pad_stores = [&]() {
@@ -687,7 +732,7 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
             for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = (v4i){0, 0, 0, 0};
         for (int s = 0; s < nsteps; ++s) {
             if (loader) {
-                // Stage s has landed once vmcnt drops to 12 (the next stage's
+                // Stage s has landed once vmcnt drops to LPS (the next stage's
                 // loads may still be in flight); in steps 0 and 1 the previous
                 // tile's r3_stores() output stores (or as many dropped stand-ins),
                 // issued after this tile's first two stages, may be in flight
@@ -699,8 +744,8 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
                     "s_waitcnt vmcnt(%1)\n\t"
                     "s_branch 2f\n"
                     "1:\n\t"
-                    "s_waitcnt vmcnt(12)\n"
-                    "2:" ::"s"(s), "n"(12 + r3_stores<ODT>()) : "memory", "scc");
+                    "s_waitcnt vmcnt(%2)\n"
+                    "2:" ::"s"(s), "n"(LPS + r3_stores<ODT>()), "n"(LPS) : "memory", "scc");
             }
             __builtin_amdgcn_s_barrier();
             const bool same = s + 2 < nsteps;
@@ -721,7 +766,8 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
         // row-contiguous and stores it with 16-byte stores.  A loader wave's
         // stores stay in flight into the next tile's first two steps (the
         // wait there counts them).
-        int8_t* eslot = smem + nxt2 * R3_SLOT;  // == slot of the step just computed
+        // (W8: the area after the three slots)
+        int8_t* eslot = W8 ? smem + 3 * SLOT : smem + nxt2 * SLOT;  // == slot of the step just computed
         __builtin_amdgcn_s_barrier();
         constexpr int SRB = r3_srb<ODT>();
         constexpr int ESZ = ODT == F32 ? 4 : 2;
@@ -771,7 +817,7 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
             for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float tv = mul_rn(mul_rn((float)(acc[mt][nt][r] >> 4), sa[r]), scl[nt]);
+                    const float tv = mul_rn(mul_rn((float)(acc[mt][nt][r] >> SHIFT), sa[r]), scl[nt]);
                     const float o = has_bias ? add_rn(tv, bia[nt]) : tv;
                     int8_t* dst = mine + (4 * q + r) * SRB + (nt * 16 + j) * ESZ;
                     if constexpr (ODT == F32)
@@ -840,7 +886,7 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
         t += G;
         if (t >= ntiles) break;
         cur_t = nxt_t;
-        nxt_t = r3_tile(a, t + G, ntiles, tiles_n);
+        nxt_t = r3_tile<W8>(a, t + G, ntiles, tiles_n);
     }
     __builtin_amdgcn_s_waitcnt(0x0070);
 }
@@ -958,8 +1004,14 @@ int gemm_path(const GemmArgs& a)
     const bool aligned = (a.K % 32) == 0 && ((uintptr_t)a.codes % 16) == 0 &&
                          ((uintptr_t)a.wp % 16) == 0;
     const bool group = a.sw_group > 0;
-    // INT8 weights: the 128 x 128 kernel
-    if (a.w8) return a.k_chunk > 0 ? kGemmTileSplitK : kGemmTile;
+    // INT8 weights: the three-stage kernel (64-deep K steps) for
+    // prefill-sized layers, else the 128 x 128 kernel
+    if (a.w8) {
+        if (a.k_chunk == 0 && a.acc_out == nullptr && a.M > 128 && (a.K % R3Geo<true>::BK) == 0 &&
+            a.K >= 2 * R3Geo<true>::BK && aligned && ((uintptr_t)a.out % 16) == 0)
+            return kGemmRing3;
+        return a.k_chunk > 0 ? kGemmTileSplitK : kGemmTile;
+    }
     // decode-sized M: the skinny kernel (every epilogue variant but group
     // scales and K-chunks)
     if (!group && a.k_chunk == 0 && a.M >= 1 && a.M <= 64 && (a.K % 64) == 0 &&
@@ -1006,6 +1058,15 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
                 n_cu = 256;
         }
         const unsigned grid = (unsigned)(nt < n_cu ? nt : n_cu);
+        if (a.w8) {
+            if (a.out_dtype == F32)
+                hipLaunchKernelGGL((w4a4_gemm_ring3_kernel<F32, true>), dim3(grid), dim3(512), 0, st, a, tm, tn);
+            else if (a.out_dtype == F16)
+                hipLaunchKernelGGL((w4a4_gemm_ring3_kernel<F16, true>), dim3(grid), dim3(512), 0, st, a, tm, tn);
+            else
+                hipLaunchKernelGGL((w4a4_gemm_ring3_kernel<BF16, true>), dim3(grid), dim3(512), 0, st, a, tm, tn);
+            return hipGetLastError();
+        }
         if (a.out_dtype == F32)
             hipLaunchKernelGGL(w4a4_gemm_ring3_kernel<F32>, dim3(grid), dim3(512), 0, st, a, tm, tn);
         else if (a.out_dtype == F16)

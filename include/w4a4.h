@@ -181,6 +181,11 @@ size_t w8a8_linear_workspace_size(int64_t M, int64_t K, int64_t N);
 int w8a8_rotate_quant_plan(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
                            int64_t stride_k, const float* rot, int32_t g, const void* smooth,
                            const int8_t* codes, const void* rotated_out, int* kernel);
+/* host-only: the kernel w8a8_gemm_from_codes would take for these operand
+ * addresses (ids as for w4a4_gemm_plan: 0 128 x 128 tile, 1 the same with
+ * int64 K-chunks, 2 three-stage 256 x 256) */
+int w8a8_gemm_plan(const int8_t* codes, int64_t M, int64_t K, const int8_t* w, int64_t N,
+                   const void* out, int* kernel);
 
 /*
  * w4a4_linear for callers that cannot allocate device memory (code under

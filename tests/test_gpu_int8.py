@@ -112,11 +112,14 @@ def test_int8_exact_ties_half_even():
     assert np.array_equal(c[7, 64:127], -((k + 1) // 2 * 2))
 
 
-@pytest.mark.parametrize("M,K,N", [(300, 2048, 520), (513, 1024, 257), (64, 256, 64), (1000, 640, 1000),
-                                   (5, 96, 17)])
+@pytest.mark.parametrize("M,K,N,kernel", [(300, 2048, 520, "ring3"), (513, 1024, 257, "ring3"),
+                                          (260, 192, 300, "ring3"), (1000, 640, 1000, "ring3"),
+                                          (64, 256, 64, "tile128"), (5, 96, 17, "tile128"),
+                                          (200, 100, 40, "tile128")])
 @pytest.mark.parametrize("odt", ["bf16", "f16", "f32"])
-def test_int8_gemm_bit_exact(M, K, N, odt):
+def test_int8_gemm_bit_exact(M, K, N, kernel, odt):
     need_gpu()
+    assert w4.w8a8_gemm_plan(M, K, N) == kernel
     rng = np.random.default_rng(M + K + N)
     codes = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
     w = rng.integers(-128, 128, size=(N, K)).astype(np.int8)
@@ -131,6 +134,25 @@ def test_int8_gemm_bit_exact(M, K, N, odt):
     acc = oracle.gemm(codes, w)
     ref = oracle.epilogue(acc, sa, sw, odt, odt, bias=b, bias_dtype=odt)
     assert np.array_equal(bits(host(out)), bits(ref))
+
+
+@pytest.mark.parametrize("odt", ["bf16", "f32"])
+def test_int8_gemm_ring3_many_tiles(odt):
+    # more 256 x 256 tiles than workgroups (each walks several, the operand
+    # ring running across them), ragged in M and N; sampled rows, every column
+    need_gpu()
+    M, K, N = 4500, 256, 3900
+    assert w4.w8a8_gemm_plan(M, K, N) == "ring3"
+    rng = np.random.default_rng(57)
+    codes = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    w = rng.integers(-128, 128, size=(N, K)).astype(np.int8)
+    sa = rng.uniform(0.001, 0.1, size=M).astype(np.float32)
+    sw = workloads.f32_to_storage(rng.uniform(0.001, 0.01, size=N).astype(np.float32), odt)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[odt]
+    out = host(w4.w8a8_gemm_from_codes(dev(codes), dev(sa), dev(w), dev(sw, odt), out_dtype=tdt))
+    rows = np.unique(np.concatenate([np.arange(4352, M), rng.choice(M, 150, replace=False), [0, 255, 256]]))
+    ref = oracle.epilogue(oracle.gemm(codes[rows], w), sa[rows], sw, odt, odt)
+    assert np.array_equal(bits(out[rows]), bits(ref))
 
 
 def test_int8_gemm_int64_chunks():
