@@ -320,6 +320,9 @@ def measure(name, steps, warmup, torch, np, w4, workloads, cpu=True):
     }
     if par is not None:
         res["parity"] = par
+    if not w.transposed and w.dtype != "f32":
+        res["hadamard"] = _hadamard_leg(w, sets, outs, wss, qbufs, steps, warmup, torch, np, w4, b, stream,
+                                        rq_bytes, qmax=7)
     if rank:
         res["gemm"]["note"] = "low-rank term excluded from the GEMM-alone timing"
         # low-rank down projection alone (the first kernel of a low-rank step)
@@ -342,6 +345,56 @@ def measure(name, steps, warmup, torch, np, w4, workloads, cpu=True):
                                "frac_hbm": lrd_bytes / (t_lrd["ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                "algorithmic_bytes": lrd_bytes}
     return w, inp, res
+
+
+def _hadamard_leg(w, sets, outs, wss, qbufs, steps, warmup, torch, np, w4, b, stream, rq_bytes, qmax):
+    """The same workload with the rotation given by its structure (the
+    normalized Hadamard the workload uses): rotate-quant alone through
+    w4a4_rotate_quant_hadamard (fast Walsh-Hadamard kernel), and for INT4
+    codes the whole layer through w4a4_linear_hadamard."""
+    lib = w4.lib()
+    M, K, g = w.M, w.K, w.g
+    xc = _dtcode(torch, sets[0]["x"])
+
+    def rq(i):
+        s = sets[i % 4]
+        c, sc = qbufs[i % 4]
+        x = s["x"]
+        sm = s.get("smooth")
+        rc = lib.w4a4_rotate_quant_hadamard(x.data_ptr(), xc, M, K, x.stride(0), 1, g, None, None,
+                                            sm.data_ptr() if sm is not None else None, qmax, c.data_ptr(),
+                                            sc.data_ptr(), None, stream)
+        if rc:
+            b._check(rc, "w4a4_rotate_quant_hadamard")
+    nk = max(steps, MIN_KERNEL_LAUNCHES)
+    for i in range(warmup):
+        rq(i)
+    t = _time_each(rq, nk, torch, np)
+    out = {"kernel": "rq_hadamard_kernel (fast Walsh-Hadamard, qmax %d)" % qmax, **t,
+           "GB_s": rq_bytes / (t["ms_median"] * 1e-3) / 1e9,
+           "frac_hbm": rq_bytes / (t["ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if qmax == 7:
+        h = w4.Hadamard(g)
+
+        def step(i):
+            s = sets[i % 4]
+            w4.w4a4_linear_hadamard(s["x"], h, s["w_packed"], s["w_scale"], w_scale_group=w.sw_group,
+                                    bias=s["bias"], smooth=s["smooth"], proj_down=s["proj_down"],
+                                    proj_up=s["proj_up"], workspace=wss[i % 4], out=outs[i % 4])
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for i in range(steps):
+            step(i)
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        out["ms_per_step"] = ms
+        out["tops"] = 2.0 * M * w.N * K / (ms * 1e-3) / 1e12
+    return out
 
 
 def measure_int8(name, steps, warmup, torch, np, w4, workloads, cpu=True):
@@ -477,6 +530,8 @@ def measure_int8(name, steps, warmup, torch, np, w4, workloads, cpu=True):
                     "GB_s": gemm_bytes / (ms_gemm * 1e-3) / 1e9, "algorithmic_bytes": gemm_bytes}}
     if par is not None:
         res["parity"] = par
+    res["hadamard"] = _hadamard_leg(w, [dict(s, smooth=None) for s in sets], outs, wss, qbufs, steps, warmup,
+                                    torch, np, w4, b, stream, rq_bytes, qmax=127)
     return res
 
 
@@ -808,6 +863,8 @@ def main():
                                   if ceiling else None},
         "stream_ceiling": _rounded(ceiling) if ceiling else None,
     }
+    if "hadamard" in main_res:
+        line["hadamard"] = _rounded(main_res["hadamard"])
     for name, extra in extras.items():
         line[name] = {"workload": extra["workload"], "ms_per_step": round(extra["ms_per_step"], 5),
                       "tops": round(extra["tops"], 2), "parity": extra.get("parity"),
@@ -815,6 +872,8 @@ def main():
                       "gemm": _rounded(extra["gemm"])}
         if "lowrank_down" in extra:
             line[name]["lowrank_down"] = _rounded(extra["lowrank_down"])
+        if "hadamard" in extra:
+            line[name]["hadamard"] = _rounded(extra["hadamard"])
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, inp, np)
     print(json.dumps(line), flush=True)

@@ -24,5 +24,10 @@ from ._binding import (  # noqa: F401
     w8a8_linear_workspace_size,
     w8a8_rotate_quant_plan,
     w8a8_gemm_plan,
+    Hadamard,
+    w4a4_rotate_quant_hadamard,
+    w4a4_rotate_quant_hadamard_plan,
+    w4a4_linear_hadamard,
+    w8a8_linear_hadamard,
     w8a8_rotate_quant_rowwise,
 )

@@ -49,6 +49,16 @@ _SIGNATURES = {
     "w8a8_rotate_quant_plan": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp,
                                 ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
     "w8a8_gemm_plan": ([_vp, _i64, _i64, _vp, _i64, _vp, ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
+    "w4a4_rotate_quant_hadamard": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp,
+                                    _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "w4a4_rotate_quant_hadamard_plan": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i32, _vp, _i32,
+                                         _vp, _vp, ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
+    "w4a4_linear_hadamard": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp,
+                              _i64, _vp, ctypes.c_int, _i32, _vp, _vp, _vp, _i32, _vp, ctypes.c_int,
+                              _vp, _sz, _vp], ctypes.c_int),
+    "w8a8_linear_hadamard": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp,
+                              _i64, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _sz, _vp],
+                             ctypes.c_int),
     "w4a4_linear_noalloc": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _i64,
                              _vp, ctypes.c_int, _i32, _vp, _vp, _vp, _i32, _vp, ctypes.c_int, _vp],
                             ctypes.c_int),
@@ -537,4 +547,162 @@ def w8a8_linear(x: torch.Tensor, rot: Optional[torch.Tensor], g: int, w: torch.T
         _ptr(w_scale), _dt(w_scale), _ptr(bias), _ptr(out), _DT[out.dtype], _ptr(workspace),
         workspace.numel(), _stream(dev))
     _check(rc, "w8a8_linear")
+    return out.view(*lead, N)
+
+
+# ---- structured (Hadamard) rotation: the fast Walsh-Hadamard kernel --------
+
+class Hadamard:
+    """The rotation R = diag(sign_in) . H_g . diag(sign_out) / sqrt(g), given by
+    its structure (H_g the Sylvester Hadamard matrix); sign_in / sign_out are
+    int8 (g,) device tensors of +-1 or None (all +1).  The *_hadamard calls
+    take it in place of a dense (g, g) rot."""
+
+    def __init__(self, g: int, sign_in: Optional[torch.Tensor] = None,
+                 sign_out: Optional[torch.Tensor] = None):
+        if g not in (16, 32, 64, 128, 256):
+            raise ValueError(f"g must be a power of two in [16, 256], got {g}")
+        for name, s in (("sign_in", sign_in), ("sign_out", sign_out)):
+            if s is not None:
+                _need(s, name, (g,), (torch.int8,))
+        self.g, self.sign_in, self.sign_out = g, sign_in, sign_out
+
+    def dense(self) -> torch.Tensor:
+        """The same R written out, fp32 (g, g) on the signs' device (CPU if
+        none): what the dense calls take."""
+        h = torch.ones((1, 1), dtype=torch.float64)
+        while h.shape[0] < self.g:
+            h = torch.cat([torch.cat([h, h], 1), torch.cat([h, -h], 1)], 0)
+        dev = next((s.device for s in (self.sign_in, self.sign_out) if s is not None), torch.device("cpu"))
+        h = h.to(dev)
+        if self.sign_in is not None:
+            h = h * torch.where(self.sign_in < 0, -1.0, 1.0).to(torch.float64)[:, None]
+        if self.sign_out is not None:
+            h = h * torch.where(self.sign_out < 0, -1.0, 1.0).to(torch.float64)[None, :]
+        return (h / float(self.g) ** 0.5).to(torch.float32)
+
+
+def _hadamard_arg(h) -> "Hadamard":
+    if not isinstance(h, Hadamard):
+        raise ValueError(f"expected a Hadamard rotation, got {type(h).__name__}")
+    return h
+
+
+def w4a4_rotate_quant_hadamard(x: torch.Tensor, h: Hadamard, qmax: int = 7,
+                               smooth: Optional[torch.Tensor] = None,
+                               return_rotated: bool = False):
+    """Rotate + per-row quantization with a Hadamard rotation (fast
+    Walsh-Hadamard transform), INT4 codes (qmax 7) or the INT8 mode (127).
+    Returns (codes int8 (M, K), scales fp32 (M,)) and, if requested, the
+    rotated values (M, K) in x.dtype."""
+    h = _hadamard_arg(h)
+    x2 = _as_2d(_need(x, "x", contiguous=False))
+    M, K = x2.shape
+    _dt(x2)
+    if smooth is not None:
+        _need(smooth, "smooth", (K,), (x2.dtype,))
+    _same_device(x2, sign_in=h.sign_in, sign_out=h.sign_out, smooth=smooth)
+    dev = x2.device
+    codes = torch.empty((M, K), dtype=torch.int8, device=dev)
+    scales = torch.empty((M,), dtype=torch.float32, device=dev)
+    rotated = torch.empty((M, K), dtype=x2.dtype, device=dev) if return_rotated else None
+    rc = lib().w4a4_rotate_quant_hadamard(
+        _ptr(x2), _dt(x2), M, K, x2.stride(0), x2.stride(1), h.g, _ptr(h.sign_in), _ptr(h.sign_out),
+        _ptr(smooth), qmax, _ptr(codes), _ptr(scales), _ptr(rotated), _stream(dev))
+    _check(rc, "w4a4_rotate_quant_hadamard")
+    return (codes, scales, rotated) if return_rotated else (codes, scales)
+
+
+def w4a4_rotate_quant_hadamard_plan(x: torch.Tensor, g: int, qmax: int = 7,
+                                    smooth: Optional[torch.Tensor] = None,
+                                    return_rotated: bool = False) -> str:
+    """"hadamard" when w4a4_rotate_quant_hadamard serves these arguments;
+    raises W4A4Error (unsupported) otherwise.  Host-only."""
+    x2 = _as_2d(x)
+    M, K = x2.shape
+    k = ctypes.c_int(-1)
+    rc = lib().w4a4_rotate_quant_hadamard_plan(
+        _ptr(x2), _dt(x2), M, K, x2.stride(0), x2.stride(1), g, _ptr(smooth), qmax, _ALIGNED,
+        _ALIGNED if return_rotated else None, ctypes.byref(k))
+    _check(rc, "w4a4_rotate_quant_hadamard_plan")
+    return {7: "hadamard"}.get(k.value, "none")
+
+
+def w4a4_linear_hadamard(x: torch.Tensor, h: Hadamard, w_packed: torch.Tensor,
+                         w_scale: torch.Tensor, w_scale_group: int = 0,
+                         bias: Optional[torch.Tensor] = None, smooth: Optional[torch.Tensor] = None,
+                         proj_down: Optional[torch.Tensor] = None,
+                         proj_up: Optional[torch.Tensor] = None,
+                         out_dtype: Optional[torch.dtype] = None,
+                         workspace: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """w4a4_linear with a Hadamard rotation (fast Walsh-Hadamard transform)."""
+    h = _hadamard_arg(h)
+    lead, x2, _, _, N, rank, out_dtype = _linear_checks(
+        x, None, h.g, w_packed, w_scale, w_scale_group, bias, smooth, proj_down, proj_up, out_dtype, out)
+    M, K = x2.shape
+    need = w4a4_linear_workspace_size(M, K, N, rank)
+    if workspace is not None:
+        _need(workspace, "workspace", dtypes=(torch.uint8,))
+        if workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, need {need}")
+    _same_device(x2, sign_in=h.sign_in, sign_out=h.sign_out, w_packed=w_packed, w_scale=w_scale,
+                 bias=bias, smooth=smooth, proj_down=proj_down, proj_up=proj_up, out=out,
+                 workspace=workspace)
+    dev = x2.device
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    rc = lib().w4a4_linear_hadamard(
+        _ptr(x2), _dt(x2), M, K, x2.stride(0), x2.stride(1), h.g, _ptr(h.sign_in), _ptr(h.sign_out),
+        _ptr(smooth), _ptr(w_packed), N, _ptr(w_scale), _dt(w_scale), w_scale_group, _ptr(bias),
+        _ptr(proj_down), _ptr(proj_up), rank, _ptr(out), _DT[out.dtype], _ptr(workspace),
+        workspace.numel(), _stream(dev))
+    _check(rc, "w4a4_linear_hadamard")
+    return out.view(*lead, N)
+
+
+def w8a8_linear_hadamard(x: torch.Tensor, h: Hadamard, w: torch.Tensor, w_scale: torch.Tensor,
+                         bias: Optional[torch.Tensor] = None, smooth: Optional[torch.Tensor] = None,
+                         out_dtype: Optional[torch.dtype] = None,
+                         workspace: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The dynamic INT8 linear with a Hadamard rotation."""
+    h = _hadamard_arg(h)
+    lead = _need(x, "x", contiguous=False).shape[:-1]
+    x2 = _as_2d(x)
+    M, K = x2.shape
+    _dt(x2)
+    _need(w, "w", dtypes=(torch.int8,))
+    if w.dim() != 2 or w.shape[1] != K:
+        raise ValueError(f"w has shape {tuple(w.shape)}, expected (N, {K})")
+    N = w.shape[0]
+    _need(w_scale, "w_scale", (N,), _FLOAT)
+    if bias is not None:
+        _need(bias, "bias", (N,), (x2.dtype,))
+    if smooth is not None:
+        _need(smooth, "smooth", (K,), (x2.dtype,))
+    out_dtype = out_dtype or (out.dtype if out is not None else x2.dtype)
+    if out_dtype not in _FLOAT:
+        raise ValueError(f"out_dtype {out_dtype} is not float32/float16/bfloat16")
+    if out is not None:
+        _need(out, "out", (M, N), (out_dtype,))
+    need = w8a8_linear_workspace_size(M, K, N)
+    if workspace is not None:
+        _need(workspace, "workspace", dtypes=(torch.uint8,))
+        if workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, need {need}")
+    _same_device(x2, sign_in=h.sign_in, sign_out=h.sign_out, w=w, w_scale=w_scale, bias=bias,
+                 smooth=smooth, out=out, workspace=workspace)
+    dev = x2.device
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    rc = lib().w8a8_linear_hadamard(
+        _ptr(x2), _dt(x2), M, K, x2.stride(0), x2.stride(1), h.g, _ptr(h.sign_in), _ptr(h.sign_out),
+        _ptr(smooth), _ptr(w), N, _ptr(w_scale), _dt(w_scale), _ptr(bias), _ptr(out), _DT[out.dtype],
+        _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(rc, "w8a8_linear_hadamard")
     return out.view(*lead, N)

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a4.so")
 PROBE_LIB = os.path.join(HERE, "libw4a4_probe.so")
-SOURCES = ["api.hip", "rotate_quant.hip", "rq_row.hip", "gemm.hip", "lowrank.hip"]
+SOURCES = ["api.hip", "rotate_quant.hip", "rq_row.hip", "rq_hadamard.hip", "gemm.hip", "lowrank.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -24,7 +24,8 @@ HIPCC_FLAGS = [
 # VGPRs (the group-scale loop converts every result with VALU instructions,
 # which cannot read accumulation registers)
 SOURCE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-                "rq_row.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+                "rq_row.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "rq_hadamard.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:

@@ -66,12 +66,12 @@ int check_activation(const void* x, int dt, int64_t M, int64_t K, int64_t sm, in
     return W4A4_OK;
 }
 
-int rq_validate(const void* x, int dt, int64_t M, int64_t K, int64_t sm, int64_t sk, const float* rot,
-                int g, int8_t* codes, float* scales, bool int4 = true)
+int rq_validate_g(const void* x, int dt, int64_t M, int64_t K, int64_t sm, int64_t sk, bool rotated,
+                  int g, int8_t* codes, float* scales, bool int4)
 {
     int rc = check_activation(x, dt, M, K, sm, sk, int4);
     if (rc) return rc;
-    if (rot) {
+    if (rotated) {
         if (g <= 0) return fail(W4A4_INVALID, "group size g=%d", g);
         if (K % g) return fail(W4A4_INVALID, "K=%lld is not a multiple of g=%d", (long long)K, g);
         if (!pow2_g(g)) return fail(W4A4_UNSUPPORTED, "g=%d is not a power of two in [16, 256]", g);
@@ -79,6 +79,25 @@ int rq_validate(const void* x, int dt, int64_t M, int64_t K, int64_t sm, int64_t
     if (M > 0 && (!codes || !scales)) return fail(W4A4_INVALID, "codes/scales is NULL");
     if (M > 0 && K == 0) return fail(W4A4_INVALID, "K=0 with M>0");
     return W4A4_OK;
+}
+
+int rq_validate(const void* x, int dt, int64_t M, int64_t K, int64_t sm, int64_t sk, const float* rot,
+                int g, int8_t* codes, float* scales, bool int4 = true)
+{
+    return rq_validate_g(x, dt, M, K, sm, sk, rot != nullptr, g, codes, scales, int4);
+}
+
+// the rotate-quant arguments of a structured (Hadamard) rotation
+RQArgs hadamard_args(const void* x, int x_dtype, int64_t M, int64_t K, int64_t sm, int64_t sk, int32_t g,
+                     const int8_t* sign_in, const int8_t* sign_out, const void* smooth, int qmax,
+                     int8_t* codes, float* scales, void* rotated_out)
+{
+    RQArgs a{x, x_dtype, M, K, sm, sk, nullptr, g, smooth, codes, scales, rotated_out};
+    a.qmax = qmax;
+    a.hadamard = 1;
+    a.sign_in = sign_in;
+    a.sign_out = sign_out;
+    return a;
 }
 
 int64_t guard_chunk(int64_t K) { return K > kGemmMaxK ? kGemmMaxK : 0; }
@@ -137,6 +156,139 @@ int scratch_address(void** ptr)
         g_scratch_dev[dev] = p;
     }
     *ptr = g_scratch_dev[dev];
+    return W4A4_OK;
+}
+
+// w4a4_linear given its rotate-quant arguments (x, shape, rotation,
+// smoothing; codes and scales are placed in the workspace here)
+int linear4_impl(RQArgs qa, bool rotated, const uint8_t* w_packed, int64_t N, const void* w_scale,
+                 int w_scale_dtype, int32_t w_scale_group, const void* bias, const void* proj_down,
+                 const void* proj_up, int32_t rank, void* out, int out_dtype, void* workspace,
+                 size_t workspace_bytes, void* stream)
+{
+    const int64_t M = qa.M, K = qa.K;
+    const int x_dtype = qa.dtype;
+    // Validate everything before the first launch.
+    int rc = rq_validate_g(qa.x, x_dtype, M, K, qa.sm, qa.sk, rotated, qa.g, (int8_t*)1, (float*)1, true);
+    if (rc) return rc;
+    if ((proj_down == nullptr) != (proj_up == nullptr))
+        return fail(W4A4_INVALID, "proj_down and proj_up go together");
+    const int r = proj_down ? rank : 0;
+    if (proj_down && (rank < 1 || rank > 64)) return fail(W4A4_INVALID, "rank=%d outside [1, 64]", rank);
+    const float* fake_lora = r ? (const float*)1 : nullptr;
+    rc = gemm_validate((const int8_t*)1, (const float*)1, M, K, w_packed, N, w_scale, w_scale_dtype,
+                       w_scale_group, bias, x_dtype, fake_lora, proj_up, x_dtype, r, out, out_dtype, 0);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return W4A4_OK;
+    const size_t need = w4a4_linear_workspace_size(M, K, N, r);
+    if (!workspace || workspace_bytes < need)
+        return fail(W4A4_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    rc = device_check();
+    if (rc) return rc;
+
+    uint8_t* ws = (uint8_t*)workspace;
+    int8_t* codes = (int8_t*)ws;
+    ws += align256((size_t)M * (size_t)K);
+    float* scales = (float*)ws;
+    ws += align256((size_t)M * 4);
+    float* lora = nullptr;
+    if (r) {
+        lora = (float*)ws;
+        ws += align256((size_t)M * r * 4);
+    }
+    const int64_t kc = w_scale_group ? 0 : guard_chunk(K);
+    int64_t* acc64 = kc > 0 ? (int64_t*)ws : nullptr;
+    hipStream_t st = (hipStream_t)stream;
+
+    // decide every launch before the first one, so that a call that is
+    // refused leaves nothing enqueued
+    qa.codes = codes;
+    qa.scales = scales;
+    qa.yout = nullptr;
+    if (rotate_quant_path(qa) < 0)
+        return fail(W4A4_UNSUPPORTED, "no rotate_quant kernel for this shape (K=%lld)", (long long)K);
+    hipError_t e;
+    if (r) {
+        LowRankArgs la{qa.x, x_dtype, M, K, qa.sm, qa.sk, proj_down, r, lora};
+        e = launch_lowrank_down(la, st);
+        if (e != hipSuccess) return hip_fail(e, "lowrank_down launch");
+    }
+    int path = 0;
+    e = launch_rotate_quant(qa, st, &path);
+    if (e == hipErrorNotSupported)
+        return fail(W4A4_UNSUPPORTED, "no rotate_quant kernel for this shape (K=%lld)", (long long)K);
+    if (e != hipSuccess) return hip_fail(e, "rotate_quant launch");
+    GemmArgs ga{codes, scales, M, K, N, w_packed, w_scale, w_scale_dtype, w_scale_group,
+                bias, x_dtype, lora, proj_up, x_dtype, r, out, out_dtype, nullptr, kc, acc64};
+    e = launch_gemm(ga, st);
+    if (e != hipSuccess) return hip_fail(e, "gemm launch");
+    return W4A4_OK;
+}
+
+size_t w8_workspace(int64_t M, int64_t K, int64_t N)
+{
+    if (M <= 0) return 0;
+    size_t s = align256((size_t)M * (size_t)K) + align256((size_t)M * 4);
+    if (N > 0 && guard_chunk8(K) > 0) s += align256((size_t)M * (size_t)N * 8);
+    return s;
+}
+
+// w8a8_linear given its rotate-quant arguments
+int linear8_impl(RQArgs qa, bool rotated, const int8_t* w, int64_t N, const void* w_scale, int w_scale_dtype,
+                 const void* bias, void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                 void* stream)
+{
+    const int64_t M = qa.M, K = qa.K;
+    const int x_dtype = qa.dtype;
+    int rc = rq_validate_g(qa.x, x_dtype, M, K, qa.sm, qa.sk, rotated, qa.g, (int8_t*)1, (float*)1, false);
+    if (rc) return rc;
+    if (N < 0) return fail(W4A4_INVALID, "negative size");
+    if (!dtype_ok(w_scale_dtype) || !dtype_ok(out_dtype)) return fail(W4A4_UNSUPPORTED, "unknown dtype code");
+    if (M > 0 && N > 0 && (!w || !w_scale || !out)) return fail(W4A4_INVALID, "a required pointer is NULL");
+    if (M == 0 || N == 0) return W4A4_OK;
+    const size_t need = w8_workspace(M, K, N);
+    if (!workspace || workspace_bytes < need)
+        return fail(W4A4_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    rc = device_check();
+    if (rc) return rc;
+    uint8_t* ws = (uint8_t*)workspace;
+    int8_t* codes = (int8_t*)ws;
+    ws += align256((size_t)M * (size_t)K);
+    float* scales = (float*)ws;
+    ws += align256((size_t)M * 4);
+    const int64_t kc = guard_chunk8(K);
+    hipStream_t st = (hipStream_t)stream;
+    qa.codes = codes;
+    qa.scales = scales;
+    qa.yout = nullptr;
+    qa.qmax = 127;
+    if (rotate_quant_path(qa) < 0)
+        return fail(W4A4_UNSUPPORTED, "no INT8 rotate_quant kernel for this shape (K=%lld)", (long long)K);
+    int path = 0;
+    hipError_t e = launch_rotate_quant(qa, st, &path);
+    if (e != hipSuccess) return hip_fail(e, "rotate_quant launch");
+    GemmArgs ga{codes, scales, M, K, N, (const uint8_t*)w, w_scale, w_scale_dtype, 0,
+                bias, x_dtype, nullptr, nullptr, 0, 0, out, out_dtype, nullptr, kc, kc > 0 ? (int64_t*)ws : nullptr};
+    ga.w8 = 1;
+    e = launch_gemm(ga, st);
+    if (e != hipSuccess) return hip_fail(e, "gemm launch");
+    return W4A4_OK;
+}
+
+// rotate-quant entry (both code ranges) given its arguments
+int rq_impl(const RQArgs& a, bool rotated, void* stream)
+{
+    int rc = rq_validate_g(a.x, a.dtype, a.M, a.K, a.sm, a.sk, rotated, a.g, a.codes, a.scales, a.qmax == 7);
+    if (rc) return rc;
+    if (a.M == 0) return W4A4_OK;
+    rc = device_check();
+    if (rc) return rc;
+    int path = 0;
+    hipError_t e = launch_rotate_quant(a, (hipStream_t)stream, &path);
+    if (e == hipErrorNotSupported)
+        return fail(W4A4_UNSUPPORTED, "no rotate_quant kernel for this shape and layout (K=%lld, g=%d)",
+                    (long long)a.K, a.g);
+    if (e != hipSuccess) return hip_fail(e, "rotate_quant launch");
     return W4A4_OK;
 }
 
@@ -274,60 +426,9 @@ int w4a4_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride
                 const void* proj_up, int32_t rank, void* out, int out_dtype, void* workspace,
                 size_t workspace_bytes, void* stream)
 {
-    // Validate everything before the first launch.
-    int8_t* codes = nullptr;
-    int rc = rq_validate(x, x_dtype, M, K, stride_m, stride_k, rot, g, (int8_t*)1, (float*)1);
-    if (rc) return rc;
-    if ((proj_down == nullptr) != (proj_up == nullptr))
-        return fail(W4A4_INVALID, "proj_down and proj_up go together");
-    const int r = proj_down ? rank : 0;
-    if (proj_down && (rank < 1 || rank > 64)) return fail(W4A4_INVALID, "rank=%d outside [1, 64]", rank);
-    const float* fake_lora = r ? (const float*)1 : nullptr;
-    rc = gemm_validate((const int8_t*)1, (const float*)1, M, K, w_packed, N, w_scale, w_scale_dtype,
-                       w_scale_group, bias, x_dtype, fake_lora, proj_up, x_dtype, r, out, out_dtype, 0);
-    if (rc) return rc;
-    if (M == 0 || N == 0) return W4A4_OK;
-    const size_t need = w4a4_linear_workspace_size(M, K, N, r);
-    if (!workspace || workspace_bytes < need)
-        return fail(W4A4_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, need);
-    rc = device_check();
-    if (rc) return rc;
-
-    uint8_t* ws = (uint8_t*)workspace;
-    codes = (int8_t*)ws;
-    ws += align256((size_t)M * (size_t)K);
-    float* scales = (float*)ws;
-    ws += align256((size_t)M * 4);
-    float* lora = nullptr;
-    if (r) {
-        lora = (float*)ws;
-        ws += align256((size_t)M * r * 4);
-    }
-    const int64_t kc = w_scale_group ? 0 : guard_chunk(K);
-    int64_t* acc64 = kc > 0 ? (int64_t*)ws : nullptr;
-    hipStream_t st = (hipStream_t)stream;
-
-    // decide every launch before the first one, so that a call that is
-    // refused leaves nothing enqueued
-    RQArgs qa{x, x_dtype, M, K, stride_m, stride_k, rot, rot ? g : 0, smooth, codes, scales, nullptr};
-    if (rotate_quant_path(qa) < 0)
-        return fail(W4A4_UNSUPPORTED, "no rotate_quant kernel for this shape (K=%lld)", (long long)K);
-    hipError_t e;
-    if (r) {
-        LowRankArgs la{x, x_dtype, M, K, stride_m, stride_k, proj_down, r, lora};
-        e = launch_lowrank_down(la, st);
-        if (e != hipSuccess) return hip_fail(e, "lowrank_down launch");
-    }
-    int path = 0;
-    e = launch_rotate_quant(qa, st, &path);
-    if (e == hipErrorNotSupported)
-        return fail(W4A4_UNSUPPORTED, "no rotate_quant kernel for this shape (K=%lld)", (long long)K);
-    if (e != hipSuccess) return hip_fail(e, "rotate_quant launch");
-    GemmArgs ga{codes, scales, M, K, N, w_packed, w_scale, w_scale_dtype, w_scale_group,
-                bias, x_dtype, lora, proj_up, x_dtype, r, out, out_dtype, nullptr, kc, acc64};
-    e = launch_gemm(ga, st);
-    if (e != hipSuccess) return hip_fail(e, "gemm launch");
-    return W4A4_OK;
+    RQArgs qa{x, x_dtype, M, K, stride_m, stride_k, rot, rot ? g : 0, smooth, nullptr, nullptr, nullptr};
+    return linear4_impl(qa, rot != nullptr, w_packed, N, w_scale, w_scale_dtype, w_scale_group, bias,
+                        proj_down, proj_up, rank, out, out_dtype, workspace, workspace_bytes, stream);
 }
 
 // ---- INT8 mode (qmax = 127) and the dynamic INT8 linear ----------------
@@ -409,50 +510,70 @@ int w8a8_gemm_plan(const int8_t* codes, int64_t M, int64_t K, const int8_t* w, i
     return W4A4_OK;
 }
 
-size_t w8a8_linear_workspace_size(int64_t M, int64_t K, int64_t N)
-{
-    if (M <= 0) return 0;
-    size_t s = align256((size_t)M * (size_t)K) + align256((size_t)M * 4);
-    if (N > 0) s += w8a8_gemm_workspace_size(M, N, K);
-    return s;
-}
+size_t w8a8_linear_workspace_size(int64_t M, int64_t K, int64_t N) { return w8_workspace(M, K, N); }
 
 int w8a8_linear(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m, int64_t stride_k,
                 const float* rot, int32_t g, const void* smooth, const int8_t* w, int64_t N,
                 const void* w_scale, int w_scale_dtype, const void* bias, void* out, int out_dtype,
                 void* workspace, size_t workspace_bytes, void* stream)
 {
-    int rc = rq_validate(x, x_dtype, M, K, stride_m, stride_k, rot, g, (int8_t*)1, (float*)1, false);
+    RQArgs qa{x, x_dtype, M, K, stride_m, stride_k, rot, rot ? g : 0, smooth, nullptr, nullptr, nullptr};
+    return linear8_impl(qa, rot != nullptr, w, N, w_scale, w_scale_dtype, bias, out, out_dtype, workspace,
+                        workspace_bytes, stream);
+}
+
+// ---- structured (Hadamard) rotation: the fast Walsh-Hadamard kernel ------
+
+int w4a4_rotate_quant_hadamard(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                               int64_t stride_k, int32_t g, const int8_t* sign_in, const int8_t* sign_out,
+                               const void* smooth, int32_t qmax, int8_t* codes, float* scales,
+                               void* rotated_out, void* stream)
+{
+    if (qmax != 7 && qmax != 127) return fail(W4A4_INVALID, "qmax=%d is neither 7 nor 127", qmax);
+    const RQArgs a = hadamard_args(x, x_dtype, M, K, stride_m, stride_k, g, sign_in, sign_out, smooth, qmax,
+                                   codes, scales, rotated_out);
+    return rq_impl(a, true, stream);
+}
+
+int w4a4_rotate_quant_hadamard_plan(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                                    int64_t stride_k, int32_t g, const void* smooth, int32_t qmax,
+                                    const int8_t* codes, const void* rotated_out, int* kernel)
+{
+    if (qmax != 7 && qmax != 127) return fail(W4A4_INVALID, "qmax=%d is neither 7 nor 127", qmax);
+    int rc = rq_validate_g(x, x_dtype, M, K, stride_m, stride_k, true, g, (int8_t*)codes, (float*)1, qmax == 7);
     if (rc) return rc;
-    if (N < 0) return fail(W4A4_INVALID, "negative size");
-    if (!dtype_ok(w_scale_dtype) || !dtype_ok(out_dtype)) return fail(W4A4_UNSUPPORTED, "unknown dtype code");
-    if (M > 0 && N > 0 && (!w || !w_scale || !out)) return fail(W4A4_INVALID, "a required pointer is NULL");
-    if (M == 0 || N == 0) return W4A4_OK;
-    const size_t need = w8a8_linear_workspace_size(M, K, N);
-    if (!workspace || workspace_bytes < need)
-        return fail(W4A4_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, need);
-    rc = device_check();
-    if (rc) return rc;
-    uint8_t* ws = (uint8_t*)workspace;
-    int8_t* codes = (int8_t*)ws;
-    ws += align256((size_t)M * (size_t)K);
-    float* scales = (float*)ws;
-    ws += align256((size_t)M * 4);
-    const int64_t kc = guard_chunk8(K);
-    hipStream_t st = (hipStream_t)stream;
-    RQArgs qa{x, x_dtype, M, K, stride_m, stride_k, rot, rot ? g : 0, smooth, codes, scales, nullptr};
-    qa.qmax = 127;
-    if (rotate_quant_path(qa) < 0)
-        return fail(W4A4_UNSUPPORTED, "no INT8 rotate_quant kernel for this shape (K=%lld)", (long long)K);
-    int path = 0;
-    hipError_t e = launch_rotate_quant(qa, st, &path);
-    if (e != hipSuccess) return hip_fail(e, "rotate_quant launch");
-    GemmArgs ga{codes, scales, M, K, N, (const uint8_t*)w, w_scale, w_scale_dtype, 0,
-                bias, x_dtype, nullptr, nullptr, 0, 0, out, out_dtype, nullptr, kc, kc > 0 ? (int64_t*)ws : nullptr};
-    ga.w8 = 1;
-    e = launch_gemm(ga, st);
-    if (e != hipSuccess) return hip_fail(e, "gemm launch");
+    const RQArgs a = hadamard_args(x, x_dtype, M, K, stride_m, stride_k, g, nullptr, nullptr, smooth, qmax,
+                                   (int8_t*)codes, nullptr, (void*)rotated_out);
+    const int p = M > 0 ? rotate_quant_path(a) : -1;
+    if (M > 0 && p < 0)
+        return fail(W4A4_UNSUPPORTED, "no Hadamard rotate_quant kernel for this shape and layout (K=%lld, g=%d)",
+                    (long long)K, g);
+    if (kernel) *kernel = p;
     return W4A4_OK;
+}
+
+int w4a4_linear_hadamard(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                         int64_t stride_k, int32_t g, const int8_t* sign_in, const int8_t* sign_out,
+                         const void* smooth, const uint8_t* w_packed, int64_t N, const void* w_scale,
+                         int w_scale_dtype, int32_t w_scale_group, const void* bias, const void* proj_down,
+                         const void* proj_up, int32_t rank, void* out, int out_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream)
+{
+    const RQArgs qa = hadamard_args(x, x_dtype, M, K, stride_m, stride_k, g, sign_in, sign_out, smooth, 7,
+                                    nullptr, nullptr, nullptr);
+    return linear4_impl(qa, true, w_packed, N, w_scale, w_scale_dtype, w_scale_group, bias, proj_down, proj_up,
+                        rank, out, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int w8a8_linear_hadamard(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m, int64_t stride_k,
+                         int32_t g, const int8_t* sign_in, const int8_t* sign_out, const void* smooth,
+                         const int8_t* w, int64_t N, const void* w_scale, int w_scale_dtype, const void* bias,
+                         void* out, int out_dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    const RQArgs qa = hadamard_args(x, x_dtype, M, K, stride_m, stride_k, g, sign_in, sign_out, smooth, 127,
+                                    nullptr, nullptr, nullptr);
+    return linear8_impl(qa, true, w, N, w_scale, w_scale_dtype, bias, out, out_dtype, workspace,
+                        workspace_bytes, stream);
 }
 
 int w4a4_linear_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,

@@ -73,7 +73,6 @@ __device__ __forceinline__ void store_any(int dt, void* p, int64_t i, float v)
     else ((uint16_t*)p)[i] = f32_to_bf16(v);
 }
 
-// IEEE-exact fp32 multiply and add (never contracted into an FMA).
 // Non-temporal (streaming) stores for outputs that no later kernel of the
 // same call reads back soon: codes and exported rotated values are written
 // once and would otherwise displace the input rows still to be read from the
@@ -90,6 +89,7 @@ __device__ __forceinline__ void st_stream8(void* p, uint32_t a, uint32_t b)
     __builtin_nontemporal_store((v2u_st){a, b}, (v2u_st*)p);
 }
 
+// IEEE-exact fp32 multiply and add (never contracted into an FMA).
 __device__ __forceinline__ float mul_rn(float a, float b) { return __fmul_rn(a, b); }
 __device__ __forceinline__ float add_rn(float a, float b) { return __fadd_rn(a, b); }
 

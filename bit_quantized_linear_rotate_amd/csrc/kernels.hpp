@@ -17,6 +17,11 @@ struct RQArgs {
     float* scales;          // (M,)
     void* yout;             // (M, K) in dtype or nullptr
     int qmax = 7;           // 7: INT4 codes; 127: the INT8 mode
+    // structured rotation (rot unused): R = diag(sign_in) H_g diag(sign_out) / sqrt(g),
+    // signs +-1 as int8 (g,) on the device, NULL for all +1
+    int hadamard = 0;
+    const int8_t* sign_in = nullptr;
+    const int8_t* sign_out = nullptr;
 };
 
 // The kernel that launch_rotate_quant takes for these arguments (>= 0), or -1
@@ -26,6 +31,9 @@ int rotate_quant_path(const RQArgs& a);
 bool row_kernel_ok(const RQArgs& a);
 hipError_t launch_rotate_quant_row(const RQArgs& a, hipStream_t st);
 hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path);
+// the fast Walsh-Hadamard kernel for a.hadamard (contiguous 16-bit rows)
+bool hadamard_kernel_ok(const RQArgs& a);
+hipError_t launch_rotate_quant_hadamard(const RQArgs& a, hipStream_t st);
 
 struct GemmArgs {
     const int8_t* codes;    // (M, K) row-major

@@ -1888,6 +1888,8 @@ static bool colmajor_ok(const RQArgs& a)
 // when none does (a row too long for the generic kernel's LDS buffer).
 int rotate_quant_path(const RQArgs& a)
 {
+    // structured (Hadamard) rotation: the fast Walsh-Hadamard kernel only
+    if (a.hadamard) return hadamard_kernel_ok(a) ? 7 : -1;
     // INT8 mode: the row-streaming and g = 256 kernels, else the generic one
     if (a.qmax == 127) {
         if (g256_ok(a)) return 5;
@@ -1947,6 +1949,7 @@ hipError_t launch_rotate_quant(const RQArgs& a, hipStream_t st, int* path)
     const bool bf = a.dtype == BF16;
     const int GP = a.rot ? (a.g < 32 ? 32 : a.g) : 32;
     const bool contig = a.sk == 1 && (a.sm % 8) == 0 && ((uintptr_t)a.x % 16) == 0;
+    if (p == 7) return launch_rotate_quant_hadamard(a, st);
     if (a.qmax == 127) {
         switch (p) {
         case 5: return bf ? launch_g256_dt<BF16, 127>(a, st) : launch_g256_dt<F16, 127>(a, st);

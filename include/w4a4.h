@@ -188,6 +188,53 @@ int w8a8_gemm_plan(const int8_t* codes, int64_t M, int64_t K, const int8_t* w, i
                    const void* out, int* kernel);
 
 /*
+ * Structured rotation (fast Walsh-Hadamard transform).  The rotation is given
+ * by its structure instead of its entries:
+ *   R = diag(sign_in) . H_g . diag(sign_out) . T(1 / sqrt(g)),
+ * H_g the Sylvester Hadamard matrix (H_1 = [1], H_2n = [[H_n, H_n],
+ * [H_n, -H_n]]), i.e. the normalized Hadamard rotation with random signs on
+ * either side.  Every other step is that of the dense calls above
+ * ("[Feat][Ascend] Add fused RotateQuant backend", "What this PR does / why
+ * we need it" and "How was this patch tested?": group sizes and asymmetric
+ * rotations; "[Feat][Ascend] Consolidate INT8, RotateQuant, RoPE and ConvRot
+ * W4A4 backends", "W4A4 correctness and performance scope"); the result equals
+ * the dense call's with this R up to the order of the fp32 sum of the same
+ * exact products.
+ *   g:        16, 32, 64, 128 or 256; K a multiple of g, K <= 16384.
+ *   sign_in, sign_out: device int8 arrays of g entries, 8-byte aligned (a
+ *             negative entry is -1, any other +1), or NULL for all +1.  Read
+ *             by the kernel.
+ *   qmax:     7 (INT4 codes) or 127 (the INT8 mode).
+ *   Layout:   16-bit x with contiguous rows (stride_k == 1, stride_m a
+ *             multiple of 8, 16-byte aligned); other layouts and fp32 x are
+ *             W4A4_UNSUPPORTED (use the dense calls with R written out).
+ * w4a4_linear_hadamard / w8a8_linear_hadamard are w4a4_linear / w8a8_linear
+ * with this rotation (same workspace sizes).
+ */
+int w4a4_rotate_quant_hadamard(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                               int64_t stride_k, int32_t g, const int8_t* sign_in,
+                               const int8_t* sign_out, const void* smooth, int32_t qmax,
+                               int8_t* codes, float* scales, void* rotated_out, void* stream);
+/* host-only: 7 when w4a4_rotate_quant_hadamard takes its kernel for these
+ * arguments, W4A4_UNSUPPORTED otherwise */
+int w4a4_rotate_quant_hadamard_plan(const void* x, int x_dtype, int64_t M, int64_t K,
+                                    int64_t stride_m, int64_t stride_k, int32_t g,
+                                    const void* smooth, int32_t qmax, const int8_t* codes,
+                                    const void* rotated_out, int* kernel);
+int w4a4_linear_hadamard(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                         int64_t stride_k, int32_t g, const int8_t* sign_in,
+                         const int8_t* sign_out, const void* smooth, const uint8_t* w_packed,
+                         int64_t N, const void* w_scale, int w_scale_dtype,
+                         int32_t w_scale_group, const void* bias, const void* proj_down,
+                         const void* proj_up, int32_t rank, void* out, int out_dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+int w8a8_linear_hadamard(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                         int64_t stride_k, int32_t g, const int8_t* sign_in,
+                         const int8_t* sign_out, const void* smooth, const int8_t* w, int64_t N,
+                         const void* w_scale, int w_scale_dtype, const void* bias, void* out,
+                         int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * w4a4_linear for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same arguments without the workspace, and the same kernels, which work
@@ -234,6 +281,7 @@ int w4a4_int32_guard(int64_t K, int64_t* k_chunk);
  *   4 column-major (unit row stride, i.e. a transposed view; M % 8 == 0)
  *   5 g = 256 on contiguous rows
  *   6 one wave per contiguous row, g = 64, 16 < K/64 <= 64 (many rows)
+ *   7 fast Walsh-Hadamard transform (w4a4_rotate_quant_hadamard_plan only)
  * w4a4_gemm_plan, *kernel (has_lowrank: a low-rank term will be added):
  *   0 128 x 128 tiles          1 128 x 128 tiles over K chunks (int64 combine)
  *   2 persistent 256 x 256 ring (prefill-sized M)     3 skinny M (M <= 64)
