@@ -64,10 +64,13 @@ def lib() -> ctypes.CDLL:
         L.orc_lowrank_down.argtypes = [i32, vp, i64, i64, vp, i32, vp]
         L.orc_epilogue.argtypes = [vp, i64, i64, i64, i32, vp, vp, i32, vp, i32, vp, vp, i32,
                                    i32, vp, i32]
+        L.orc_shift.argtypes = [i32, vp, i64, i64, ctypes.c_double, vp]
+        L.orc_quantize_ex.argtypes = [i32, vp, i64, i64, i32, i32, vp, vp]
+        L.orc_epilogue_ag.argtypes = [vp, i64, i64, i64, vp, vp, i32, i32, vp, i32, vp, vp, i32, i32, vp, i32]
         L.orc_num_threads.argtypes = []
         for f in ("orc_round_to", "orc_decode", "orc_smooth", "orc_rotate", "orc_quantize", "orc_quantize_q",
                   "orc_unpack", "orc_pack", "orc_gemm", "orc_lowrank_down", "orc_epilogue",
-                  "orc_num_threads"):
+                  "orc_shift", "orc_quantize_ex", "orc_epilogue_ag", "orc_num_threads"):
             getattr(L, f).restype = ctypes.c_int
     return _lib
 
@@ -154,6 +157,32 @@ def quantize(y, dtype: str, qmax: int = 7) -> tuple:
     return codes, scales
 
 
+# the post-GELU shift of the SVDQuant page's act_unsigned layers
+GELU_UNSIGNED_SHIFT = 0.171875
+
+
+def shift(x, dtype: str, c: float = GELU_UNSIGNED_SHIFT) -> np.ndarray:
+    """T(fp32(x) + c): the act_unsigned main-path activation (reading R18)."""
+    x = _t(x, dtype)
+    M, K = x.shape
+    out = np.empty_like(x)
+    _check(lib().orc_shift(DT[dtype], _p(x), M, K, float(c), _p(out)), "shift")
+    return out
+
+
+def quantize_groups(y, dtype: str, unsigned: bool = False, group: int = 0) -> tuple:
+    """The INT4 quantizer per block of ``group`` entries of a row (0: the whole
+    row), signed [-7, 7] or on the unsigned grid [0, 15] (readings R18/R19).
+    Returns (codes int8 (M, K), scales fp32 (M, K/group) or (M,))."""
+    y = _t(y, dtype)
+    M, K = y.shape
+    codes = np.empty((M, K), dtype=np.int8)
+    scales = np.empty((M, K // group) if group else (M,), dtype=np.float32)
+    _check(lib().orc_quantize_ex(DT[dtype], _p(y), M, K, int(bool(unsigned)), int(group), _p(codes),
+                                 _p(scales)), "quantize_groups")
+    return codes, scales
+
+
 def unpack(w_packed, K: int) -> np.ndarray:
     wp = _c(w_packed, np.uint8)
     N = wp.shape[0]
@@ -212,6 +241,62 @@ def epilogue(acc, s_a, s_w, sw_dtype: str, out_dtype: str, bias=None, bias_dtype
                             DT[up_dtype] if up_dtype else 0, R, _p(out), DT[out_dtype])
     _check(rc, "epilogue")
     return out
+
+
+def epilogue_ag(acc, s_a, s_w, sw_dtype: str, out_dtype: str, sw_group: int = 0, bias=None,
+                bias_dtype=None, L=None, proj_up=None, up_dtype=None) -> np.ndarray:
+    """Epilogue with per-group activation scales s_a (M, G) on per-group sums
+    acc (M, G, N); s_w (N,) or (G, N) (reading R19)."""
+    acc = _c(acc, np.int64)
+    s_a = _c(s_a, np.float32)
+    s_w = _t(s_w, sw_dtype)
+    M, G, N = acc.shape
+    assert s_a.shape == (M, G)
+    bias = _t(bias, bias_dtype) if bias is not None else None
+    L = _c(L, np.float32) if L is not None else None
+    up = _t(proj_up, up_dtype) if proj_up is not None else None
+    R = 0 if L is None else L.shape[1]
+    out = np.empty((M, N), dtype=_NP[out_dtype])
+    _check(lib().orc_epilogue_ag(_p(acc), M, N, G, _p(s_a), _p(s_w), DT[sw_dtype], int(sw_group), _p(bias),
+                                 DT[bias_dtype] if bias_dtype else 0, _p(L), _p(up),
+                                 DT[up_dtype] if up_dtype else 0, R, _p(out), DT[out_dtype]), "epilogue_ag")
+    return out
+
+
+def linear_svdquant(x, w_packed, s_w, dtype: str, sw_dtype: str, sw_group: int = 64, smooth_factors=None,
+                    bias=None, proj_down=None, proj_up=None, act_unsigned: bool = False,
+                    act_group: int = 64, rows=None, cols=None) -> dict:
+    """The SVDQuant W4A4 layer of the svdquant page (``_w4a4_forward``):
+    main path x_main = shift(x) when act_unsigned, smoothed, quantized per
+    ``act_group`` (no rotation); the low-rank branch on the raw x; the exact
+    integer product; the epilogue with per-group activation scales (R19), or
+    the per-row epilogue (R9/R10) when act_group = 0.  Optional subsets of
+    rows and output columns."""
+    x = _t(x, dtype)
+    if rows is not None:
+        x = x[rows]
+    K = x.shape[1]
+    wq = unpack(w_packed, K)
+    if cols is not None:
+        wq = wq[cols]
+        s_w = np.asarray(s_w)[..., cols]
+        bias = np.asarray(bias)[cols] if bias is not None else None
+        proj_up = np.asarray(proj_up)[cols] if proj_up is not None else None
+    xm = shift(x, dtype) if act_unsigned else x
+    xs = smooth(xm, smooth_factors, dtype) if smooth_factors is not None else xm
+    codes, scales = quantize_groups(xs, dtype, act_unsigned, act_group)
+    L = lowrank_down(x, proj_down, dtype) if proj_down is not None else None
+    bd = dtype if bias is not None else None
+    ud = dtype if proj_up is not None else None
+    if act_group:
+        acc = gemm(codes, wq, act_group)
+        out = epilogue_ag(acc, scales, s_w, sw_dtype, dtype, sw_group, bias=bias, bias_dtype=bd, L=L,
+                          proj_up=proj_up, up_dtype=ud)
+    else:
+        acc = gemm(codes, wq, sw_group)
+        out = epilogue(acc, scales, s_w, sw_dtype, dtype, bias=bias, bias_dtype=bd, group=sw_group, L=L,
+                       proj_up=proj_up, up_dtype=ud)
+    return {"codes": codes, "scales": scales, "L": L, "out": out}
 
 
 def rotate_quant(x, R, g, dtype, smooth_factors=None, qmax: int = 7):

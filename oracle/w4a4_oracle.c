@@ -24,7 +24,7 @@
  * quotient, epilogue) are done in IEEE binary32.  Build with
  * -ffp-contract=off -fno-fast-math so that no multiply-add is fused.
  *
- * Readings of points the pages leave open (R1..R12) are stated at each step.
+ * Readings of points the pages leave open (R1..R19) are stated at each step.
  */
 #include <float.h>
 #include <math.h>
@@ -237,6 +237,74 @@ int orc_quantize(int dt, const void *y, int64_t M, int64_t K, int8_t *codes, flo
 }
 
 /* ------------------------------------------------------------------------ */
+/* SVDQuant activation quantizer ([P4] _w4a4_forward docstring: post-GELU    */
+/* layers flagged act_unsigned add the shift 0.171875 to the main-path       */
+/* activation so that it falls into the unsigned [0, 15] grid; the low-rank  */
+/* branch keeps the raw activation; module docstring: INT4 group size 64).   */
+/* Reading R18: the shifted activation is T(fp32(x) + 0.171875), one fp32    */
+/* add rounded to T, as an elementwise add of a scalar to a T tensor.        */
+/* ------------------------------------------------------------------------ */
+int orc_shift(int dt, const void *x, int64_t M, int64_t K, double c, void *out)
+{
+    const float fc = (float)c;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            float v = (float)load_T(dt, x, m * K + k) + fc;
+            store_T(dt, out, m * K + k, round_to(dt, (double)v));
+        }
+    return 0;
+}
+
+/* Readings R18/R19: the quantizer of a3/a4 applied to each block of `group`  */
+/* consecutive entries of a row (group = 0: the whole row), scales (M, K /   */
+/* group) row-major (or (M,)).  Signed: s = max(absmax / 7, 2^-126), codes   */
+/* clamp(rne(y / s), -7, 7).  Unsigned grid: s = max(absmax / 15, 2^-126),   */
+/* codes clamp(rne(y / s), 0, 15) (a value below zero gives 0).  NaN in a    */
+/* block makes its scale NaN and a NaN quotient gives code 0, as in a4.      */
+/* ------------------------------------------------------------------------ */
+int orc_quantize_ex(int dt, const void *y, int64_t M, int64_t K, int is_unsigned, int group,
+                    int8_t *codes, float *scales)
+{
+    if (group < 0 || (group > 0 && K % group)) return 1;
+    const int64_t glen = group > 0 ? group : K;
+    const int64_t G = group > 0 ? K / group : 1;
+    const float fq = is_unsigned ? 15.0f : 7.0f;
+    const float lo = is_unsigned ? 0.0f : -7.0f;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t gi = 0; gi < G; ++gi) {
+            const int64_t k0 = gi * glen;
+            float a = 0.0f;
+            int nan_blk = 0;
+            for (int64_t k = k0; k < k0 + glen; ++k) {
+                float v = (float)load_T(dt, y, m * K + k);
+                if (isnan(v)) nan_blk = 1;
+                else if (fabsf(v) > a) a = fabsf(v);
+            }
+            float s;
+            if (nan_blk) s = NAN;
+            else {
+                s = a / fq;
+                if (s < FLT_MIN) s = FLT_MIN;
+            }
+            scales[m * G + gi] = s;
+            for (int64_t k = k0; k < k0 + glen; ++k) {
+                float q = (float)load_T(dt, y, m * K + k) / s;
+                int8_t c = 0;
+                if (!isnan(q)) {
+                    float r = nearbyintf(q);
+                    if (r > fq) r = fq;
+                    if (r < lo) r = lo;
+                    c = (int8_t)r;
+                }
+                codes[m * K + k] = c;
+            }
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* a6  Weight nibble unpack ([P1] W4A4 scope: the W4 codes are unpacked to   */
 /* INT8; [P4] module docstring: qweight is (N, K/2) packed).                 */
 /* Reading R6: byte j of a row holds k = 2j in its low nibble and k = 2j+1   */
@@ -351,6 +419,42 @@ int orc_epilogue(const int64_t *acc, int64_t M, int64_t N, int64_t G, int group,
                 t = t * sa[m];
                 t = t * (float)load_T(sw_dt, sw, n);
             }
+            if (L && up) {
+                double s = 0.0;
+                for (int r = 0; r < R; ++r) s += (double)L[m * R + r] * load_T(up_dt, up, (int64_t)n * R + r);
+                float l = (float)round_to(ORC_F32, s);
+                t = t + l;
+            }
+            if (bias) t = t + (float)load_T(bias_dt, bias, n);
+            store_T(out_dt, out, m * N + n, round_to(out_dt, (double)t));
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Epilogue with per-group activation scales (reading R19, [P4]: the SVDQuant */
+/* kernel takes activation scales `ascales` with the INT4 group size 64).    */
+/* acc (M, G, N) per-group sums; sa (M, G).  With per-group weight scales:   */
+/* t = sum over G in increasing K order of (fp32(acc_G) * sa[m][G]) *        */
+/* sw[G][n]; with per-channel weight scales: t = (sum over G of fp32(acc_G)  */
+/* * sa[m][G]) * sw[n].  Each product and sum is a separately rounded fp32   */
+/* operation; the low-rank term and the bias follow as in the epilogue above. */
+/* ------------------------------------------------------------------------ */
+int orc_epilogue_ag(const int64_t *acc, int64_t M, int64_t N, int64_t G, const float *sa,
+                    const void *sw, int sw_dt, int sw_group, const void *bias, int bias_dt,
+                    const float *L, const void *up, int up_dt, int R, void *out, int out_dt)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            float t = 0.0f;
+            for (int64_t gi = 0; gi < G; ++gi) {
+                float a = (float)round_to(ORC_F32, (double)acc[(m * G + gi) * N + n]);
+                float p = a * sa[m * G + gi];
+                if (sw_group > 0) p = p * (float)load_T(sw_dt, sw, gi * N + n);
+                t = t + p;
+            }
+            if (sw_group == 0) t = t * (float)load_T(sw_dt, sw, n);
             if (L && up) {
                 double s = 0.0;
                 for (int r = 0; r < R; ++r) s += (double)L[m * R + r] * load_T(up_dt, up, (int64_t)n * R + r);
