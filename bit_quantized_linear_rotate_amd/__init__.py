@@ -29,5 +29,11 @@ from ._binding import (  # noqa: F401
     w4a4_rotate_quant_hadamard_plan,
     w4a4_linear_hadamard,
     w8a8_linear_hadamard,
+    w4a4_svdquant_workspace_size,
+    w4a4_quantize_svdquant,
+    w4a4_gemm_svdquant,
+    w4a4_linear_svdquant,
+    w4a4_linear_svdquant_grouped,
+    fuse_linear_weights,
     w8a8_rotate_quant_rowwise,
 )

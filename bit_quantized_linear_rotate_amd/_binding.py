@@ -59,6 +59,18 @@ _SIGNATURES = {
     "w8a8_linear_hadamard": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp,
                               _i64, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _sz, _vp],
                              ctypes.c_int),
+    "w4a4_svdquant_workspace_size": ([_i64, _i64, _i64, _i32, _i32, _i32], _sz),
+    "w4a4_quantize_svdquant": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _i32, _vp, _vp, _vp],
+                               ctypes.c_int),
+    "w4a4_gemm_svdquant": ([_vp, _vp, _i32, _i32, _i64, _i64, _vp, _i64, _vp, ctypes.c_int, _i32, _vp,
+                            ctypes.c_int, _vp, _vp, ctypes.c_int, _i32, _vp, ctypes.c_int, _vp, _sz, _vp],
+                           ctypes.c_int),
+    "w4a4_linear_svdquant": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _i32, _vp, _i64, _vp,
+                              ctypes.c_int, _i32, _vp, _vp, _vp, _i32, _vp, ctypes.c_int, _vp, _sz, _vp],
+                             ctypes.c_int),
+    "w4a4_linear_svdquant_grouped": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _i32, _vp, _i32,
+                                      _i32, _vp, _vp, _vp, ctypes.c_int, _i32, _vp, _vp, _vp, ctypes.c_int,
+                                      _vp, _sz, _vp], ctypes.c_int),
     "w4a4_linear_noalloc": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _i64,
                              _vp, ctypes.c_int, _i32, _vp, _vp, _vp, _i32, _vp, ctypes.c_int, _vp],
                             ctypes.c_int),
@@ -706,3 +718,191 @@ def w8a8_linear_hadamard(x: torch.Tensor, h: Hadamard, w: torch.Tensor, w_scale:
         _ptr(workspace), workspace.numel(), _stream(dev))
     _check(rc, "w8a8_linear_hadamard")
     return out.view(*lead, N)
+
+
+# ---- the SVDQuant variant ------------------------------------------------------
+
+def w4a4_svdquant_workspace_size(M: int, K: int, N: int, rank: int = 0, act_group: int = 64,
+                                 act_unsigned: bool = False) -> int:
+    return int(lib().w4a4_svdquant_workspace_size(M, K, N, rank, act_group, int(bool(act_unsigned))))
+
+
+def _svd_act(x, smooth, act_group):
+    x2 = _as_2d(_need(x, "x", contiguous=False))
+    M, K = x2.shape
+    _dt(x2)
+    if act_group not in (0, 64):
+        raise ValueError(f"act_group must be 0 or 64, got {act_group}")
+    if smooth is not None:
+        _need(smooth, "smooth", (K,), (x2.dtype,))
+    return x2, M, K
+
+
+def w4a4_quantize_svdquant(x: torch.Tensor, smooth: Optional[torch.Tensor] = None,
+                           act_unsigned: bool = False, act_group: int = 64):
+    """SVDQuant activation quantizer: (codes int8 (M, K), scales fp32 (M, K/64)
+    or (M,)); act_unsigned shifts by 0.171875 onto the unsigned grid [0, 15]."""
+    x2, M, K = _svd_act(x, smooth, act_group)
+    _same_device(x2, smooth=smooth)
+    dev = x2.device
+    codes = torch.empty((M, K), dtype=torch.int8, device=dev)
+    scales = torch.empty((M, K // 64) if act_group else (M,), dtype=torch.float32, device=dev)
+    rc = lib().w4a4_quantize_svdquant(_ptr(x2), _dt(x2), M, K, x2.stride(0), x2.stride(1), _ptr(smooth),
+                                      int(bool(act_unsigned)), act_group, _ptr(codes), _ptr(scales), _stream(dev))
+    _check(rc, "w4a4_quantize_svdquant")
+    return codes, scales
+
+
+def w4a4_gemm_svdquant(codes: torch.Tensor, scales: torch.Tensor, w_packed: torch.Tensor,
+                       w_scale: torch.Tensor, act_group: int = 64, act_unsigned: bool = False,
+                       w_scale_group: int = 64, bias: Optional[torch.Tensor] = None,
+                       lora_act: Optional[torch.Tensor] = None, proj_up: Optional[torch.Tensor] = None,
+                       out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """The SVDQuant GEMM and epilogue on quantized activations."""
+    _need(codes, "codes", dtypes=(torch.int8,))
+    if codes.dim() != 2:
+        raise ValueError(f"codes must be (M, K), got shape {tuple(codes.shape)}")
+    M, K = codes.shape
+    if act_group not in (0, 64):
+        raise ValueError(f"act_group must be 0 or 64, got {act_group}")
+    _need(scales, "scales", (M, K // 64) if act_group else (M,), (torch.float32,))
+    _need(w_packed, "w_packed", dtypes=(torch.uint8,))
+    if w_packed.dim() != 2 or w_packed.shape[1] * 2 != K:
+        raise ValueError(f"w_packed has shape {tuple(w_packed.shape)}, expected (N, {K // 2})")
+    N = w_packed.shape[0]
+    _need(w_scale, "w_scale", _wscale_shape(w_scale_group, K, N), _FLOAT)
+    if bias is not None:
+        _need(bias, "bias", (N,), _FLOAT)
+    rank = 0
+    if (lora_act is None) != (proj_up is None):
+        raise ValueError("lora_act and proj_up go together")
+    if lora_act is not None:
+        _need(lora_act, "lora_act", dtypes=(torch.float32,))
+        rank = lora_act.shape[1]
+        _need(proj_up, "proj_up", (N, rank), _FLOAT)
+    if out_dtype not in _FLOAT:
+        raise ValueError(f"out_dtype {out_dtype} is not float32/float16/bfloat16")
+    _same_device(codes, scales=scales, w_packed=w_packed, w_scale=w_scale, bias=bias, lora_act=lora_act,
+                 proj_up=proj_up)
+    dev = codes.device
+    out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    need = w4a4_svdquant_workspace_size(M, K, N, 0, act_group, act_unsigned) - \
+        w4a4_svdquant_workspace_size(M, K, 0, 0, act_group, act_unsigned) if w_scale_group == 0 else 0
+    ws = torch.empty((need,), dtype=torch.uint8, device=dev) if need > 0 else None
+    rc = lib().w4a4_gemm_svdquant(
+        _ptr(codes), _ptr(scales), act_group, int(bool(act_unsigned)), M, K, _ptr(w_packed), N, _ptr(w_scale),
+        _dt(w_scale), w_scale_group, _ptr(bias), _dt(bias) if bias is not None else 0, _ptr(lora_act),
+        _ptr(proj_up), _dt(proj_up) if proj_up is not None else 0, rank, _ptr(out), _DT[out_dtype], _ptr(ws),
+        need, _stream(dev))
+    _check(rc, "w4a4_gemm_svdquant")
+    return out
+
+
+def w4a4_linear_svdquant_grouped(x: torch.Tensor, projections, smooth: Optional[torch.Tensor] = None,
+                                 proj_down: Optional[torch.Tensor] = None, act_unsigned: bool = False,
+                                 act_group: int = 64, w_scale_group: int = 64,
+                                 out_dtype: Optional[torch.dtype] = None,
+                                 workspace: Optional[torch.Tensor] = None):
+    """Split projections of one activation sharing smoothing and proj_down
+    (e.g. Q/K/V): quantized and projected down once, then one GEMM each.
+    ``projections``: sequence of dicts with w_packed, w_scale and optional bias
+    and proj_up.  Returns one (..., N_i) output per projection."""
+    lead = _need(x, "x", contiguous=False).shape[:-1]
+    x2, M, K = _svd_act(x, smooth, act_group)
+    out_dtype = out_dtype or x2.dtype
+    if out_dtype not in _FLOAT:
+        raise ValueError(f"out_dtype {out_dtype} is not float32/float16/bfloat16")
+    projections = list(projections)
+    if not projections:
+        return ()
+    rank = 0
+    if proj_down is not None:
+        _need(proj_down, "proj_down", dtypes=(x2.dtype,))
+        if proj_down.dim() != 2 or proj_down.shape[0] != K:
+            raise ValueError(f"proj_down has shape {tuple(proj_down.shape)}, expected ({K}, R)")
+        rank = proj_down.shape[1]
+    ws_dtype = None
+    Ns, outs = [], []
+    for i, p in enumerate(projections):
+        wp, sw = p["w_packed"], p["w_scale"]
+        _need(wp, f"w_packed[{i}]", dtypes=(torch.uint8,))
+        if wp.dim() != 2 or wp.shape[1] * 2 != K:
+            raise ValueError(f"w_packed[{i}] has shape {tuple(wp.shape)}, expected (N, {K // 2})")
+        N = wp.shape[0]
+        _need(sw, f"w_scale[{i}]", _wscale_shape(w_scale_group, K, N), _FLOAT)
+        if ws_dtype is None:
+            ws_dtype = sw.dtype
+        elif sw.dtype != ws_dtype:
+            raise ValueError("every projection's w_scale must have the same dtype")
+        if p.get("bias") is not None:
+            _need(p["bias"], f"bias[{i}]", (N,), (x2.dtype,))
+        up = p.get("proj_up")
+        if (up is None) != (proj_down is None):
+            raise ValueError(f"projection {i}: proj_down and proj_up go together")
+        if up is not None:
+            _need(up, f"proj_up[{i}]", (N, rank), (x2.dtype,))
+        _same_device(x2, w_packed=wp, w_scale=sw, bias=p.get("bias"), proj_up=up)
+        Ns.append(N)
+        outs.append(torch.empty((M, N), dtype=out_dtype, device=x2.device))
+    _same_device(x2, smooth=smooth, proj_down=proj_down, workspace=workspace)
+    need = w4a4_svdquant_workspace_size(M, K, max(Ns), rank, act_group, act_unsigned)
+    if workspace is not None:
+        _need(workspace, "workspace", dtypes=(torch.uint8,))
+        if workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, need {need}")
+    else:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x2.device)
+    n = len(projections)
+    P = ctypes.c_void_p * n
+    wps = P(*[p["w_packed"].data_ptr() for p in projections])
+    sws = P(*[p["w_scale"].data_ptr() for p in projections])
+    bs = P(*[(p["bias"].data_ptr() if p.get("bias") is not None else None) for p in projections])
+    ups = P(*[(p["proj_up"].data_ptr() if p.get("proj_up") is not None else None) for p in projections])
+    os_ = P(*[o.data_ptr() for o in outs])
+    Narr = (ctypes.c_int64 * n)(*Ns)
+    rc = lib().w4a4_linear_svdquant_grouped(
+        _ptr(x2), _dt(x2), M, K, x2.stride(0), x2.stride(1), _ptr(smooth), int(bool(act_unsigned)), act_group,
+        _ptr(proj_down), rank, n, wps, Narr, sws, _DT[ws_dtype], w_scale_group, bs, ups, os_, _DT[out_dtype],
+        _ptr(workspace), workspace.numel(), _stream(x2.device))
+    _check(rc, "w4a4_linear_svdquant_grouped")
+    return tuple(o.view(*lead, N) for o, N in zip(outs, Ns))
+
+
+def w4a4_linear_svdquant(x: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor,
+                         w_scale_group: int = 64, bias: Optional[torch.Tensor] = None,
+                         smooth: Optional[torch.Tensor] = None, proj_down: Optional[torch.Tensor] = None,
+                         proj_up: Optional[torch.Tensor] = None, act_unsigned: bool = False,
+                         act_group: int = 64, out_dtype: Optional[torch.dtype] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The SVDQuant W4A4 layer (one projection)."""
+    return w4a4_linear_svdquant_grouped(
+        x, [dict(w_packed=w_packed, w_scale=w_scale, bias=bias, proj_up=proj_up)], smooth=smooth,
+        proj_down=proj_down, act_unsigned=act_unsigned, act_group=act_group, w_scale_group=w_scale_group,
+        out_dtype=out_dtype, workspace=workspace)[0]
+
+
+def fuse_linear_weights(projections, w_scale_group: int = 64):
+    """Runtime N-fusion of split projections that share their activation
+    side: concatenates w_packed (N_i, K/2), w_scale (along N), bias (zeros
+    where a projection has none) and proj_up along N, so that the projections
+    run as one wider layer.  Returns (fused dict, out_features); split the
+    fused output with ``torch.split(out, out_features, dim=-1)``.  Weight
+    preparation, done once; nothing of the layer's arithmetic happens here."""
+    projections = list(projections)
+    if not projections:
+        raise ValueError("expected at least one projection")
+    feats = tuple(int(p["w_packed"].shape[0]) for p in projections)
+    wp = torch.cat([p["w_packed"] for p in projections], dim=0).contiguous()
+    sw = torch.cat([p["w_scale"] for p in projections], dim=1 if w_scale_group else 0).contiguous()
+    fused = dict(w_packed=wp, w_scale=sw, bias=None, proj_up=None)
+    if any(p.get("bias") is not None for p in projections):
+        ref = next(p["bias"] for p in projections if p.get("bias") is not None)
+        fused["bias"] = torch.cat([p["bias"] if p.get("bias") is not None else
+                                   torch.zeros(n, dtype=ref.dtype, device=ref.device)
+                                   for p, n in zip(projections, feats)]).contiguous()
+    ups = [p.get("proj_up") for p in projections]
+    if any(u is not None for u in ups):
+        if any(u is None for u in ups):
+            raise ValueError("either every projection has proj_up or none")
+        fused["proj_up"] = torch.cat(ups, dim=0).contiguous()
+    return fused, feats

@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a4.so")
 PROBE_LIB = os.path.join(HERE, "libw4a4_probe.so")
-SOURCES = ["api.hip", "rotate_quant.hip", "rq_row.hip", "rq_hadamard.hip", "gemm.hip", "lowrank.hip"]
+SOURCES = ["api.hip", "rotate_quant.hip", "rq_row.hip", "rq_hadamard.hip", "rq_svdquant.hip", "gemm.hip",
+           "lowrank.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

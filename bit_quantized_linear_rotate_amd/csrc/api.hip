@@ -275,6 +275,52 @@ int linear8_impl(RQArgs qa, bool rotated, const int8_t* w, int64_t N, const void
     return W4A4_OK;
 }
 
+// ---- SVDQuant variant: validation, K-chunk guard, workspace -------------
+
+int64_t svd_chunk(int64_t K, int act_group, int w_scale_group, int act_unsigned)
+{
+    // per-group conversions (either side grouped) never overflow INT32
+    if (act_group || w_scale_group) return 0;
+    const int64_t lim = act_unsigned ? kGemmMaxKU : kGemmMaxK;
+    return K > lim ? lim : 0;
+}
+
+size_t svd_workspace(int64_t M, int64_t K, int64_t N, int rank, int act_group, int act_unsigned)
+{
+    if (M <= 0) return 0;
+    size_t s = align256((size_t)M * (size_t)K);                                 // codes
+    s += align256((size_t)M * (size_t)(act_group ? K / 64 : 1) * 4);            // scales
+    if (rank > 0) s += align256((size_t)M * rank * 4);                          // lora_act
+    if (N > 0 && svd_chunk(K, act_group, 0, act_unsigned) > 0) s += align256((size_t)M * (size_t)N * 8);
+    return s;
+}
+
+int svd_act_validate(const void* x, int dt, int64_t M, int64_t K, int64_t sm, int64_t sk, int act_unsigned,
+                     int act_group)
+{
+    int rc = check_activation(x, dt, M, K, sm, sk, true);
+    if (rc) return rc;
+    if (act_unsigned != 0 && act_unsigned != 1) return fail(W4A4_INVALID, "act_unsigned must be 0 or 1");
+    if (act_group != 0 && act_group != 64) return fail(W4A4_INVALID, "act_group must be 0 or 64");
+    if (act_group && K % 64) return fail(W4A4_INVALID, "K=%lld is not a multiple of 64", (long long)K);
+    if (M > 0 && K == 0) return fail(W4A4_INVALID, "K=0 with M>0");
+    return W4A4_OK;
+}
+
+// one projection of the SVDQuant layer on prepared codes / scales / lora
+int svd_gemm(const int8_t* codes, const float* scales, int act_group, int act_unsigned, int64_t M, int64_t K,
+             const uint8_t* w_packed, int64_t N, const void* w_scale, int sw_dt, int sw_group, const void* bias,
+             int bias_dt, const float* lora, const void* up, int up_dt, int rank, void* out, int out_dt,
+             int64_t* acc64, hipStream_t st)
+{
+    const int64_t kc = svd_chunk(K, act_group, sw_group, act_unsigned);
+    GemmArgs ga{codes, scales, M, K, N, w_packed, w_scale, sw_dt, sw_group, bias, bias_dt, lora, up, up_dt,
+                lora ? rank : 0, out, out_dt, nullptr, kc, kc > 0 ? acc64 : nullptr};
+    ga.sa_group = act_group;
+    const hipError_t e = launch_gemm(ga, st);
+    return e == hipSuccess ? W4A4_OK : hip_fail(e, "gemm launch");
+}
+
 // rotate-quant entry (both code ranges) given its arguments
 int rq_impl(const RQArgs& a, bool rotated, void* stream)
 {
@@ -574,6 +620,139 @@ int w8a8_linear_hadamard(const void* x, int x_dtype, int64_t M, int64_t K, int64
                                     nullptr, nullptr, nullptr);
     return linear8_impl(qa, true, w, N, w_scale, w_scale_dtype, bias, out, out_dtype, workspace,
                         workspace_bytes, stream);
+}
+
+// ---- the SVDQuant layer: shift, per-group activation scales, grouped ------
+
+size_t w4a4_svdquant_workspace_size(int64_t M, int64_t K, int64_t N, int32_t rank, int32_t act_group,
+                                    int32_t act_unsigned)
+{
+    return svd_workspace(M, K, N, rank, act_group, act_unsigned);
+}
+
+int w4a4_quantize_svdquant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                           int64_t stride_k, const void* smooth, int32_t act_unsigned, int32_t act_group,
+                           int8_t* codes, float* scales, void* stream)
+{
+    int rc = svd_act_validate(x, x_dtype, M, K, stride_m, stride_k, act_unsigned, act_group);
+    if (rc) return rc;
+    if (M > 0 && (!codes || !scales)) return fail(W4A4_INVALID, "codes/scales is NULL");
+    if (M == 0) return W4A4_OK;
+    RQArgs a{x, x_dtype, M, K, stride_m, stride_k, nullptr, 0, smooth, codes, scales, nullptr};
+    if (!svd_quant_ok(a, act_group))
+        return fail(W4A4_UNSUPPORTED, "no SVDQuant quantizer for this dtype, layout or width (K=%lld)", (long long)K);
+    rc = device_check();
+    if (rc) return rc;
+    const hipError_t e = launch_svd_quant(a, act_group, act_unsigned != 0, (hipStream_t)stream);
+    return e == hipSuccess ? W4A4_OK : hip_fail(e, "svdquant quantizer launch");
+}
+
+int w4a4_gemm_svdquant(const int8_t* codes, const float* scales, int32_t act_group, int32_t act_unsigned,
+                       int64_t M, int64_t K, const uint8_t* w_packed, int64_t N, const void* w_scale,
+                       int w_scale_dtype, int32_t w_scale_group, const void* bias, int bias_dtype,
+                       const float* lora_act, const void* proj_up, int up_dtype, int32_t rank, void* out,
+                       int out_dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc = gemm_validate(codes, scales, M, K, w_packed, N, w_scale, w_scale_dtype, w_scale_group, bias,
+                           bias_dtype, lora_act, proj_up, up_dtype, rank, out, out_dtype, 0);
+    if (rc) return rc;
+    if (act_unsigned != 0 && act_unsigned != 1) return fail(W4A4_INVALID, "act_unsigned must be 0 or 1");
+    if (act_group != 0 && act_group != 64) return fail(W4A4_INVALID, "act_group must be 0 or 64");
+    if (act_group && K % 64) return fail(W4A4_INVALID, "K=%lld is not a multiple of 64", (long long)K);
+    if (M == 0 || N == 0) return W4A4_OK;
+    const int64_t kc = svd_chunk(K, act_group, w_scale_group, act_unsigned);
+    const size_t need = kc > 0 ? align256((size_t)M * (size_t)N * 8) : 0;
+    if (workspace_bytes < need || (need && !workspace))
+        return fail(W4A4_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    rc = device_check();
+    if (rc) return rc;
+    return svd_gemm(codes, scales, act_group, act_unsigned, M, K, w_packed, N, w_scale, w_scale_dtype,
+                    w_scale_group, bias, bias_dtype, lora_act, proj_up, up_dtype, rank, out, out_dtype,
+                    (int64_t*)workspace, (hipStream_t)stream);
+}
+
+int w4a4_linear_svdquant_grouped(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                                 int64_t stride_k, const void* smooth, int32_t act_unsigned, int32_t act_group,
+                                 const void* proj_down, int32_t rank, int32_t nproj,
+                                 const uint8_t* const* w_packed, const int64_t* N, const void* const* w_scale,
+                                 int w_scale_dtype, int32_t w_scale_group, const void* const* bias,
+                                 const void* const* proj_up, void* const* out, int out_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream)
+{
+    // Validate everything before the first launch.
+    int rc = svd_act_validate(x, x_dtype, M, K, stride_m, stride_k, act_unsigned, act_group);
+    if (rc) return rc;
+    if (nproj < 1) return fail(W4A4_INVALID, "nproj=%d", nproj);
+    if (!w_packed || !N || !w_scale || !out) return fail(W4A4_INVALID, "a projection array is NULL");
+    const int r = proj_down ? rank : 0;
+    if (proj_down && (rank < 1 || rank > 64)) return fail(W4A4_INVALID, "rank=%d outside [1, 64]", rank);
+    int64_t maxN = 0;
+    for (int i = 0; i < nproj; ++i) {
+        const void* up = proj_up ? proj_up[i] : nullptr;
+        if ((proj_down == nullptr) != (up == nullptr))
+            return fail(W4A4_INVALID, "projection %d: proj_down and proj_up go together", i);
+        rc = gemm_validate((const int8_t*)1, (const float*)1, M, K, w_packed[i], N[i], w_scale[i], w_scale_dtype,
+                           w_scale_group, bias ? bias[i] : nullptr, x_dtype, r ? (const float*)1 : nullptr, up,
+                           x_dtype, r, out[i], out_dtype, 0);
+        if (rc) return rc;
+        maxN = N[i] > maxN ? N[i] : maxN;
+    }
+    if (M == 0) return W4A4_OK;
+    const size_t need = svd_workspace(M, K, maxN, r, act_group, act_unsigned);
+    if (!workspace || workspace_bytes < need)
+        return fail(W4A4_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    uint8_t* ws = (uint8_t*)workspace;
+    int8_t* codes = (int8_t*)ws;
+    ws += align256((size_t)M * (size_t)K);
+    float* scales = (float*)ws;
+    ws += align256((size_t)M * (size_t)(act_group ? K / 64 : 1) * 4);
+    float* lora = nullptr;
+    if (r) {
+        lora = (float*)ws;
+        ws += align256((size_t)M * r * 4);
+    }
+    RQArgs qa{x, x_dtype, M, K, stride_m, stride_k, nullptr, 0, smooth, codes, scales, nullptr};
+    if (!svd_quant_ok(qa, act_group))
+        return fail(W4A4_UNSUPPORTED, "no SVDQuant quantizer for this dtype, layout or width (K=%lld)", (long long)K);
+    rc = device_check();
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (r) {
+        // the low-rank branch sees the raw activation (not shifted, not smoothed)
+        LowRankArgs la{x, x_dtype, M, K, stride_m, stride_k, proj_down, r, lora};
+        e = launch_lowrank_down(la, st);
+        if (e != hipSuccess) return hip_fail(e, "lowrank_down launch");
+    }
+    e = launch_svd_quant(qa, act_group, act_unsigned != 0, st);
+    if (e != hipSuccess) return hip_fail(e, "svdquant quantizer launch");
+    for (int i = 0; i < nproj; ++i) {
+        if (N[i] == 0) continue;
+        rc = svd_gemm(codes, scales, act_group, act_unsigned, M, K, w_packed[i], N[i], w_scale[i], w_scale_dtype,
+                      w_scale_group, bias ? bias[i] : nullptr, x_dtype, lora, proj_up ? proj_up[i] : nullptr,
+                      x_dtype, r, out[i], out_dtype, (int64_t*)ws, st);
+        if (rc) return rc;
+    }
+    return W4A4_OK;
+}
+
+int w4a4_linear_svdquant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m, int64_t stride_k,
+                         const void* smooth, int32_t act_unsigned, int32_t act_group, const uint8_t* w_packed,
+                         int64_t N, const void* w_scale, int w_scale_dtype, int32_t w_scale_group,
+                         const void* bias, const void* proj_down, const void* proj_up, int32_t rank, void* out,
+                         int out_dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (N < 0) return fail(W4A4_INVALID, "negative size");
+    if (N == 0) {
+        int rc = svd_act_validate(x, x_dtype, M, K, stride_m, stride_k, act_unsigned, act_group);
+        return rc;
+    }
+    const void* bb[1] = {bias};
+    const void* uu[1] = {proj_up};
+    void* oo[1] = {out};
+    return w4a4_linear_svdquant_grouped(x, x_dtype, M, K, stride_m, stride_k, smooth, act_unsigned, act_group,
+                                        proj_down, rank, 1, &w_packed, &N, &w_scale, w_scale_dtype,
+                                        w_scale_group, bb, uu, oo, out_dtype, workspace, workspace_bytes, stream);
 }
 
 int w4a4_linear_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,

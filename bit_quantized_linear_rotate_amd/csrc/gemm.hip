@@ -81,16 +81,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // GSW: -1 for one weight scale per column, else the dtype of the per-64-group
 // weight scales (F32, F16 or BF16)
-template <int GSW, bool SPLIT, bool ALIGNED, bool W8 = false>
+template <int GSW, bool SPLIT, bool ALIGNED, bool W8 = false, bool AG = false>
 __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
 {
     // W8: INT8 weights (N, K) taken as they are (no unpack, no factor 16)
     static_assert(!(W8 && GSW >= 0), "INT8 weights come with per-channel scales");
+    // AG: activation scales per row and 64-wide K group, sa (M, K / 64): every
+    // K step (one group) converts its INT32 tile and accumulates
+    // (f32(acc) * sa[row][g]) [* sw[g][col]] in fp32, in increasing g
+    static_assert(!(AG && (W8 || SPLIT)), "activation group scales: INT4 weights, whole K");
     constexpr int SHIFT = W8 ? 0 : 4;
     constexpr bool GROUP = GSW >= 0;
+    constexpr bool FACC = GROUP || AG;   // per-step fp32 accumulation
     __shared__ __align__(16) int8_t As[2][BM * LDR];
     __shared__ __align__(16) int8_t Bs[2][BN * LDR];
     __shared__ __align__(16) float Ss[GSW >= 0 ? 2 : 1][GSW >= 0 ? 256 : 4];
+    __shared__ __align__(16) float Sa[AG ? 2 : 1][AG ? BM : 4];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -227,12 +233,12 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
     };
 
     v4i acc[4][4];
-    v4f facc[GROUP ? 4 : 1][GROUP ? 4 : 1];
+    v4f facc[FACC ? 4 : 1][FACC ? 4 : 1];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = (v4i){0, 0, 0, 0};
-    if constexpr (GROUP) {
+    if constexpr (FACC) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -277,11 +283,29 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
                 Ss[buf][tid] = w;
             }
         };
+        // activation scales of the step's group for the tile's 128 rows:
+        // thread t loads row t mod 128 (threads 128..255 repeat them, no
+        // branch); rows past M read row M - 1 and steps past the end the last
+        // group (never used)
+        float rsa = 0.0f;
+        const int64_t sarow = min(m0 + (tid & 127), M - 1);
+        const int64_t G64 = (K + 63) / 64;
+        auto saload = [&](int step) {
+            if constexpr (AG) {
+                const int64_t gidx = min((kbeg + (int64_t)step * BK) / 64, G64 - 1);
+                rsa = a.sa[sarow * G64 + gidx];
+            }
+        };
+        auto sastore = [&](int buf) {
+            if constexpr (AG) Sa[buf][tid & 127] = rsa;
+        };
         if (nsteps > 0) {
             sgload(0);
+            saload(0);
             gload(kbeg);
             sstore(0);
             ssstore(0);
+            sastore(0);
         }
         __syncthreads();
         for (int s = 0; s < nsteps; ++s) {
@@ -289,6 +313,7 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
             // (past the last step the loads are masked off and the stores
             // fill the idle buffer with zeros: no branch in the loop)
             sgload(s + 1);
+            saload(s + 1);
             gload(kbeg + (int64_t)(s + 1) * BK);
             v4i af[4], bf[4];
 #pragma unroll
@@ -297,7 +322,25 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
                 bf[nt] = *(const v4i*)(&Bs[buf][(wn * 64 + nt * 16 + j) * LDR + q * 16]);
-            if constexpr (GROUP) {
+            if constexpr (AG) {
+                v4f swv = (v4f){1.f, 1.f, 1.f, 1.f};
+                if constexpr (GROUP) swv = *(const v4f*)(&Ss[buf][(wn * 16 + j) * 4]);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const v4f sav = *(const v4f*)(&Sa[buf][wm * 64 + mt * 16 + 4 * q]);
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) {
+                        v4i t = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt], bf[nt], (v4i){0, 0, 0, 0},
+                                                                      0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            float p = mul_rn((float)(t[r] >> SHIFT), sav[r]);
+                            if constexpr (GROUP) p = mul_rn(p, swv[nt]);
+                            facc[mt][nt][r] = add_rn(facc[mt][nt][r], p);
+                        }
+                    }
+                }
+            } else if constexpr (GROUP) {
                 const v4f swv = *(const v4f*)(&Ss[buf][(wn * 16 + j) * 4]);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
@@ -332,11 +375,12 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
             __builtin_amdgcn_sched_barrier(0);
             sstore(buf ^ 1);
             ssstore(buf ^ 1);
+            sastore(buf ^ 1);
             __syncthreads();
         }
         return exact;
     };
-    if constexpr (GROUP) {
+    if constexpr (GROUP && !AG) {
         if (__syncthreads_or(!kloop(std::true_type{}))) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
@@ -413,7 +457,12 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
                               (unsigned long long)(int64_t)(acc[mt][nt][r] >> SHIFT));
                 } else {
                     float t;
-                    if constexpr (GROUP) {
+                    if constexpr (AG) {
+                        // activation scales already applied per group; a
+                        // per-channel weight scale follows the sum
+                        t = facc[mt][nt][r];
+                        if constexpr (!GROUP) t = mul_rn(t, load_any_f32(a.sw_dtype, a.sw, col));
+                    } else if constexpr (GROUP) {
                         t = mul_rn(facc[mt][nt][r], a.sa[row]);
                     } else {
                         const int32_t iv = acc[mt][nt][r] >> SHIFT;
@@ -1004,6 +1053,9 @@ int gemm_path(const GemmArgs& a)
     const bool aligned = (a.K % 32) == 0 && ((uintptr_t)a.codes % 16) == 0 &&
                          ((uintptr_t)a.wp % 16) == 0;
     const bool group = a.sw_group > 0;
+    // activation scales per 64-wide group: the 128 x 128 kernel (no K chunks:
+    // every group's INT32 sums are converted at once)
+    if (a.sa_group) return kGemmTile;
     // INT8 weights: the three-stage kernel (64-deep K steps) for
     // prefill-sized layers, else the 128 x 128 kernel
     if (a.w8) {
@@ -1103,6 +1155,23 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
     // (the aligned kernels without K-chunks stage through buffer loads that
     // need whole 64-deep K steps and 32-bit offsets within a 128-row tile)
     const bool aligned_buf = aligned && (a.K % 64) == 0 && a.K < (1 << 24);
+    if (a.sa_group) {
+#define W4A4_AG_LAUNCH(DT)                                                                                  \
+    do {                                                                                                    \
+        if (aligned_buf)                                                                                    \
+            hipLaunchKernelGGL((w4a4_gemm_kernel<DT, false, true, false, true>), dim3(gx, gy, 1), dim3(256), \
+                               0, st, a, kc);                                                               \
+        else                                                                                                \
+            hipLaunchKernelGGL((w4a4_gemm_kernel<DT, false, false, false, true>), dim3(gx, gy, 1),          \
+                               dim3(256), 0, st, a, kc);                                                    \
+    } while (0)
+        if (!group) W4A4_AG_LAUNCH(-1);
+        else if (a.sw_dtype == F32) W4A4_AG_LAUNCH(F32);
+        else if (a.sw_dtype == F16) W4A4_AG_LAUNCH(F16);
+        else W4A4_AG_LAUNCH(BF16);
+#undef W4A4_AG_LAUNCH
+        return hipGetLastError();
+    }
     if (group) {
 #define W4A4_GROUP_LAUNCH(DT)                                                                    \
     do {                                                                                         \

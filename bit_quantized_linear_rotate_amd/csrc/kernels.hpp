@@ -55,6 +55,7 @@ struct GemmArgs {
     int64_t k_chunk;        // > 0: accumulate K in chunks of this many (exact int64 combine)
     int64_t* acc64;         // workspace (M, N) int64 when k_chunk > 0
     int w8 = 0;             // 1: wp holds INT8 weights (N, K), codes up to +-127
+    int sa_group = 0;       // 64: sa holds (M, K/64) activation scales (K % 64 == 0)
 };
 
 // GEMM kernels, as gemm_path names them (host-only choice, no device access)
@@ -73,6 +74,11 @@ struct LowRankArgs {
 
 hipError_t launch_lowrank_down(const LowRankArgs& a, hipStream_t st);
 
+// SVDQuant activation quantizer (contiguous 16-bit rows, no rotation): shift
+// (act_unsigned), smoothing, INT4 codes per row or per 64-wide group
+bool svd_quant_ok(const RQArgs& a, int group);
+hipError_t launch_svd_quant(const RQArgs& a, int group, bool act_unsigned, hipStream_t st);
+
 // Largest K whose accumulation cannot overflow the kernel's INT32 registers.
 // The kernel accumulates 16 * c * w (weights are unpacked as 16 * w, which
 // needs no per-nibble sign extension), |c| <= 7 and |w| <= 8.
@@ -80,5 +86,7 @@ constexpr int64_t kGemmMaxK = (int64_t)2147483647 / (7 * 8 * 16) / 64 * 64;
 // The same for INT8 codes (|c| <= 127) and INT8 weights (|w| <= 128), which
 // the kernel multiplies as they are.
 constexpr int64_t kGemmMaxK8 = (int64_t)2147483647 / (127 * 128) / 64 * 64;
+// The same for codes on the unsigned grid [0, 15] with INT4 weights.
+constexpr int64_t kGemmMaxKU = (int64_t)2147483647 / (15 * 8 * 16) / 64 * 64;
 
 }  // namespace w4a4

@@ -235,6 +235,63 @@ int w8a8_linear_hadamard(const void* x, int x_dtype, int64_t M, int64_t K, int64
                          int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The SVDQuant variant of the layer (source page
+ * comfy_kitchen/tensor/svdquant_w4a4.py: module docstring, _w4a4_forward,
+ * svdquant_w4a4_grouped_linear): no rotation; optional smoothing; INT4
+ * activation codes with one scale per row (act_group 0) or per row and
+ * 64-wide K group (act_group 64, scales (M, K/64) row-major); act_unsigned = 1
+ * for post-GELU layers: the main path quantizes T(fp32(x) + 0.171875) on the
+ * unsigned grid [0, 15] (s = max(absmax / 15, 2^-126)), the low-rank branch
+ * sees the raw x.  Epilogue with group activation scales:
+ * t = sum_G (fp32(acc_G) * s_a[m][G]) * s_w[G][n] in increasing G (per-channel
+ * weights: t = (sum_G fp32(acc_G) * s_a[m][G]) * s_w[n]), then + low-rank term
+ * + bias as in w4a4_gemm_from_codes; with act_group 0 it is exactly that call's
+ * epilogue.
+ *   Layout: 16-bit x with contiguous rows (stride_k == 1, stride_m a multiple
+ *   of 8, 16-byte aligned), K <= 16384 (a multiple of 64 with act_group 64,
+ *   else of 8); other layouts are W4A4_UNSUPPORTED.
+ * w4a4_quantize_svdquant: codes (M, K) int8 (8-byte aligned) and scales.
+ * w4a4_gemm_svdquant: the GEMM and epilogue on such codes and scales; a
+ *   workspace of M*N*8 bytes only when act_group == 0, w_scale_group == 0 and
+ *   K exceeds the INT32-safe length (15 * 8 * 16 per product for unsigned
+ *   codes), else none.
+ * w4a4_linear_svdquant: the whole layer (low-rank down projection, quantizer,
+ *   GEMM), workspace of w4a4_svdquant_workspace_size(M, K, N, rank, act_group,
+ *   act_unsigned) bytes.
+ * w4a4_linear_svdquant_grouped: nproj projections of the same activation that
+ *   share smoothing and proj_down (split Q/K/V): the activation is quantized and
+ *   projected down once, then one GEMM per projection; per-projection host
+ *   arrays of device pointers w_packed[i] (N[i], K/2), w_scale[i], bias[i] and
+ *   proj_up[i] (either array may be NULL) and out[i] (M, N[i]); workspace of
+ *   w4a4_svdquant_workspace_size with N the largest N[i].
+ */
+size_t w4a4_svdquant_workspace_size(int64_t M, int64_t K, int64_t N, int32_t rank, int32_t act_group,
+                                    int32_t act_unsigned);
+int w4a4_quantize_svdquant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                           int64_t stride_k, const void* smooth, int32_t act_unsigned,
+                           int32_t act_group, int8_t* codes, float* scales, void* stream);
+int w4a4_gemm_svdquant(const int8_t* codes, const float* scales, int32_t act_group,
+                       int32_t act_unsigned, int64_t M, int64_t K, const uint8_t* w_packed,
+                       int64_t N, const void* w_scale, int w_scale_dtype, int32_t w_scale_group,
+                       const void* bias, int bias_dtype, const float* lora_act,
+                       const void* proj_up, int up_dtype, int32_t rank, void* out, int out_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int w4a4_linear_svdquant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                         int64_t stride_k, const void* smooth, int32_t act_unsigned,
+                         int32_t act_group, const uint8_t* w_packed, int64_t N, const void* w_scale,
+                         int w_scale_dtype, int32_t w_scale_group, const void* bias,
+                         const void* proj_down, const void* proj_up, int32_t rank, void* out,
+                         int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+int w4a4_linear_svdquant_grouped(const void* x, int x_dtype, int64_t M, int64_t K,
+                                 int64_t stride_m, int64_t stride_k, const void* smooth,
+                                 int32_t act_unsigned, int32_t act_group, const void* proj_down,
+                                 int32_t rank, int32_t nproj, const uint8_t* const* w_packed,
+                                 const int64_t* N, const void* const* w_scale, int w_scale_dtype,
+                                 int32_t w_scale_group, const void* const* bias,
+                                 const void* const* proj_up, void* const* out, int out_dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * w4a4_linear for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same arguments without the workspace, and the same kernels, which work
