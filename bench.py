@@ -27,7 +27,8 @@ p90; plus the average over one event pair around the back-to-back launches
 The line also carries the other four workloads (wide-K transposed-view fp16,
 decode-like M=32, tiny fp32, large-K with smoothing, per-64-group scales and a
 rank-32 term), each as a step and per kernel, and the INT8 mode (qmax = 127,
-INT8 weights) on the prefill and wide-K shapes.
+INT8 weights) on the prefill and wide-K shapes, and the SVDQuant variant (act_unsigned,
+per-64-group activation scales) on the low-rank shape.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload prefill]
                        [--no-cpu] [--no-extra] [--copy-calibration]
@@ -535,6 +536,137 @@ def measure_int8(name, steps, warmup, torch, np, w4, workloads, cpu=True):
     return res
 
 
+def measure_svdquant(steps, warmup, torch, np, w4, workloads, cpu=True):
+    """The SVDQuant variant on the low-rank workload's shape and inputs
+    (M=4096, K=16384, N=6144, bf16, smoothing, rank 32, per-64-group weight
+    scales), as a post-GELU layer: activations floored at -0.17, the
+    act_unsigned shift onto the unsigned grid, per-64-group activation
+    scales, no rotation.  Times the layer step (w4a4_linear_svdquant), the
+    quantizer alone and the GEMM alone; the CPU leg checks sampled rows
+    against the oracle first."""
+    from bit_quantized_linear_rotate_amd import _binding as b
+    w = workloads.WORKLOADS["lowrank"]
+    inp = workloads.generate(w)
+    M, K, N, R = w.M, w.K, w.N, w.rank
+    xf = np.maximum(workloads.storage_to_f32(inp["x"], w.dtype), np.float32(-0.17))
+    x_host = workloads.f32_to_storage(xf, w.dtype)
+
+    def d(a, dt=None):
+        a = np.ascontiguousarray(a)
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+    base = dict(x=d(x_host, w.dtype), w_packed=d(inp["w_packed"]), w_scale=d(inp["s_w"], w.sw_dtype),
+                smooth=d(inp["smooth"], w.dtype), down=d(inp["proj_down"], w.dtype), up=d(inp["proj_up"], w.dtype))
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(3)]
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in sets]
+    need = w4.w4a4_svdquant_workspace_size(M, K, N, R, 64, True)
+    wss = [torch.empty((need,), dtype=torch.uint8, device="cuda") for _ in sets]
+    qbufs = [(torch.empty((M, K), dtype=torch.int8, device="cuda"),
+              torch.empty((M, K // 64), dtype=torch.float32, device="cuda"),
+              torch.empty((M, R), dtype=torch.float32, device="cuda")) for _ in sets]
+    lib = w4.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        s_ = sets[i % 4]
+        w4.w4a4_linear_svdquant(s_["x"], s_["w_packed"], s_["w_scale"], 64, smooth=s_["smooth"],
+                                proj_down=s_["down"], proj_up=s_["up"], act_unsigned=True, act_group=64,
+                                workspace=wss[i % 4])
+
+    def quant(i):
+        s_ = sets[i % 4]
+        c, sc, _ = qbufs[i % 4]
+        x = s_["x"]
+        rc = lib.w4a4_quantize_svdquant(x.data_ptr(), 2, M, K, K, 1, s_["smooth"].data_ptr(), 1, 64,
+                                        c.data_ptr(), sc.data_ptr(), stream)
+        if rc:
+            b._check(rc, "w4a4_quantize_svdquant")
+
+    def gemm(i):
+        s_ = sets[i % 4]
+        c, sc, L = qbufs[i % 4]
+        rc = lib.w4a4_gemm_svdquant(c.data_ptr(), sc.data_ptr(), 64, 1, M, K, s_["w_packed"].data_ptr(), N,
+                                    s_["w_scale"].data_ptr(), 2, 64, None, 0, L.data_ptr(), s_["up"].data_ptr(),
+                                    2, R, outs[i % 4].data_ptr(), 2, None, 0, stream)
+        if rc:
+            b._check(rc, "w4a4_gemm_svdquant")
+
+    par = None
+    if cpu:
+        import oracle
+        quant(0)
+        qbufs[0][2].copy_(w4.w4a4_lowrank_down(sets[0]["x"], sets[0]["down"]))
+        gemm(0)
+        torch.cuda.synchronize()
+        rows = np.sort(np.random.default_rng(7).choice(M, 24, replace=False))
+
+        def host(t):
+            t = t.detach().cpu().contiguous()
+            return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+        gc, gs = host(qbufs[0][0])[rows], host(qbufs[0][1])[rows]
+        ref = oracle.linear_svdquant(x_host, inp["w_packed"], inp["s_w"], w.dtype, w.sw_dtype, 64, inp["smooth"],
+                                     None, inp["proj_down"], inp["proj_up"], act_unsigned=True, act_group=64,
+                                     rows=rows)
+        codes_ok = bool(np.array_equal(gc, ref["codes"]) and np.array_equal(gs.view(np.uint32),
+                                                                            ref["scales"].view(np.uint32)))
+        go = host(outs[0])[rows].astype(np.int64)
+        ro = ref["out"].astype(np.int64)
+        ia = np.where(go >= 0x8000, -(go - 0x8000), go)
+        ib = np.where(ro >= 0x8000, -(ro - 0x8000), ro)
+        ulp = np.abs(ia - ib)
+        # the low-rank term is an fp32 sum on the GPU (L over K, l over R)
+        # where the oracle rounds exact sums once: beyond one ulp an output
+        # must lie within those sums' fp32 error bounds
+        upv = np.abs(oracle.decode(w.dtype, inp["proj_up"]))
+        S = np.abs(oracle.decode(w.dtype, x_host[rows])) @ np.abs(oracle.decode(w.dtype, inp["proj_down"]))
+        bound = (R * 2.0 ** -23 * np.abs(ref["L"].astype(np.float64))) @ upv.T + (K * 2.0 ** -24 * S) @ upv.T
+        diff = np.abs(oracle.decode(w.dtype, host(outs[0])[rows]) - oracle.decode(w.dtype, ref["out"]))
+        ok = (ulp <= 1) | (diff <= bound)
+        par = {"rows": int(len(rows)), "cols": int(N), "codes_scales_bit_exact": codes_ok,
+               "out_bit_exact_frac": float((ulp == 0).mean()), "out_max_ulp": int(ulp.max()),
+               "out_beyond_1ulp_within_lowrank_bound": int(((ulp > 1) & ok).sum()),
+               "rule": "codes and scales bit-exact; outputs within 1 ulp, or within the fp32 summation "
+                       "bound of the low-rank term",
+               "pass": bool(codes_ok and ok.all())}
+        if not par["pass"]:
+            raise SystemExit(f"SVDQuant parity check failed: {par}")
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(steps):
+        step(i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    nk = max(steps, MIN_KERNEL_LAUNCHES)
+    for i in range(warmup):
+        quant(i)
+    t_q = _time_each(quant, nk, torch, np)
+    for i in range(warmup):
+        gemm(i)
+    t_g = _time_each(gemm, nk, torch, np)
+    q_bytes = M * K * 2 + K * 2 + M * K + M * (K // 64) * 4
+    ops = 2.0 * M * N * K
+    res = {"workload": f"SVDQuant layer, lowrank shape: M={M} K={K} N={N} bf16, act_unsigned shift, "
+                       f"per-64-group activation and weight scales, smoothing, rank {R}, no rotation",
+           "ms_per_step": ms_step, "tops": ops / (ms_step * 1e-3) / 1e12,
+           "quantizer": {"kernel": "rq_svd_kernel (group 64, unsigned grid)", **t_q,
+                         "GB_s": q_bytes / (t_q["ms_median"] * 1e-3) / 1e9,
+                         "frac_hbm": q_bytes / (t_q["ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "algorithmic_bytes": q_bytes},
+           "gemm": {"kernel": "w4a4_gemm_kernel (activation and weight group scales, low-rank term)", **t_g,
+                    "TOPS": ops / (t_g["ms_median"] * 1e-3) / 1e12,
+                    "frac_int8": ops / (t_g["ms_median"] * 1e-3) / 1e12 / INT8_PEAK_TOPS, "ops": ops}}
+    if par is not None:
+        res["parity"] = par
+    return res
+
+
 def stream_ceiling(w, steps, torch, np):
     """The HBM ceiling for rotate-quant's traffic on this device: a plain
     streaming kernel of this repository (bit_quantized_linear_rotate_amd/
@@ -822,6 +954,10 @@ def main():
             _, _, extras[name] = measure(name, max(10, args.steps // 2), args.warmup, torch, np, w4,
                                          workloads, cpu=cpu)
             print(f"# {name}: {extras[name]['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+        extras["svdquant_lowrank"] = measure_svdquant(max(10, args.steps // 2), args.warmup, torch, np, w4,
+                                                      workloads, cpu=cpu)
+        print(f"# svdquant lowrank: {extras['svdquant_lowrank']['ms_per_step']:.4f} ms/step", file=sys.stderr,
+              flush=True)
         for name in ("prefill", "widek"):
             extras["int8_" + name] = measure_int8(name, max(10, args.steps // 2), args.warmup, torch, np, w4,
                                                   workloads, cpu=cpu)
@@ -868,8 +1004,10 @@ def main():
     for name, extra in extras.items():
         line[name] = {"workload": extra["workload"], "ms_per_step": round(extra["ms_per_step"], 5),
                       "tops": round(extra["tops"], 2), "parity": extra.get("parity"),
-                      "rotate_quant": _rounded(extra["rotate_quant"]),
                       "gemm": _rounded(extra["gemm"])}
+        for part in ("rotate_quant", "quantizer"):
+            if part in extra:
+                line[name][part] = _rounded(extra[part])
         if "lowrank_down" in extra:
             line[name]["lowrank_down"] = _rounded(extra["lowrank_down"])
         if "hadamard" in extra:
