@@ -54,6 +54,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, published
+FP6_PEAK_TOPS = 10100.0        # MI355X dense FP6/FP4 MFMA, published
 MIN_KERNEL_LAUNCHES = 50
 TRAFFIC_FILES = {  # kernel source -> committed counter summary
     "gemm": ("bit_quantized_linear_rotate_amd/csrc/gemm.hip",
@@ -321,6 +322,8 @@ def measure(name, steps, warmup, torch, np, w4, workloads, cpu=True):
     }
     if par is not None:
         res["parity"] = par
+    if w.sw_group == 0 and rank == 0 and K % 128 == 0 and K >= 256 and M > 64:
+        res["fp6"] = _bf6_leg(w, sets, outs, qbufs, steps, warmup, torch, np, w4, ops)
     if not w.transposed and w.dtype != "f32":
         res["hadamard"] = _hadamard_leg(w, sets, outs, wss, qbufs, steps, warmup, torch, np, w4, b, stream,
                                         rq_bytes, qmax=7)
@@ -346,6 +349,60 @@ def measure(name, steps, warmup, torch, np, w4, workloads, cpu=True):
                                "frac_hbm": lrd_bytes / (t_lrd["ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                "algorithmic_bytes": lrd_bytes}
     return w, inp, res
+
+
+def _bf6_leg(w, sets, outs, qbufs, steps, warmup, torch, np, w4, ops):
+    """The same GEMM on the FP6 matrix cores: the codes just produced and the
+    weights as bf6 blocks (encoded once, outside the timed region), then the
+    whole layer through w4a4_linear_bf6 (rotate-quant, bf6 encoding, GEMM)."""
+    b6 = [(w4.w4a4_codes_to_bf6(c), sc, w4.w4a4_pack_weights_bf6(s["w_packed"]))
+          for (c, sc), s in zip(qbufs, sets)]
+    torch.cuda.synchronize()
+
+    from bit_quantized_linear_rotate_amd import _binding as b
+    lib = w4.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    M, K = sets[0]["x"].shape
+    N = sets[0]["w_packed"].shape[0]
+    odt = _dtcode(torch, outs[0])
+
+    def gemm(i):
+        c6, sc, w6 = b6[i % 4]
+        s = sets[i % 4]
+        bi = s["bias"]
+        rc = lib.w4a4_gemm_bf6(c6.data_ptr(), sc.data_ptr(), M, K, w6.data_ptr(), N, s["w_scale"].data_ptr(),
+                               _dtcode(torch, s["w_scale"]), bi.data_ptr() if bi is not None else None,
+                               _dtcode(torch, bi) if bi is not None else 0, outs[i % 4].data_ptr(), odt, stream)
+        if rc:
+            b._check(rc, "w4a4_gemm_bf6")
+    nk = max(steps, MIN_KERNEL_LAUNCHES)
+    for i in range(warmup):
+        gemm(i)
+    t = _time_each(gemm, nk, torch, np)
+    res = {"kernel": "w4a4_gemm_bf6_kernel (bf6 e3m2 operands, v_mfma_f32_16x16x128_f8f6f4)", **t,
+           "TOPS": ops / (t["ms_median"] * 1e-3) / 1e12,
+           "frac_int8_peak": ops / (t["ms_median"] * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+           "frac_fp6_peak": ops / (t["ms_median"] * 1e-3) / 1e12 / FP6_PEAK_TOPS}
+    need = w4.w4a4_linear_bf6_workspace_size(M, K)
+    wss = [torch.empty((need,), dtype=torch.uint8, device="cuda") for _ in sets]
+
+    def step(i):
+        s = sets[i % 4]
+        w4.w4a4_linear_bf6(s["x"], s["rot"], w.g, b6[i % 4][2], s["w_scale"], bias=s["bias"],
+                           smooth=s["smooth"], workspace=wss[i % 4], out=outs[i % 4])
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(steps):
+        step(i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    res["ms_per_step"] = e0.elapsed_time(e1) / steps
+    res["tops_step"] = ops / (res["ms_per_step"] * 1e-3) / 1e12
+    return res
 
 
 def _hadamard_leg(w, sets, outs, wss, qbufs, steps, warmup, torch, np, w4, b, stream, rq_bytes, qmax):
@@ -1001,6 +1058,8 @@ def main():
     }
     if "hadamard" in main_res:
         line["hadamard"] = _rounded(main_res["hadamard"])
+    if "fp6" in main_res:
+        line["fp6"] = _rounded(main_res["fp6"])
     for name, extra in extras.items():
         line[name] = {"workload": extra["workload"], "ms_per_step": round(extra["ms_per_step"], 5),
                       "tops": round(extra["tops"], 2), "parity": extra.get("parity"),
@@ -1012,6 +1071,8 @@ def main():
             line[name]["lowrank_down"] = _rounded(extra["lowrank_down"])
         if "hadamard" in extra:
             line[name]["hadamard"] = _rounded(extra["hadamard"])
+        if "fp6" in extra:
+            line[name]["fp6"] = _rounded(extra["fp6"])
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, inp, np)
     print(json.dumps(line), flush=True)

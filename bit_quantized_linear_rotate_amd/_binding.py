@@ -71,6 +71,13 @@ _SIGNATURES = {
     "w4a4_linear_svdquant_grouped": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _i32, _vp, _i32,
                                       _i32, _vp, _vp, _vp, ctypes.c_int, _i32, _vp, _vp, _vp, ctypes.c_int,
                                       _vp, _sz, _vp], ctypes.c_int),
+    "w4a4_codes_to_bf6": ([_vp, _i64, _i64, _vp, _vp], ctypes.c_int),
+    "w4a4_pack_weights_bf6": ([_vp, _i64, _i64, _vp, _vp], ctypes.c_int),
+    "w4a4_gemm_bf6": ([_vp, _vp, _i64, _i64, _vp, _i64, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, ctypes.c_int,
+                       _vp], ctypes.c_int),
+    "w4a4_linear_bf6_workspace_size": ([_i64, _i64], _sz),
+    "w4a4_linear_bf6": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _i64, _vp, ctypes.c_int,
+                         _vp, _vp, ctypes.c_int, _vp, _sz, _vp], ctypes.c_int),
     "w4a4_linear_noalloc": ([_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _i64,
                              _vp, ctypes.c_int, _i32, _vp, _vp, _vp, _i32, _vp, ctypes.c_int, _vp],
                             ctypes.c_int),
@@ -906,3 +913,104 @@ def fuse_linear_weights(projections, w_scale_group: int = 64):
             raise ValueError("either every projection has proj_up or none")
         fused["proj_up"] = torch.cat(ups, dim=0).contiguous()
     return fused, feats
+
+
+# ---- FP6 (bf6 e3m2) GEMM path ---------------------------------------------------
+
+def w4a4_codes_to_bf6(codes: torch.Tensor) -> torch.Tensor:
+    """int8 codes (M, K) in [-8, 8] -> bf6 blocks (M, K) uint8."""
+    _need(codes, "codes", dtypes=(torch.int8,))
+    if codes.dim() != 2:
+        raise ValueError(f"codes must be (M, K), got shape {tuple(codes.shape)}")
+    M, K = codes.shape
+    out = torch.empty((M, K), dtype=torch.uint8, device=codes.device)
+    _same_device(codes)
+    rc = lib().w4a4_codes_to_bf6(_ptr(codes), M, K, _ptr(out), _stream(codes.device))
+    _check(rc, "w4a4_codes_to_bf6")
+    return out
+
+
+def w4a4_pack_weights_bf6(w_packed: torch.Tensor) -> torch.Tensor:
+    """Packed INT4 weights (N, K/2) -> bf6 blocks (N, K) uint8 (once per layer)."""
+    _need(w_packed, "w_packed", dtypes=(torch.uint8,))
+    if w_packed.dim() != 2:
+        raise ValueError(f"w_packed must be (N, K/2), got shape {tuple(w_packed.shape)}")
+    N, K = w_packed.shape[0], 2 * w_packed.shape[1]
+    out = torch.empty((N, K), dtype=torch.uint8, device=w_packed.device)
+    _same_device(w_packed)
+    rc = lib().w4a4_pack_weights_bf6(_ptr(w_packed), N, K, _ptr(out), _stream(w_packed.device))
+    _check(rc, "w4a4_pack_weights_bf6")
+    return out
+
+
+def w4a4_gemm_bf6(codes6: torch.Tensor, scales: torch.Tensor, w6: torch.Tensor, w_scale: torch.Tensor,
+                  bias: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """The W4A4 GEMM + epilogue (per-channel weight scales) on the FP6 matrix
+    cores, from bf6 codes (M, K) and bf6 weights (N, K)."""
+    _need(codes6, "codes6", dtypes=(torch.uint8,))
+    _need(w6, "w6", dtypes=(torch.uint8,))
+    if codes6.dim() != 2 or w6.dim() != 2 or w6.shape[1] != codes6.shape[1]:
+        raise ValueError(f"codes6 {tuple(codes6.shape)} and w6 {tuple(w6.shape)} must be (M, K) and (N, K)")
+    M, K = codes6.shape
+    N = w6.shape[0]
+    _need(scales, "scales", (M,), (torch.float32,))
+    _need(w_scale, "w_scale", (N,), _FLOAT)
+    if bias is not None:
+        _need(bias, "bias", (N,), _FLOAT)
+    if out_dtype not in _FLOAT:
+        raise ValueError(f"out_dtype {out_dtype} is not float32/float16/bfloat16")
+    _same_device(codes6, scales=scales, w6=w6, w_scale=w_scale, bias=bias)
+    out = torch.empty((M, N), dtype=out_dtype, device=codes6.device)
+    rc = lib().w4a4_gemm_bf6(_ptr(codes6), _ptr(scales), M, K, _ptr(w6), N, _ptr(w_scale), _dt(w_scale),
+                             _ptr(bias), _dt(bias) if bias is not None else 0, _ptr(out), _DT[out_dtype],
+                             _stream(codes6.device))
+    _check(rc, "w4a4_gemm_bf6")
+    return out
+
+
+def w4a4_linear_bf6_workspace_size(M: int, K: int) -> int:
+    return int(lib().w4a4_linear_bf6_workspace_size(M, K))
+
+
+def w4a4_linear_bf6(x: torch.Tensor, rot: Optional[torch.Tensor], g: int, w6: torch.Tensor,
+                    w_scale: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                    smooth: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                    workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The W4A4 linear (per-channel weight scales) with the GEMM on the FP6
+    matrix cores; w6 from w4a4_pack_weights_bf6."""
+    lead = _need(x, "x", contiguous=False).shape[:-1]
+    x2 = _as_2d(x)
+    M, K = x2.shape
+    _dt(x2)
+    rot, g = _rot_arg(rot, g)
+    _need(w6, "w6", dtypes=(torch.uint8,))
+    if w6.dim() != 2 or w6.shape[1] != K:
+        raise ValueError(f"w6 has shape {tuple(w6.shape)}, expected (N, {K})")
+    N = w6.shape[0]
+    _need(w_scale, "w_scale", (N,), _FLOAT)
+    if bias is not None:
+        _need(bias, "bias", (N,), (x2.dtype,))
+    if smooth is not None:
+        _need(smooth, "smooth", (K,), (x2.dtype,))
+    out_dtype = out_dtype or (out.dtype if out is not None else x2.dtype)
+    if out_dtype not in _FLOAT:
+        raise ValueError(f"out_dtype {out_dtype} is not float32/float16/bfloat16")
+    if out is not None:
+        _need(out, "out", (M, N), (out_dtype,))
+    need = w4a4_linear_bf6_workspace_size(M, K)
+    if workspace is not None:
+        _need(workspace, "workspace", dtypes=(torch.uint8,))
+        if workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, need {need}")
+    _same_device(x2, rot=rot, w6=w6, w_scale=w_scale, bias=bias, smooth=smooth, out=out, workspace=workspace)
+    dev = x2.device
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    rc = lib().w4a4_linear_bf6(
+        _ptr(x2), _dt(x2), M, K, x2.stride(0), x2.stride(1), _ptr(rot), g, _ptr(smooth), _ptr(w6), N,
+        _ptr(w_scale), _dt(w_scale), _ptr(bias), _ptr(out), _DT[out.dtype], _ptr(workspace), workspace.numel(),
+        _stream(dev))
+    _check(rc, "w4a4_linear_bf6")
+    return out.view(*lead, N)

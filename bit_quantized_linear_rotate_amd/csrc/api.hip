@@ -755,6 +755,101 @@ int w4a4_linear_svdquant(const void* x, int x_dtype, int64_t M, int64_t K, int64
                                         w_scale_group, bb, uu, oo, out_dtype, workspace, workspace_bytes, stream);
 }
 
+// ---- FP6 (bf6 e3m2) GEMM path -------------------------------------------
+
+int w4a4_codes_to_bf6(const int8_t* codes, int64_t M, int64_t K, uint8_t* out, void* stream)
+{
+    if (M < 0 || K < 0) return fail(W4A4_INVALID, "negative size");
+    if (K % 32) return fail(W4A4_INVALID, "K=%lld is not a multiple of 32", (long long)K);
+    if (M > 0 && K > 0 && (!codes || !out)) return fail(W4A4_INVALID, "codes/out is NULL");
+    if (((uintptr_t)codes % 16) || ((uintptr_t)out % 16))
+        return fail(W4A4_UNSUPPORTED, "codes and out must be 16-byte aligned");
+    if (M == 0 || K == 0) return W4A4_OK;
+    int rc = device_check();
+    if (rc) return rc;
+    const hipError_t e = launch_to_bf6(codes, false, M * (K / 32), out, (hipStream_t)stream);
+    return e == hipSuccess ? W4A4_OK : hip_fail(e, "bf6 encoder launch");
+}
+
+int w4a4_pack_weights_bf6(const uint8_t* w_packed, int64_t N, int64_t K, uint8_t* out, void* stream)
+{
+    if (N < 0 || K < 0) return fail(W4A4_INVALID, "negative size");
+    if (K % 32) return fail(W4A4_INVALID, "K=%lld is not a multiple of 32", (long long)K);
+    if (N > 0 && K > 0 && (!w_packed || !out)) return fail(W4A4_INVALID, "w_packed/out is NULL");
+    if (((uintptr_t)w_packed % 16) || ((uintptr_t)out % 16))
+        return fail(W4A4_UNSUPPORTED, "w_packed and out must be 16-byte aligned");
+    if (N == 0 || K == 0) return W4A4_OK;
+    int rc = device_check();
+    if (rc) return rc;
+    const hipError_t e = launch_to_bf6(w_packed, true, N * (K / 32), out, (hipStream_t)stream);
+    return e == hipSuccess ? W4A4_OK : hip_fail(e, "bf6 encoder launch");
+}
+
+int w4a4_gemm_bf6(const uint8_t* codes6, const float* scales, int64_t M, int64_t K, const uint8_t* w6, int64_t N,
+                  const void* w_scale, int w_scale_dtype, const void* bias, int bias_dtype, void* out,
+                  int out_dtype, void* stream)
+{
+    int rc = gemm_validate((const int8_t*)codes6, scales, M, K, w6, N, w_scale, w_scale_dtype, 0, bias,
+                           bias_dtype, nullptr, nullptr, 0, 0, out, out_dtype, 0);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return W4A4_OK;
+    GemmArgs a{(const int8_t*)codes6, scales, M, K, N, w6, w_scale, w_scale_dtype, 0, bias, bias_dtype,
+               nullptr, nullptr, 0, 0, out, out_dtype, nullptr, 0, nullptr};
+    if (!gemm_bf6_ok(a))
+        return fail(W4A4_UNSUPPORTED, "bf6 GEMM needs K a multiple of 128 in [256, %lld] and 16-byte aligned "
+                    "codes, weights and output", (long long)gemm_bf6_max_k());
+    rc = device_check();
+    if (rc) return rc;
+    const hipError_t e = launch_gemm_bf6(a, (hipStream_t)stream);
+    return e == hipSuccess ? W4A4_OK : hip_fail(e, "bf6 gemm launch");
+}
+
+size_t w4a4_linear_bf6_workspace_size(int64_t M, int64_t K)
+{
+    if (M <= 0) return 0;
+    return 2 * align256((size_t)M * (size_t)K) + align256((size_t)M * 4);
+}
+
+int w4a4_linear_bf6(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m, int64_t stride_k,
+                    const float* rot, int32_t g, const void* smooth, const uint8_t* w6, int64_t N,
+                    const void* w_scale, int w_scale_dtype, const void* bias, void* out, int out_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc = rq_validate(x, x_dtype, M, K, stride_m, stride_k, rot, g, (int8_t*)1, (float*)1);
+    if (rc) return rc;
+    rc = gemm_validate((const int8_t*)1, (const float*)1, M, K, w6, N, w_scale, w_scale_dtype, 0, bias, x_dtype,
+                       nullptr, nullptr, 0, 0, out, out_dtype, 0);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return W4A4_OK;
+    const size_t need = w4a4_linear_bf6_workspace_size(M, K);
+    if (!workspace || workspace_bytes < need)
+        return fail(W4A4_INVALID, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    uint8_t* ws = (uint8_t*)workspace;
+    int8_t* codes = (int8_t*)ws;
+    ws += align256((size_t)M * (size_t)K);
+    uint8_t* codes6 = ws;
+    ws += align256((size_t)M * (size_t)K);
+    float* scales = (float*)ws;
+    RQArgs qa{x, x_dtype, M, K, stride_m, stride_k, rot, rot ? g : 0, smooth, codes, scales, nullptr};
+    GemmArgs ga{(const int8_t*)codes6, scales, M, K, N, w6, w_scale, w_scale_dtype, 0, bias, x_dtype,
+                nullptr, nullptr, 0, 0, out, out_dtype, nullptr, 0, nullptr};
+    if (rotate_quant_path(qa) < 0)
+        return fail(W4A4_UNSUPPORTED, "no rotate_quant kernel for this shape (K=%lld)", (long long)K);
+    if (!gemm_bf6_ok(ga) || (K % 32))
+        return fail(W4A4_UNSUPPORTED, "bf6 GEMM needs K a multiple of 128 in [256, %lld] and 16-byte aligned "
+                    "weights and output", (long long)gemm_bf6_max_k());
+    rc = device_check();
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    int path = 0;
+    hipError_t e = launch_rotate_quant(qa, st, &path);
+    if (e != hipSuccess) return hip_fail(e, "rotate_quant launch");
+    e = launch_to_bf6(codes, false, M * (K / 32), codes6, st);
+    if (e != hipSuccess) return hip_fail(e, "bf6 encoder launch");
+    e = launch_gemm_bf6(ga, st);
+    return e == hipSuccess ? W4A4_OK : hip_fail(e, "bf6 gemm launch");
+}
+
 int w4a4_linear_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
                         int64_t stride_k, const float* rot, int32_t g, const void* smooth,
                         const uint8_t* w_packed, int64_t N, const void* w_scale, int w_scale_dtype,

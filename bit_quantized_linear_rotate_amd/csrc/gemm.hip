@@ -489,6 +489,8 @@ constexpr int BBM = 256, BBN = 256;
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 
 
 // -------------------------------------------------------------------------
@@ -940,6 +942,346 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
     __builtin_amdgcn_s_waitcnt(0x0070);
 }
 
+// -------------------------------------------------------------------------
+// FP6 variant of the persistent kernel (gfx950 f8f6f4 MFMA).  Codes in
+// [-7, 7] and weights in [-8, 7] are exact in bf6 (e3m2: sign, 3 exponent bits
+// with bias 3, 2 mantissa bits), their products are small integers, and the
+// fp32 accumulator holds every partial sum exactly while |sum| < 2^24 (56 K <
+// 2^24): the accumulator is the exact integer sum, the same value the INT8
+// kernels convert, so the epilogue gives the same bits.  v_mfma_f32_16x16x128
+// _f8f6f4 takes 128 K per instruction at twice the INT8 rate.
+//   * Format of both operands ("bf6 blocks"): each run of 32 consecutive K
+//     values is 24 bytes, value e in bits 6e .. 6e+5 of the little-endian
+//     192-bit block, followed by 8 unused bytes; a row of K values is K bytes
+//     (the layout of one lane's MFMA operand: lane (i, q) holds K values
+//     32 q .. 32 q + 31 of row or column i).
+//   * 256 x 128 tiles, K 128 per step; codes (32 KB) and weights (16 KB) per
+//     stage both keep 128-byte rows in LDS with the INT4 kernel's chunk
+//     swizzle and buffer_load ... lds pattern (twelve 1 KB loads per loader
+//     wave and stage), three 48 KB slots, the ring running across tiles.
+//   * Eight waves in 4 (M) x 2 (N), each a 64 x 64 block of 4 x 4 MFMAs with
+//     fp32 accumulators; a fragment is the 16 + 8 bytes of chunks 2q and 2q+1.
+//   * Epilogue, loader roles and waits as in the INT4 kernel.
+// -------------------------------------------------------------------------
+constexpr int B6_BN = 128;
+constexpr int B6_BK = 128;                              // K per step (bytes per row per step)
+constexpr int B6_ASTAGE = BBM * B6_BK;                  // 32 KB
+constexpr int B6_WSTAGE = B6_BN * B6_BK;                // 16 KB
+constexpr int B6_SLOT = B6_ASTAGE + B6_WSTAGE;
+constexpr int B6_ALOADS = B6_ASTAGE / 1024 / R3_LOADERS;   // 8
+constexpr int B6_WLOADS = B6_WSTAGE / 1024 / R3_LOADERS;   // 4
+constexpr int B6_LPS = B6_ALOADS + B6_WLOADS;
+template <int ODT> constexpr int b6_stores() { return 4 * (16 * 64 * (ODT == F32 ? 4 : 2)) / (64 * 16); }
+template <int ODT> constexpr int b6_epi_bytes() { return R3_WAVES * 16 * r3_srb<ODT>() + 2 * B6_BN * 4 + BBM * 4; }
+static_assert(b6_epi_bytes<F32>() <= B6_SLOT, "bf6 epilogue must fit in one slot");
+// the largest K whose sums stay exact in the fp32 accumulator
+constexpr int64_t kGemmMaxKBf6 = ((int64_t)1 << 24) / 56 / B6_BK * B6_BK;
+
+__device__ __forceinline__ R3Tile b6_tile(const GemmArgs& a, int t, int ntiles, int tiles_n)
+{
+    R3Tile r;
+    if (t >= ntiles) {
+        r.m0 = 0; r.n0 = 0;
+        r.ra = make_rsrc(a.codes, 0);
+        r.rw = make_rsrc(a.wp, 0);
+        return r;
+    }
+    const int q8 = ntiles >> 3, r8 = ntiles & 7;
+    const int xcd = t & 7, loc = t >> 3;
+    const int tile = xcd * q8 + min(xcd, r8) + loc;
+    constexpr int GROUP_M = 8;
+    const int tiles_m = ntiles / tiles_n;
+    const int per_group = GROUP_M * tiles_n;
+    const int first_m = (tile / per_group) * GROUP_M;
+    const int gsize = min(tiles_m - first_m, GROUP_M);
+    const int in_g = tile - (tile / per_group) * per_group;
+    r.m0 = (int64_t)(first_m + in_g % gsize) * BBM;
+    r.n0 = (int64_t)(in_g / gsize) * B6_BN;
+    r.ra = make_rsrc(a.codes + r.m0 * a.K, (uint64_t)(a.M - r.m0) * a.K);
+    r.rw = make_rsrc(a.wp + r.n0 * a.K, (uint64_t)(a.N - r.n0) * a.K);
+    return r;
+}
+
+template <int ODT>
+__global__ __launch_bounds__(512) void w4a4_gemm_bf6_kernel(GemmArgs a, int tiles_m, int tiles_n)
+{
+    __shared__ __align__(16) int8_t smem[3 * B6_SLOT];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int j = lane & 15, q = lane >> 4;
+    const int wm = wave & 3, wn = wave >> 2;   // 64-row block wm, 64-column block wn
+
+    const int ntiles = tiles_m * tiles_n;
+    const int64_t K = a.K, M = a.M, N = a.N;
+    const int nsteps = (int)(K / B6_BK);
+    int t = blockIdx.x;
+    const int G = gridDim.x;
+
+    const bool loader = wave < R3_LOADERS;
+    const int lw = wave & (R3_LOADERS - 1);
+    // both operands: lane l of a 1 KB load writes chunk (l & 7) of row
+    // (l >> 3), i.e. logical chunk (l & 7) ^ r3_swz(row)
+    const int arow = lane >> 3;
+    const int c_vo = (int)(arow * K + (((lane & 7) ^ r3_swz(arow)) * 16));
+    const int row8 = (int)(8 * K);
+    auto issue = [&](int slot, const __amdgpu_buffer_rsrc_t& ra, const __amdgpu_buffer_rsrc_t& rw, int st) {
+        if (!loader) return;
+        int8_t* as = smem + slot * B6_SLOT;
+        int8_t* ws = as + B6_ASTAGE;
+        const int k0 = st * B6_BK;
+        // codes: rows lw*64 .. lw*64+63; weights: columns lw*32 .. lw*32+31
+#pragma unroll
+        for (int i = 0; i < B6_ALOADS; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (__attribute__((address_space(3))) void*)(as + (lw * 64 + i * 8) * B6_BK), 16,
+                c_vo + (lw * 8 + i) * row8 + k0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < B6_WLOADS; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (__attribute__((address_space(3))) void*)(ws + (lw * 32 + i * 8) * B6_BK), 16,
+                c_vo + (lw * 4 + i) * row8 + k0, 0, 0, 0);
+    };
+
+    v4f acc[4][4];
+    // fragment: chunk 2q (16 bytes) and the first 8 bytes of chunk 2q + 1 of
+    // row (code) or column (weight) j of each 16-row tile
+    const int c0 = ((q * 2) ^ r3_swz(j)) * 16, c1 = ((q * 2 + 1) ^ r3_swz(j)) * 16;
+    const int a_ro = (wm * 64 + j) * B6_BK;
+    const int w_ro = B6_ASTAGE + (wn * 64 + j) * B6_BK;
+    auto frag = [&](const int8_t* p) {
+        const v4i lo = *(const v4i*)(p + c0);
+        const v2i hi = *(const v2i*)(p + c1);
+        return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+    };
+    auto compute = [&](int slot) {
+        const int8_t* as = smem + slot * B6_SLOT + a_ro;
+        const int8_t* ws = smem + slot * B6_SLOT + w_ro;
+        v8i bfr[4], afr[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) bfr[nt] = frag(ws + nt * 16 * B6_BK);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) afr[mt] = frag(as + mt * 16 * B6_BK);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr[mt], bfr[nt], acc[mt][nt],
+                                                                               3, 3, 0, 0, 0, 0);
+    };
+
+    R3Tile cur_t = b6_tile(a, t, ntiles, tiles_n);
+    R3Tile nxt_t = b6_tile(a, t + G, ntiles, tiles_n);
+    issue(0, cur_t.ra, cur_t.rw, 0);
+    issue(1, cur_t.ra, cur_t.rw, 1);
+    int cur = 0, nxt2 = 2;
+    static_assert(B6_LPS + b6_stores<ODT>() <= 63, "vmcnt range");
+    auto pad_stores = [&]() {
+        if (!loader) return;
+        const __amdgpu_buffer_rsrc_t none = make_rsrc(a.out, 0);
+#pragma unroll
+        for (int i = 0; i < b6_stores<ODT>(); ++i)
+            __builtin_amdgcn_raw_buffer_store_b32(0u, none, 4 * i, 0, (int)0x80000000);
+    };
+    pad_stores();
+    for (;;) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = (v4f){0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < nsteps; ++s) {
+            if (loader) {
+                // stage s has landed once vmcnt drops to B6_LPS; in steps 0
+                // and 1 the previous tile's stores (or their stand-ins) may be
+                // in flight too (vmcnt retires in issue order)
+                asm volatile(
+                    "s_cmp_lt_u32 %0, 2\n\t"
+                    "s_cbranch_scc0 1f\n\t"
+                    "s_waitcnt vmcnt(%1)\n\t"
+                    "s_branch 2f\n"
+                    "1:\n\t"
+                    "s_waitcnt vmcnt(%2)\n"
+                    "2:" ::"s"(s), "n"(B6_LPS + b6_stores<ODT>()), "n"(B6_LPS) : "memory", "scc");
+            }
+            __builtin_amdgcn_s_barrier();
+            const bool same = s + 2 < nsteps;
+            issue(nxt2, same ? cur_t.ra : nxt_t.ra, same ? cur_t.rw : nxt_t.rw, same ? s + 2 : s + 2 - nsteps);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(cur);
+            cur = cur == 2 ? 0 : cur + 1;
+            nxt2 = nxt2 == 2 ? 0 : nxt2 + 1;
+        }
+
+        // ---- epilogue in the slot the last step used (see the INT4 kernel)
+        int8_t* eslot = smem + nxt2 * B6_SLOT;
+        __builtin_amdgcn_s_barrier();
+        constexpr int SRB = r3_srb<ODT>();
+        constexpr int ESZ = ODT == F32 ? 4 : 2;
+        int8_t* strips = eslot;
+        float* scol = (float*)(eslot + R3_WAVES * 16 * SRB);
+        float* bcol = scol + B6_BN;
+        float* srow = bcol + B6_BN;
+        const int64_t m0 = cur_t.m0, n0 = cur_t.n0;
+        const bool has_bias = a.bias != nullptr;
+        if (!loader) {
+            // waves 4-7: 256 threads; columns from the first 128, rows all 256
+            const int c = tid - R3_LOADERS * 64;
+            const int64_t col = n0 + (c & (B6_BN - 1)), row = m0 + c;
+            const int64_t cc = col < N ? col : N - 1;
+            const int bdt = has_bias ? a.bias_dtype : a.sw_dtype;
+            const uint32_t ws = r3_scalar_word(a.sw, a.sw_dtype, N, cc);
+            const uint32_t wb = r3_scalar_word(has_bias ? a.bias : a.sw, bdt, N, cc);
+            const uint32_t wr = r3_scalar_word(a.sa, F32, M, row < M ? row : M - 1);
+            if (c < B6_BN) {
+                scol[c] = r3_scalar_value(ws, a.sw_dtype, cc);
+                bcol[c] = has_bias ? r3_scalar_value(wb, bdt, cc) : 0.0f;
+            }
+            srow[c] = __uint_as_float(wr);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_s_barrier();
+        float scl[4], bia[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            scl[nt] = scol[wn * 64 + nt * 16 + j];
+            bia[nt] = bcol[wn * 64 + nt * 16 + j];
+        }
+        const bool full = m0 + BBM <= M && n0 + B6_BN <= N && (N % 8) == 0;
+        constexpr int VPC = 16 / ESZ, CPR = 64 / VPC, CHUNKS = 16 * CPR, PER_LANE = CHUNKS / 64;
+        static_assert(PER_LANE == 2 || PER_LANE == 4, "strip read asm below");
+        int8_t* mine = strips + wave * 16 * SRB;
+        using lds_ptr = const __attribute__((address_space(3))) int8_t*;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const float* sr = srow + wm * 64 + mt * 16 + 4 * q;
+            const float sa[4] = {sr[0], sr[1], sr[2], sr[3]};
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // the accumulator is the exact integer sum (below 2^24)
+                    const float tv = mul_rn(mul_rn(acc[mt][nt][r], sa[r]), scl[nt]);
+                    const float o = has_bias ? add_rn(tv, bia[nt]) : tv;
+                    int8_t* dst = mine + (4 * q + r) * SRB + (nt * 16 + j) * ESZ;
+                    if constexpr (ODT == F32)
+                        *(float*)dst = o;
+                    else
+                        *(uint16_t*)dst = f32_to_h<ODT>(o);
+                }
+            v4u vv[PER_LANE];
+            lds_ptr la[PER_LANE];
+#pragma unroll
+            for (int i = 0; i < PER_LANE; ++i) {
+                const int c = lane + 64 * i;
+                la[i] = (lds_ptr)(mine + (c / CPR) * SRB + (c % CPR) * 16);
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            if constexpr (PER_LANE == 2) {
+                asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                             : "=v"(vv[0]), "=v"(vv[1]) : "v"(la[0]), "v"(la[1]) : "memory");
+            } else {
+                asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
+                             "ds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+                             : "=v"(vv[0]), "=v"(vv[1]), "=v"(vv[2]), "=v"(vv[3])
+                             : "v"(la[0]), "v"(la[1]), "v"(la[2]), "v"(la[3]) : "memory");
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int i = 0; i < PER_LANE; ++i) {
+                const int c = lane + 64 * i;
+                const int rr = c / CPR, ch = c % CPR;
+                const uint4 v = make_uint4(vv[i][0], vv[i][1], vv[i][2], vv[i][3]);
+                const int64_t row = m0 + wm * 64 + mt * 16 + rr;
+                const int64_t col0 = n0 + wn * 64 + ch * VPC;
+                int8_t* dst = (int8_t*)a.out + (row * N + col0) * ESZ;
+                if (full) {
+                    *(uint4*)dst = v;
+                } else if (row < M) {
+                    if (col0 + VPC <= N && (N % 8) == 0) {
+                        *(uint4*)dst = v;
+                    } else {
+                        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int e = 0; e < VPC; ++e) {
+                            if (col0 + e >= N) break;
+                            if constexpr (ODT == F32)
+                                ((uint32_t*)dst)[e] = w4[e];
+                            else
+                                ((uint16_t*)dst)[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+                        }
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (!full && loader) {
+            __builtin_amdgcn_s_waitcnt(r3_vmcnt(0));
+            pad_stores();
+        }
+        t += G;
+        if (t >= ntiles) break;
+        cur_t = nxt_t;
+        nxt_t = b6_tile(a, t + G, ntiles, tiles_n);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);
+}
+
+// ---- bf6 block encoders (codes and weights -> the FP6 kernel's operands)
+// e3m2 patterns of the integers 0..8 (sign in bit 5)
+__device__ __forceinline__ uint32_t bf6_of(int v)
+{
+    const int m = v < 0 ? -v : v;
+    // 0, 1, 2, 3, 4, 5, 6, 7, 8 -> 0x00 0x0C 0x10 0x12 0x14 0x15 0x16 0x17 0x18
+    const uint32_t e = m == 0 ? 0u : m == 1 ? 0x0Cu : m == 2 ? 0x10u : m == 3 ? 0x12u : (uint32_t)(0x10 + m);
+    return e | (v < 0 ? 0x20u : 0u);
+}
+
+// one 32-value block per thread: 6 payload dwords and 2 zero dwords
+__device__ __forceinline__ void bf6_store(uint8_t* dst, const int (&v)[32])
+{
+    uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        const uint32_t b = bf6_of(v[e]);
+        const int bit = 6 * e;
+        w[bit >> 5] |= b << (bit & 31);
+        if ((bit & 31) > 26) w[(bit >> 5) + 1] |= b >> (32 - (bit & 31));
+    }
+    *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+    *(uint4*)(dst + 16) = make_uint4(w[4], w[5], 0u, 0u);
+}
+
+__global__ void codes_to_bf6_kernel(const int8_t* __restrict__ codes, int64_t nblk, uint8_t* __restrict__ out)
+{
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk;
+         b += (int64_t)gridDim.x * blockDim.x) {
+        const uint4 p0 = *(const uint4*)(codes + 32 * b), p1 = *(const uint4*)(codes + 32 * b + 16);
+        const uint32_t d[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        int v[32];
+#pragma unroll
+        for (int e = 0; e < 32; ++e) v[e] = (int)(int8_t)(d[e >> 2] >> (8 * (e & 3)));
+        bf6_store(out + 32 * b, v);
+    }
+}
+
+__global__ void weights_to_bf6_kernel(const uint8_t* __restrict__ wp, int64_t nblk, uint8_t* __restrict__ out)
+{
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk;
+         b += (int64_t)gridDim.x * blockDim.x) {
+        const uint4 p = *(const uint4*)(wp + 16 * b);
+        const uint32_t d[4] = {p.x, p.y, p.z, p.w};
+        int v[32];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t byte = (d[i >> 2] >> (8 * (i & 3))) & 0xffu;
+            const int lo = (int)(byte & 0xfu), hi = (int)(byte >> 4);
+            v[2 * i] = lo >= 8 ? lo - 16 : lo;          // low nibble: k = 2i
+            v[2 * i + 1] = hi >= 8 ? hi - 16 : hi;      // high nibble: k = 2i + 1
+        }
+        bf6_store(out + 32 * b, v);
+    }
+}
+
 __global__ void fill_zero_i64(int64_t* p, int64_t n)
 {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -1201,6 +1543,52 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
             hipLaunchKernelGGL((w4a4_gemm_kernel<-1, false, false>), dim3(gx, gy, 1), dim3(256), 0,
                                st, a, kc);
     }
+    return hipGetLastError();
+}
+
+// ---- FP6 path (host) ---------------------------------------------------
+
+bool gemm_bf6_ok(const GemmArgs& a)
+{
+    return a.M > 0 && a.N > 0 && (a.K % B6_BK) == 0 && a.K >= 2 * B6_BK && a.K <= kGemmMaxKBf6 &&
+           a.sw_group == 0 && a.lora == nullptr && a.acc_out == nullptr && a.k_chunk == 0 &&
+           ((uintptr_t)a.codes % 16) == 0 && ((uintptr_t)a.wp % 16) == 0 && ((uintptr_t)a.out % 16) == 0;
+}
+
+int64_t gemm_bf6_max_k() { return kGemmMaxKBf6; }
+
+hipError_t launch_gemm_bf6(const GemmArgs& a, hipStream_t st)
+{
+    if (!gemm_bf6_ok(a)) return hipErrorNotSupported;
+    const int tm = (int)((a.M + BBM - 1) / BBM), tn = (int)((a.N + B6_BN - 1) / B6_BN);
+    const int nt = tm * tn;
+    static int n_cu = 0;
+    if (n_cu == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v >= 8)
+            n_cu = v & ~7;
+        else
+            n_cu = 256;
+    }
+    const unsigned grid = (unsigned)(nt < n_cu ? nt : n_cu);
+    if (a.out_dtype == F32)
+        hipLaunchKernelGGL(w4a4_gemm_bf6_kernel<F32>, dim3(grid), dim3(512), 0, st, a, tm, tn);
+    else if (a.out_dtype == F16)
+        hipLaunchKernelGGL(w4a4_gemm_bf6_kernel<F16>, dim3(grid), dim3(512), 0, st, a, tm, tn);
+    else
+        hipLaunchKernelGGL(w4a4_gemm_bf6_kernel<BF16>, dim3(grid), dim3(512), 0, st, a, tm, tn);
+    return hipGetLastError();
+}
+
+hipError_t launch_to_bf6(const void* src, bool weights, int64_t nblk, uint8_t* out, hipStream_t st)
+{
+    const int64_t want = (nblk + 255) / 256;
+    const unsigned grid = (unsigned)(want < 4096 ? (want > 0 ? want : 1) : 4096);
+    if (weights)
+        hipLaunchKernelGGL(weights_to_bf6_kernel, dim3(grid), dim3(256), 0, st, (const uint8_t*)src, nblk, out);
+    else
+        hipLaunchKernelGGL(codes_to_bf6_kernel, dim3(grid), dim3(256), 0, st, (const int8_t*)src, nblk, out);
     return hipGetLastError();
 }
 

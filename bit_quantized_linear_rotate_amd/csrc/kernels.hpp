@@ -79,6 +79,14 @@ hipError_t launch_lowrank_down(const LowRankArgs& a, hipStream_t st);
 bool svd_quant_ok(const RQArgs& a, int group);
 hipError_t launch_svd_quant(const RQArgs& a, int group, bool act_unsigned, hipStream_t st);
 
+// FP6 (bf6 e3m2) GEMM: codes (M, K) and weights (N, K) as bf6 blocks (32
+// values in 24 bytes + 8 unused bytes), per-channel scales, optional bias
+bool gemm_bf6_ok(const GemmArgs& a);
+int64_t gemm_bf6_max_k();
+hipError_t launch_gemm_bf6(const GemmArgs& a, hipStream_t st);
+// int8 codes (weights = false) or packed INT4 weights -> bf6 blocks
+hipError_t launch_to_bf6(const void* src, bool weights, int64_t nblk, uint8_t* out, hipStream_t st);
+
 // Largest K whose accumulation cannot overflow the kernel's INT32 registers.
 // The kernel accumulates 16 * c * w (weights are unpacked as 16 * w, which
 // needs no per-nibble sign extension), |c| <= 7 and |w| <= 8.

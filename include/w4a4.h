@@ -292,6 +292,41 @@ int w4a4_linear_svdquant_grouped(const void* x, int x_dtype, int64_t M, int64_t 
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * FP6 GEMM path ("[Feat][Ascend] Consolidate INT8, RotateQuant, RoPE and
+ * ConvRot W4A4 backends", "W4A4 correctness and performance scope": the same
+ * exact integer accumulation, evaluated on gfx950's f8f6f4 matrix cores).
+ * Codes in [-7, 7] and weights in [-8, 7] are exact in bf6 (e3m2: sign bit 5,
+ * exponent bits 4-2 with bias 3, mantissa bits 1-0); the products are small
+ * integers and the fp32 accumulator holds every partial sum exactly for
+ * K <= 299,520 (56 K < 2^24), so the result is bit-identical to
+ * w4a4_gemm_from_codes with per-channel scales.
+ *   "bf6 blocks": every 32 consecutive K values of a row take 32 bytes: value
+ *   e in bits 6e .. 6e+5 of the first 24 (a little-endian 192-bit block), then
+ *   8 bytes written as zero and never read.  A row of K values is K bytes.
+ * w4a4_codes_to_bf6: int8 codes (M, K) in [-8, 8] -> bf6 blocks (M, K);
+ *   K % 32 == 0, 16-byte aligned buffers.
+ * w4a4_pack_weights_bf6: packed INT4 weights (N, K/2) -> bf6 blocks (N, K),
+ *   once per layer.
+ * w4a4_gemm_bf6: the GEMM and epilogue of w4a4_gemm_from_codes (per-channel
+ *   weight scales, optional bias, no low-rank term) on bf6 codes and weights;
+ *   K a multiple of 128 in [256, 299520], 16-byte aligned codes, weights and
+ *   output, else W4A4_UNSUPPORTED.
+ * w4a4_linear_bf6: rotate-quant, bf6 encoding and w4a4_gemm_bf6 back to back;
+ *   bias in x_dtype; workspace of w4a4_linear_bf6_workspace_size(M, K) bytes.
+ */
+int w4a4_codes_to_bf6(const int8_t* codes, int64_t M, int64_t K, uint8_t* out, void* stream);
+int w4a4_pack_weights_bf6(const uint8_t* w_packed, int64_t N, int64_t K, uint8_t* out, void* stream);
+int w4a4_gemm_bf6(const uint8_t* codes6, const float* scales, int64_t M, int64_t K, const uint8_t* w6,
+                  int64_t N, const void* w_scale, int w_scale_dtype, const void* bias, int bias_dtype,
+                  void* out, int out_dtype, void* stream);
+size_t w4a4_linear_bf6_workspace_size(int64_t M, int64_t K);
+int w4a4_linear_bf6(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                    int64_t stride_k, const float* rot, int32_t g, const void* smooth,
+                    const uint8_t* w6, int64_t N, const void* w_scale, int w_scale_dtype,
+                    const void* bias, void* out, int out_dtype, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
  * w4a4_linear for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same arguments without the workspace, and the same kernels, which work
