@@ -833,11 +833,11 @@ def _profile_kernels():
     return [
         ("void w4a4::rq_row_kernel<2, false, false, 4, 1, 7>", "rotate_quant_row_prefill_m8192_k3840_g64",
          text(p), rq_bytes(p), None, src + "rq_row.hip"),
-        ("void w4a4::w4a4_gemm_ring3_kernel<2>", "gemm_ring3_prefill_m8192_k3840_n3840",
+        ("void w4a4::w4a4_gemm_ring3_kernel<2, false>", "gemm_ring3_prefill_m8192_k3840_n3840",
          text(p), gemm_bytes(p), 2.0 * p.M * p.N * p.K, src + "gemm.hip"),
         ("void w4a4::rq_colmajor_kernel<1, 256, false, false, 6>", "rotate_quant_colmajor_widek_m8192_k10240_g256",
          text(wk), rq_bytes(wk), None, src + "rotate_quant.hip"),
-        ("void w4a4::w4a4_gemm_ring3_kernel<1>", "gemm_ring3_widek_m8192_k10240_n3840",
+        ("void w4a4::w4a4_gemm_ring3_kernel<1, false>", "gemm_ring3_widek_m8192_k10240_n3840",
          text(wk), gemm_bytes(wk), 2.0 * wk.M * wk.N * wk.K, src + "gemm.hip"),
         ("void w4a4::rq_g256_kernel<2, true, 7>", "rotate_quant_g256_lowrank_m4096_k16384",
          text(lr), rq_bytes(lr), None, src + "rotate_quant.hip"),
@@ -848,6 +848,34 @@ def _profile_kernels():
         ("void (anonymous namespace)::stream_probe_kernel<true>", "stream_probe_nt_prefill_m8192_k3840",
          "streaming probe, the prefill rotate-quant's bytes (non-temporal stores)",
          p.M * p.K * 2 + p.M * p.K + 4 * p.M, None, src + "stream_probe.hip"),
+        # INT8 mode (qmax 127, INT8 weights (N, K))
+        ("void w4a4::rq_row_kernel<2, false, false, 4, 1, 127>", "rotate_quant_row_int8_prefill_m8192_k3840_g64",
+         "INT8 mode, " + text(p), rq_bytes(p), None, src + "rq_row.hip"),
+        ("void w4a4::w4a4_gemm_ring3_kernel<2, true>", "gemm_ring3_int8_weights_prefill_m8192_k3840_n3840",
+         "INT8 mode, " + text(p) + ", INT8 weights",
+         p.M * p.K + p.N * p.K + 4 * p.M + 2 * p.N + 2 * p.M * p.N, 2.0 * p.M * p.N * p.K, src + "gemm.hip"),
+        # structured (Hadamard) rotation
+        ("void w4a4::(anonymous namespace)::rq_hadamard_kernel<2, 256, true, 7, 2, 1>",
+         "rotate_quant_hadamard_lowrank_m4096_k16384_g256", "Hadamard rotation, " + text(lr),
+         lr.M * lr.K * 3 + 4 * lr.M + 2 * lr.K, None, src + "rq_hadamard.hip"),
+        ("void w4a4::(anonymous namespace)::rq_hadamard_kernel<1, 256, false, 127, 2, 1>",
+         "rotate_quant_hadamard_int8_widek_m8192_k10240_g256",
+         "Hadamard rotation, INT8 mode, widek shape with contiguous rows (f16, g=256)",
+         wk.M * wk.K * 3 + 4 * wk.M, None, src + "rq_hadamard.hip"),
+        # SVDQuant variant
+        ("void w4a4::(anonymous namespace)::rq_svd_kernel<2, 64, true, true, true>",
+         "quantize_svdquant_lowrank_m4096_k16384_group64",
+         "SVDQuant quantizer (act_unsigned shift, smoothing, per-64-group scales), lowrank shape",
+         lr.M * lr.K * 3 + 2 * lr.K + 4 * lr.M * (lr.K // 64), None, src + "rq_svdquant.hip"),
+        ("void w4a4::w4a4_gemm_kernel<2, false, true, false, true>",
+         "gemm_tile128_svdquant_lowrank_m4096_k16384_n6144",
+         "SVDQuant GEMM (activation and weight group scales, rank 32), lowrank shape",
+         lr.M * lr.K + lr.N * lr.K // 2 + 4 * lr.M * (lr.K // 64) + 2 * (lr.K // 64) * lr.N + 2 * lr.M * lr.N
+         + 4 * lr.M * lr.rank + 2 * lr.N * lr.rank, 2.0 * lr.M * lr.N * lr.K, src + "gemm.hip"),
+        # FP6 (bf6) GEMM
+        ("void w4a4::w4a4_gemm_bf6_kernel<2>", "gemm_bf6_prefill_m8192_k3840_n3840",
+         "FP6 path, " + text(p) + ", bf6 codes and weights",
+         p.M * p.K + p.N * p.K + 4 * p.M + 2 * p.N + 2 * p.M * p.N, 2.0 * p.M * p.N * p.K, src + "gemm.hip"),
     ]
 
 
