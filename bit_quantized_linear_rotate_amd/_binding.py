@@ -218,7 +218,7 @@ def w4a4_gemm_workspace_size(M: int, N: int, K: int, k_chunk: int = 0) -> int:
 
 # kernel names of the plan queries (include/w4a4.h)
 RQ_KERNELS = {0: "generic", 1: "mfma_lds", 2: "reg", 3: "wave", 4: "colmajor", 5: "g256", 6: "row"}
-GEMM_KERNELS = {0: "tile128", 1: "tile128_splitk", 2: "ring3", 3: "skinny"}
+GEMM_KERNELS = {0: "tile128", 1: "tile128_splitk", 2: "ring3", 3: "skinny", 4: "pingpong"}
 _ALIGNED = 1 << 12   # stands for a buffer the binding allocates (torch aligns to >= 256 bytes)
 
 

@@ -943,6 +943,322 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
 }
 
 // -------------------------------------------------------------------------
+// w4a4_gemm_pp_kernel: the prefill kernel with the two waves of every SIMD
+// taking turns ("ping-pong").  Same 256 x 256 tiles, 128-deep K steps, three
+// 48 KB LDS-DMA slots, LDS layout of the codes and XCD-aware tile order as
+// the kernel above, but:
+//   * The eight waves form two groups of four, one wave of each per SIMD
+//     (group A: waves 0-3, group B: waves 4-7).  Each wave alternates a
+//     memory phase (the LDS fragment reads of one K step; group A also puts
+//     the stage two steps ahead in flight) and a compute phase (the step's 64
+//     MFMAs, the nibble unpack of the weights interleaved with them at 1.25
+//     VALU instructions per MFMA, which the SIMD issues beside the matrix
+//     core).  Group B runs one phase behind group A, so on every SIMD one wave
+//     computes while the other reads: the matrix core is fed by one wave at a
+//     time and does not wait for LDS.  Every phase ends at a workgroup
+//     barrier.
+//   * A stage's slot is read only in the two groups' memory phases of its
+//     step; group A puts stage s+2 in flight into the slot of stage s-1 in
+//     its memory phase of step s, after group B's memory phase of step s-1,
+//     and waits for stage s+1 at the end of its compute phase of step s: a
+//     load has four phases to land.
+//   * The MFMA takes the weights as its first operand: lane (j, q) then holds
+//     output row j and output columns 4q .. 4q+3 of every 16 x 16 tile.  The
+//     weight columns of a wave's four column tiles are interleaved (tile nt,
+//     MFMA row c is column 16 (c >> 2) + 4 nt + (c & 3)), so a lane holds
+//     sixteen consecutive columns of one row and the epilogue writes them
+//     from registers with 16-byte stores.  Packed weight column n keeps its
+//     16-byte chunk c at c ^ pp_wswz(n) in LDS, which spreads these reads
+//     over all banks.
+//   * A tile's column scales, bias and row scales are staged in LDS by group
+//     B in the tile's first two memory phases (two buffers, used by
+//     alternate tiles).
+//   * Each group's epilogue is a phase of its own; group A's overlaps group
+//     B's last compute phase.  Output rows past M and columns past N are
+//     dropped by the buffer range check, so every wave issues the same
+//     number of stores in every tile (the wait that counts them stays exact).
+// Lane (j, q) covers k = q*32 .. q*32+31 of a step, k-substep t the sixteen
+// from q*32 + t*16, as in the kernel above.
+// -------------------------------------------------------------------------
+constexpr int PP_SCL = 3 * BBN * 4;                 // column scales, bias, row scales (f32)
+constexpr int PP_LDS = 3 * R3_SLOT + 2 * PP_SCL;    // 150 KB
+static_assert(BBM == BBN && PP_LDS <= 160 * 1024, "LDS");
+// output store instructions per wave and tile (8 row tiles, 16 values per lane)
+template <int ODT> constexpr int pp_stores() { return 8 * (ODT == F32 ? 4 : 2); }
+// chunk permutation of packed weight column n in LDS (bits 4-5 of n: 0, 2, 3, 1)
+__device__ __forceinline__ int pp_wswz(int n) { return (0x78 >> (2 * ((n >> 4) & 3))) & 3; }
+
+// two f32 values rounded to the 16-bit output format, low half first
+template <int ODT> __device__ __forceinline__ uint32_t pp_pack2(float lo, float hi)
+{
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    if constexpr (ODT == BF16) {
+        typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, h2));
+    } else {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, h2));
+    }
+}
+
+template <int ODT>
+__global__ __launch_bounds__(512) void w4a4_gemm_pp_kernel(GemmArgs a, int tiles_m, int tiles_n)
+{
+    constexpr int BK = R3_BK, SLOT = R3_SLOT, ASTAGE = BBM * BK, LPS = 12;
+    constexpr int ST = pp_stores<ODT>(), ESZ = ODT == F32 ? 4 : 2;
+    using lds_vptr = __attribute__((address_space(3))) void*;
+    __shared__ __align__(16) int8_t smem[PP_LDS];
+
+    const int tid = threadIdx.x;
+    // (the wave index is uniform: LDS destinations of the DMA stay scalar)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int j = lane & 15, q = lane >> 4;
+    const bool grp_a = wave < 4;
+    const int wm = wave & 1, wn = wave >> 1;  // 128-row block wm, 64-column block wn
+
+    const int ntiles = tiles_m * tiles_n;
+    const int64_t K = a.K, M = a.M, N = a.N;
+    const int nsteps = (int)(K / BK);
+    int t = blockIdx.x;
+    const int G = gridDim.x;
+    if (t >= ntiles) return;  // (the whole workgroup)
+
+    // DMA by group A, wave lw: code rows lw*64 + 8 i + (lane >> 3) (chunk
+    // (lane & 7) of the row's 128 bytes, stored at position (lane & 7)), packed
+    // weight columns lw*64 + 16 i + (lane >> 2) (chunk (lane & 3) ^ swizzle
+    // stored at position (lane & 3)).  Row and column offsets travel in the
+    // voffset, so the range check drops rows past M and columns past N; the
+    // step's K offset is the scalar offset.
+    const int lw = wave & 3;
+    const int arow = lane >> 3;
+    const int a_vo = (int)((lw * 64 + arow) * K + (((lane & 7) ^ r3_swz(arow)) * 16));
+    const int a_rowl = (int)(8 * K);
+    const int64_t wrow = K >> 1;
+    const int w_vo = (int)((lw * 64 + (lane >> 2)) * wrow);
+    const int w_col16 = (int)(16 * wrow);
+    auto issue = [&](int slot, const __amdgpu_buffer_rsrc_t& ra, const __amdgpu_buffer_rsrc_t& rw, int st) {
+        int8_t* as = smem + slot * SLOT;
+        int8_t* ws = as + ASTAGE;
+        const int ka = st * BK, kw = st * (BK / 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)(as + (lw * 64 + i * 8) * BK), 16,
+                                                     a_vo + i * a_rowl, ka, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)  // column lw*64 + 16 i + c has swizzle pp_wswz = entry i
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (lds_vptr)(ws + (lw * 64 + i * 16) * (BK / 2)), 16,
+                w_vo + i * w_col16 + (((lane & 3) ^ ((0x78 >> (2 * i)) & 3)) * 16), kw, 0, 0);
+    };
+
+    // fragment offsets inside a slot: code row wm*128 + 16 mt + j, chunks
+    // 2q and 2q+1; weight column wcol + 4 nt, chunk q
+    const int a_ro = (wm * 128 + j) * BK;
+    const int a_c0 = ((q * 2) ^ r3_swz(j)) * 16, a_c1 = ((q * 2 + 1) ^ r3_swz(j)) * 16;
+    const int wcol = wn * 64 + 16 * (j >> 2) + (j & 3);
+    const int w_ro = ASTAGE + wcol * (BK / 2) + ((q ^ pp_wswz(wcol)) * 16);
+    v4u wp[4];
+    v4i af[2][8];
+    v4i acc[8][4];
+    auto mem = [&](int slot) {
+        const int8_t* as = smem + slot * SLOT + a_ro;
+        const int8_t* ws = smem + slot * SLOT + w_ro;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) wp[nt] = *(const v4u*)(ws + nt * 4 * (BK / 2));
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+                af[tt][mt] = *(const v4i*)(as + mt * 16 * BK + (tt ? a_c1 : a_c0));
+    };
+    // compute phase: eight groups of eight MFMAs (group g: substep g >> 2,
+    // column tile g & 3); group 0's weights are unpacked at the end of the
+    // memory phase, group g+1's (ten VALU instructions) two at a time between
+    // group g's first five MFMAs, each group a scheduling region of its own
+    v4i bfc;
+    auto unpack0 = [&]() { bfc = r3_half(wp[0], 0); };
+    auto comp = [&]() {
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const int tt = g >> 2, nt = g & 3;
+            const v4i bfn = g < 7 ? r3_half(wp[(g + 1) & 3], (g + 1) >> 2) : bfc;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bfc, af[tt][mt], acc[mt][nt], 0, 0, 0);
+            if (g < 7) {
+#pragma unroll
+                for (int m = 0; m < 5; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            bfc = bfn;
+        }
+    };
+
+    // group B stages the tile's column scales, bias and row scales in LDS
+    // as they are stored (DMA, no registers): wave b = wave - 4 moves bytes
+    // 256 b .. 256 b + 255 of each; the epilogue widens them to f32
+    const bool has_bias = a.bias != nullptr;
+    const int sw_sz = a.sw_dtype == F32 ? 4 : 2, b_sz = has_bias && a.bias_dtype != F32 ? 2 : 4;
+    auto scale_issue = [&](int par, int64_t m0, int64_t n0) {
+        int8_t* sc = smem + 3 * SLOT + par * PP_SCL;
+        const int b = wave - 4;
+        const int vo = b * 256 + lane * 4;
+        if (b * 256 < BBN * sw_sz)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                make_rsrc((const int8_t*)a.sw + n0 * sw_sz, (uint64_t)(N - n0) * sw_sz),
+                (lds_vptr)(sc + b * 256), 4, vo, 0, 0, 0);
+        if (has_bias && b * 256 < BBN * b_sz)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                make_rsrc((const int8_t*)a.bias + n0 * b_sz, (uint64_t)(N - n0) * b_sz),
+                (lds_vptr)(sc + BBN * 4 + b * 256), 4, vo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(a.sa + m0, (uint64_t)(M - m0) * 4),
+                                                 (lds_vptr)(sc + 2 * BBN * 4 + b * 256), 4, vo, 0, 0, 0);
+    };
+
+    // epilogue: lane (j, q) of wave (wm, wn) holds, for row tile mt, row
+    // wm*128 + 16 mt + j and columns c0 .. c0+15, value i = 4 nt + r in
+    // acc[mt][nt][r]
+    const int c0 = wn * 64 + 16 * q;
+    auto epi = [&](int par, int64_t m0, int64_t n0) {
+        // The lane's offsets are formed here, every tile, from values the
+        // compiler cannot see through: hoisted out of the tile loop they
+        // would take registers the K loop needs.
+        int scl = c0 * 4, row0 = (wm * 128 + j) * 4;
+        asm volatile("" : "+v"(scl), "+v"(row0));
+        const int8_t* sc = smem + 3 * SLOT + par * PP_SCL;
+        // the sixteen column scales and biases of this lane, widened to f32
+        v4f swv[4], bv[4];
+        auto widen = [&](v4f* dst, const int8_t* base, int dt) {
+            if (dt == F32) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[i] = *(const v4f*)(base + scl + 16 * i);
+            } else {
+                const v4u h0 = *(const v4u*)(base + scl / 2), h1 = *(const v4u*)(base + scl / 2 + 16);
+                const uint32_t w[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const uint16_t hb = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+                    dst[i >> 2][i & 3] = dt == BF16 ? bf16_to_f32(hb) : f16_to_f32(hb);
+                }
+            }
+        };
+        widen(swv, sc, a.sw_dtype);
+        if (has_bias) widen(bv, sc + BBN * 4, a.bias_dtype);
+        const int64_t rows = M - m0 < BBM ? M - m0 : BBM;
+        const uint32_t nrec = (uint32_t)((rows * N - n0) * ESZ);
+        const __amdgpu_buffer_rsrc_t ro =
+            __builtin_amdgcn_make_buffer_rsrc((void*)((int8_t*)a.out + (m0 * N + n0) * ESZ), (short)0, (int)nrec,
+                                              0x00020000);
+        // byte offset of (row wm*128 + j, column c0), or past the end for
+        // columns past N (dropped); row tile mt adds 16 mt rows
+        uint32_t off = n0 + c0 < N ? (uint32_t)(((wm * 128 + j) * N + c0) * ESZ) : nrec;
+        asm volatile("" : "+v"(off));
+        const uint32_t rstep = (uint32_t)(16 * N * ESZ);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const float sa = *(const float*)(sc + 2 * BBN * 4 + row0 + 64 * mt);
+            float o[16];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float tv = mul_rn(mul_rn((float)(acc[mt][nt][e] >> 4), sa), swv[nt][e]);
+                    o[4 * nt + e] = has_bias ? add_rn(tv, bv[nt][e]) : tv;
+                }
+            const uint32_t o_mt = off + mt * rstep;
+            if constexpr (ODT == F32) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        (v4u){__float_as_uint(o[4 * h]), __float_as_uint(o[4 * h + 1]), __float_as_uint(o[4 * h + 2]),
+                              __float_as_uint(o[4 * h + 3])},
+                        ro, o_mt + 16 * h, 0, 0);
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        (v4u){pp_pack2<ODT>(o[8 * h], o[8 * h + 1]), pp_pack2<ODT>(o[8 * h + 2], o[8 * h + 3]),
+                              pp_pack2<ODT>(o[8 * h + 4], o[8 * h + 5]), pp_pack2<ODT>(o[8 * h + 6], o[8 * h + 7])},
+                        ro, o_mt + 16 * h, 0, 0);
+            }
+        }
+    };
+
+    R3Tile cur_t = r3_tile<false>(a, t, ntiles, tiles_n);
+    R3Tile nxt_t = r3_tile<false>(a, t + G, ntiles, tiles_n);
+    if (grp_a) {
+        issue(0, cur_t.ra, cur_t.rw, 0);
+        issue(1, cur_t.ra, cur_t.rw, 1);
+        // stand-ins for a previous tile's output stores, so that the wait of
+        // every tile's first compute phase counts the same operations
+        const __amdgpu_buffer_rsrc_t none = make_rsrc(a.out, 0);
+#pragma unroll
+        for (int i = 0; i < ST; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 4 * i, 0, (int)0x80000000);
+        __builtin_amdgcn_s_waitcnt(r3_vmcnt(LPS + ST));  // stage 0 landed
+    }
+    __builtin_amdgcn_s_barrier();
+    if (!grp_a) __builtin_amdgcn_s_barrier();  // group B: one phase behind
+    __builtin_amdgcn_sched_barrier(0);
+    int slot = 0, par = 0;
+    for (;;) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = (v4i){0, 0, 0, 0};
+        for (int s = 0; s < nsteps; ++s) {
+            // ---- memory phase: the fragment reads first, then (group A)
+            // the DMA, whose issue takes a while, under their latency
+            const int nslot = slot == 0 ? 2 : slot - 1;  // (slot + 2) % 3
+            mem(slot);
+            if (grp_a) {
+                const bool same = s + 2 < nsteps;
+                issue(nslot, same ? cur_t.ra : nxt_t.ra, same ? cur_t.rw : nxt_t.rw, same ? s + 2 : s + 2 - nsteps);
+            } else if (s == 0) {
+                scale_issue(par, cur_t.m0, cur_t.n0);
+            } else if (s == 1) {
+                __builtin_amdgcn_s_waitcnt(r3_vmcnt(0));  // the tile's scales landed
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): fragments (and scales) in
+            unpack0();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- compute phase
+            comp();
+            if (grp_a) {
+                // stage s+1 landed: after it, this wave has issued stage s+2's
+                // loads and, in a tile's first step, the previous tile's
+                // output stores (or their stand-ins) before them
+                asm volatile(
+                    "s_cmp_eq_u32 %0, 0\n\t"
+                    "s_cbranch_scc0 1f\n\t"
+                    "s_waitcnt vmcnt(%1)\n\t"
+                    "s_branch 2f\n"
+                    "1:\n\t"
+                    "s_waitcnt vmcnt(%2)\n"
+                    "2:" ::"s"(s), "n"(LPS + ST), "n"(LPS) : "memory", "scc");
+            }
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            slot = slot == 2 ? 0 : slot + 1;
+        }
+        // ---- epilogue phase
+        epi(par, cur_t.m0, cur_t.n0);
+        t += G;
+        if (t >= ntiles) break;
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        cur_t = nxt_t;
+        nxt_t = r3_tile<false>(a, t + G, ntiles, tiles_n);
+        par ^= 1;
+    }
+    if (grp_a) __builtin_amdgcn_s_barrier();  // pairs with group B's last
+}
+
+// -------------------------------------------------------------------------
 // FP6 variant of the persistent kernel (gfx950 f8f6f4 MFMA).  Codes in
 // [-7, 7] and weights in [-8, 7] are exact in bf6 (e3m2: sign, 3 exponent bits
 // with bias 3, 2 mantissa bits), their products are small integers, and the
@@ -1411,12 +1727,18 @@ int gemm_path(const GemmArgs& a)
     if (!group && a.k_chunk == 0 && a.M >= 1 && a.M <= 64 && (a.K % 64) == 0 &&
         ((uintptr_t)a.codes % 16) == 0 && ((uintptr_t)a.wp % 8) == 0)
         return kGemmSkinny;
-    // Prefill-sized layers take the 256 x 256 three-stage kernel; everything
-    // else (small M, group scales, low-rank term, INT32 export, K chunks,
-    // K not a multiple of 128, unaligned operands) the 128 x 128 kernel.
+    // Prefill-sized layers take a 256 x 256 three-stage kernel: the
+    // ping-pong one when whole 16-column output pieces exist (N % 16 == 0)
+    // and a tile's output offsets fit its 32-bit range check, else the ring
+    // kernel; everything else (small M, group scales, low-rank term, INT32
+    // export, K chunks, K not a multiple of 128, unaligned operands) the
+    // 128 x 128 kernel.
     if (!group && a.lora == nullptr && a.acc_out == nullptr && a.k_chunk == 0 && a.M > 128 &&
-        (a.K % R3_BK) == 0 && a.K >= 2 * R3_BK && aligned && ((uintptr_t)a.out % 16) == 0)
+        (a.K % R3_BK) == 0 && a.K >= 2 * R3_BK && aligned && ((uintptr_t)a.out % 16) == 0) {
+        const uint64_t esz = a.out_dtype == F32 ? 4 : 2;
+        if (a.N % 16 == 0 && (uint64_t)a.N * esz * 512 < (1ull << 32)) return kGemmPP;
         return kGemmRing3;
+    }
     if (a.k_chunk > 0 && !group) return kGemmTileSplitK;
     return kGemmTile;
 }
@@ -1437,7 +1759,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
             hipLaunchKernelGGL(w4a4_gemm_skinny_kernel<4>, dim3(gx), dim3(1024), 0, st, a);
         return hipGetLastError();
     }
-    if (path == kGemmRing3) {
+    if (path == kGemmRing3 || path == kGemmPP) {
         const int tm = (int)((a.M + BBM - 1) / BBM), tn = (int)((a.N + BBN - 1) / BBN);
         const int nt = tm * tn;
         // persistent grid: one workgroup per CU (a multiple of 8 so that a
@@ -1452,6 +1774,15 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st)
                 n_cu = 256;
         }
         const unsigned grid = (unsigned)(nt < n_cu ? nt : n_cu);
+        if (path == kGemmPP) {
+            if (a.out_dtype == F32)
+                hipLaunchKernelGGL(w4a4_gemm_pp_kernel<F32>, dim3(grid), dim3(512), 0, st, a, tm, tn);
+            else if (a.out_dtype == F16)
+                hipLaunchKernelGGL(w4a4_gemm_pp_kernel<F16>, dim3(grid), dim3(512), 0, st, a, tm, tn);
+            else
+                hipLaunchKernelGGL(w4a4_gemm_pp_kernel<BF16>, dim3(grid), dim3(512), 0, st, a, tm, tn);
+            return hipGetLastError();
+        }
         if (a.w8) {
             if (a.out_dtype == F32)
                 hipLaunchKernelGGL((w4a4_gemm_ring3_kernel<F32, true>), dim3(grid), dim3(512), 0, st, a, tm, tn);

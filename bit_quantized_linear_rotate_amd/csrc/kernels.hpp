@@ -59,7 +59,7 @@ struct GemmArgs {
 };
 
 // GEMM kernels, as gemm_path names them (host-only choice, no device access)
-enum { kGemmTile = 0, kGemmTileSplitK = 1, kGemmRing3 = 2, kGemmSkinny = 3 };
+enum { kGemmTile = 0, kGemmTileSplitK = 1, kGemmRing3 = 2, kGemmSkinny = 3, kGemmPP = 4 };
 int gemm_path(const GemmArgs& a);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 

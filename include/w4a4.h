@@ -377,6 +377,7 @@ int w4a4_int32_guard(int64_t K, int64_t* k_chunk);
  * w4a4_gemm_plan, *kernel (has_lowrank: a low-rank term will be added):
  *   0 128 x 128 tiles          1 128 x 128 tiles over K chunks (int64 combine)
  *   2 persistent 256 x 256 ring (prefill-sized M)     3 skinny M (M <= 64)
+ *   4 persistent 256 x 256 ping-pong (prefill-sized M, N % 16 == 0)
  */
 int w4a4_rotate_quant_plan(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
                            int64_t stride_k, const float* rot, int32_t g, const void* smooth,

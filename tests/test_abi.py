@@ -123,8 +123,9 @@ def test_plan_queries_name_the_config_kernels(L):
                                     smooth=torch.zeros(16384, dtype=bf)) == "g256"
     assert b.w4a4_rotate_quant_plan(torch.zeros(32, 3840, dtype=bf), torch.zeros(64, 64), 64) == "reg"
     assert b.w4a4_rotate_quant_plan(torch.zeros(32, 256), torch.zeros(16, 16), 16) == "generic"
-    assert b.w4a4_gemm_plan(8192, 3840, 3840) == "ring3"
-    assert b.w4a4_gemm_plan(8192, 10240, 3840) == "ring3"
+    assert b.w4a4_gemm_plan(8192, 3840, 3840) == "pingpong"
+    assert b.w4a4_gemm_plan(8192, 10240, 3840) == "pingpong"
+    assert b.w4a4_gemm_plan(300, 1024, 260) == "ring3"    # N % 16 != 0
     assert b.w4a4_gemm_plan(32, 3840, 3840) == "skinny"
     assert b.w4a4_gemm_plan(4096, 16384, 6144, 64, lowrank=True) == "tile128"
     assert b.w4a4_gemm_plan(300, 1024, 200, k_chunk=128) == "tile128_splitk"

@@ -6,10 +6,14 @@ any other load reads base + per-lane offset + scalar offset.  The kernels
 rely on that check for ragged tiles and for the prefetch past a tile's last
 K step, so every load must either fall wholly inside its resource or be
 wholly out of range by its per-lane offset alone.  This test restates, in
-numpy, the offsets each of the three buffer-load GEMM kernels issues (the
-128 x 128 tile kernel's staging, the persistent 256 x 256 ring, the skinny
-kernel) and checks that rule for the configs' shapes and ragged ones.  It
-must be kept in step with the kernels' index arithmetic in gemm.hip."""
+numpy, the offsets each of the buffer-load GEMM kernels issues (the 128 x 128 tile
+kernel's staging, the persistent 256 x 256 ring, the ping-pong kernel, the
+skinny kernel) and checks that rule for the configs' shapes and ragged ones.
+The ping-pong kernel also writes its outputs with range-checked buffer
+stores: the model checks that every in-range store lands on its own output
+row and columns, that every output is written exactly once, and that the
+stores it drops are out of range by their per-lane offset.  It must be kept
+in step with the kernels' index arithmetic in gemm.hip."""
 import numpy as np
 import pytest
 
@@ -70,6 +74,68 @@ def ring3_loads(M, K, N):
                   f"ring weights n0={n0} st={st}")
 
 
+def pp_loads(M, K, N, sw_sz=2, b_sz=2):
+    """Ping-pong 256 x 256 kernel (K % 128 == 0): every stage of every tile
+    (the step's K offset in the scalar offset, never past the tile's last
+    step), and the scale staging."""
+    nsteps = K // 128
+    lw = np.arange(4)[:, None, None]
+    lane = np.arange(64)[None, :, None]
+    i8 = np.arange(8)[None, None, :]
+    i4 = np.arange(4)[None, None, :]
+    a_vo = (lw * 64 + (lane >> 3)) * K + (((lane & 7) ^ r3_swz(lane >> 3)) * 16) + i8 * (8 * K)
+    swz = (0x78 >> (2 * i4)) & 3
+    w_vo = (lw * 64 + i4 * 16 + (lane >> 2)) * (K // 2) + (((lane & 3) ^ swz) * 16)
+    for m0 in range(0, M, 256):
+        for st in range(nsteps):
+            check(a_vo, st * 128, 16, (M - m0) * K, f"pp codes m0={m0} st={st}")
+    for n0 in range(0, N, 256):
+        for st in range(nsteps):
+            check(w_vo, st * 64, 16, (N - n0) * (K // 2), f"pp weights n0={n0} st={st}")
+    b = np.arange(4)[:, None]
+    vo = b * 256 + np.arange(64)[None, :] * 4
+    for n0 in range(0, N, 256):
+        for sz, what in ((sw_sz, "scales"), (b_sz, "bias")):
+            check(vo[: 256 * sz // 256], 0, 4, (N - n0) * sz, f"pp {what} n0={n0}")
+    for m0 in range(0, M, 256):
+        check(vo, 0, 4, (M - m0) * 4, f"pp row scales m0={m0}")
+
+
+def pp_stores(M, N, esz, col_check=True):
+    """Ping-pong kernel's output stores (N % 16 == 0): per tile, wave (wm, wn)
+    lane (j, q) writes row wm*128 + 16 mt + j, columns wn*64 + 16 q .. +15;
+    a lane whose columns start past N takes an offset past the resource
+    (col_check=False leaves that out, for the test of the model)."""
+    assert N % 16 == 0 and N * esz * 512 < 2 ** 32
+    per = 16 // esz
+    written = np.zeros((M, N), dtype=np.int32)
+    wave = np.arange(8)[:, None, None, None]
+    lane = np.arange(64)[None, :, None, None]
+    mt = np.arange(8)[None, None, :, None]
+    h = np.arange(16 // per)[None, None, None, :]
+    wm, wn, j, q = wave & 1, wave >> 1, lane & 15, lane >> 4
+    c0 = wn * 64 + 16 * q
+    for m0 in range(0, M, 256):
+        for n0 in range(0, N, 256):
+            rows = min(M - m0, 256)
+            nrec = (rows * N - n0) * esz
+            off = ((wm * 128 + j) * N + c0) * esz
+            if col_check:
+                off = np.where(n0 + c0 < N, off, nrec)
+            o = np.broadcast_to(off + mt * (16 * N * esz) + 16 * h, (8, 64, 8, 16 // per)).astype(np.int64)
+            assert (o < 2 ** 32).all(), "store offset outside 32 bits"
+            inr = o < nrec
+            assert (o[inr] + 16 <= nrec).all(), "a store straddles the resource's end"
+            row = np.broadcast_to(m0 + wm * 128 + mt * 16 + j, o.shape)[inr]
+            col = np.broadcast_to(n0 + c0 + per * h, o.shape)[inr]
+            # the in-range store's address is the one of its output
+            assert np.array_equal(o[inr], ((row - m0) * N + (col - n0)) * esz)
+            assert (row < M).all() and (col + per <= N).all()
+            for e in range(per):
+                np.add.at(written, (row, col + e), 1)
+    assert (written == 1).all(), "an output written never or twice"
+
+
 def skinny_loads(M, K, N):
     """Skinny-M kernel (M <= 64, K % 64 == 0)."""
     MT = 1 if M <= 16 else 2 if M <= 32 else 4
@@ -97,6 +163,26 @@ def test_tile128_staging_stays_in_bounds(M, K, N):
                                    (4100, 256, 4130), (4352, 384, 4112)])
 def test_ring3_stays_in_bounds(M, K, N):
     ring3_loads(M, K, N)
+
+
+@pytest.mark.parametrize("M,K,N", [(8192, 3840, 3840), (8192, 10240, 3840), (300, 2048, 528),
+                                   (4100, 256, 4112), (4352, 384, 4128), (129, 256, 16)])
+@pytest.mark.parametrize("sw_sz,b_sz", [(2, 2), (4, 4), (2, 4)])
+def test_pingpong_loads_stay_in_bounds(M, K, N, sw_sz, b_sz):
+    pp_loads(M, K, N, sw_sz, b_sz)
+
+
+@pytest.mark.parametrize("M,N", [(300, 528), (4100, 272), (129, 16), (513, 4112), (1024, 3840)])
+@pytest.mark.parametrize("esz", [2, 4])
+def test_pingpong_stores_cover_each_output_once(M, N, esz):
+    pp_stores(M, N, esz)
+
+
+def test_store_model_catches_a_missing_column_check():
+    # without the past-N redirect, a ragged tile's lanes beyond the last
+    # column write the next row's first outputs
+    with pytest.raises(AssertionError):
+        pp_stores(300, 272, 2, col_check=False)
 
 
 @pytest.mark.parametrize("M,K,N", [(32, 3840, 3840), (1, 64, 16), (33, 640, 129), (64, 4096, 272)])

@@ -177,7 +177,7 @@ def test_empty_shapes():
 
 
 @pytest.mark.parametrize("M,K,N", [(300, 2048, 520), (513, 1024, 257), (256, 3840, 256),
-                                   (1000, 640, 1000)])
+                                   (1000, 640, 1000), (300, 2048, 528), (1000, 640, 1008)])
 @pytest.mark.parametrize("odt", ["f32", "bf16", "f16"])
 def test_output_bit_exact_without_acc_export(M, K, N, odt):
     # the large-tile kernels run only when the INT32 sums are not exported
@@ -195,7 +195,7 @@ def test_output_bit_exact_without_acc_export(M, K, N, odt):
     assert np.array_equal(bits(host(out2)), bits(oout))
 
 
-@pytest.mark.parametrize("M,K,N", [(4100, 256, 4130), (4352, 384, 4112)])
+@pytest.mark.parametrize("M,K,N", [(4100, 256, 4130), (4352, 384, 4112), (4100, 256, 4128)])
 def test_several_tiles_per_workgroup(M, K, N):
     # more 256 x 256 tiles than CUs: the persistent kernel walks several tiles
     # per workgroup and prefetches the next tile during the last steps; ragged
@@ -207,6 +207,26 @@ def test_several_tiles_per_workgroup(M, K, N):
     oacc = oracle.gemm(codes, oracle.unpack(wp, K))
     oout = oracle.epilogue(oacc, sa, sw, "bf16", "bf16", bias=b, bias_dtype="bf16")
     assert np.array_equal(bits(host(out)), bits(oout))
+
+
+@pytest.mark.parametrize("sw_dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("b_dt", [None, "f32", "bf16", "f16"])
+def test_pingpong_scale_and_bias_dtypes(sw_dt, b_dt):
+    # the ping-pong kernel stages the scales and bias in LDS as stored and
+    # widens them in the epilogue: every dtype pair, with and without bias,
+    # on a ragged 2 x 2 tile grid
+    need_gpu()
+    M, K, N = 300, 512, 272
+    assert w4.w4a4_gemm_plan(M, K, N) == "pingpong"
+    codes, sa, wp, sw, _ = _operands(M, K, N, "f32", sw_dt, bias=False, seed=7)
+    rng = np.random.default_rng(8)
+    b = workloads.f32_to_storage(rng.normal(0, 0.1, size=N), b_dt) if b_dt else None
+    for odt, tdt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+        out = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, sw_dt),
+                                      bias=dev(b, b_dt) if b_dt else None, out_dtype=tdt)
+        oout = oracle.epilogue(oracle.gemm(codes, oracle.unpack(wp, K)), sa, sw, sw_dt, odt, bias=b,
+                               bias_dtype=b_dt)
+        assert np.array_equal(bits(host(out)), bits(oout)), (odt, sw_dt, b_dt)
 
 
 SKINNY = [  # (M, K, N): decode-sized M takes the skinny kernel (K % 64 == 0)
@@ -271,7 +291,8 @@ def _full_range_weights(rng, N, K):
 
 
 @pytest.mark.parametrize("M,K,N,kernel", [
-    (300, 1024, 260, "ring3"), (4100, 256, 300, "ring3"),
+    (300, 1024, 260, "ring3"), (4100, 256, 300, "ring3"), (300, 1024, 272, "pingpong"),
+    (4100, 256, 304, "pingpong"),
     (100, 192, 130, "tile128"), (77, 1024, 40, "tile128"),
     (32, 3840, 384, "skinny"), (5, 160, 17, "tile128")])
 def test_minus_eight_nibble_every_kernel(M, K, N, kernel):
@@ -297,13 +318,14 @@ def test_minus_eight_nibble_every_kernel(M, K, N, kernel):
                                                                      group=64)))
 
 
-def test_extreme_codes_ring_kernel():
-    # +-7 codes against -8 / 7 weights at K = 16384 through the persistent ring
-    # (no INT32 export there): unit scales and fp32 output give f32(acc), exact
-    # below 2^24
+@pytest.mark.parametrize("N,kernel", [(256, "pingpong"), (264, "ring3")])
+def test_extreme_codes_ring_kernel(N, kernel):
+    # +-7 codes against -8 / 7 weights at K = 16384 through the persistent
+    # kernels (no INT32 export there): unit scales and fp32 output give
+    # f32(acc), exact below 2^24
     need_gpu()
-    M, N, K = 512, 256, 16384
-    assert w4.w4a4_gemm_plan(M, K, N) == "ring3"
+    M, K = 512, 16384
+    assert w4.w4a4_gemm_plan(M, K, N) == kernel
     codes = np.full((M, K), 7, dtype=np.int8)
     codes[1::2] = -7
     codes[2::5, ::3] = 0
