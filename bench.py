@@ -58,11 +58,12 @@ FP6_PEAK_TOPS = 10100.0        # MI355X dense FP6/FP4 MFMA, published
 MIN_KERNEL_LAUNCHES = 50
 TRAFFIC_FILES = {  # kernel source -> committed counter summary
     "gemm": ("bit_quantized_linear_rotate_amd/csrc/gemm.hip",
-             "profiles/gemm_ring3_prefill_m8192_k3840_n3840_traffic.json"),
+             "profiles/gemm_pingpong_prefill_m8192_k3840_n3840_traffic.json"),
     "rotate_quant": ("bit_quantized_linear_rotate_amd/csrc/rq_row.hip",
                      "profiles/rotate_quant_row_prefill_m8192_k3840_g64_traffic.json"),
 }
-GEMM_NAMES = {"ring3": "w4a4_gemm_ring3_kernel", "skinny": "w4a4_gemm_skinny_kernel",
+GEMM_NAMES = {"pingpong": "w4a4_gemm_pp_kernel", "ring3": "w4a4_gemm_ring3_kernel",
+              "skinny": "w4a4_gemm_skinny_kernel",
               "tile128": "w4a4_gemm_kernel", "tile128_splitk": "w4a4_gemm_kernel (K chunks)"}
 RQ_NAMES = {"row": "rq_row_kernel", "wave": "rq_wave_kernel", "colmajor": "rq_colmajor_kernel", "g256": "rq_g256_kernel",
             "reg": "rq_reg_kernel", "mfma_lds": "rq_mfma_kernel", "generic": "rq_generic_kernel"}
@@ -582,7 +583,7 @@ def measure_int8(name, steps, warmup, torch, np, w4, workloads, cpu=True):
                             "GB_s": rq_bytes / (ms_rq * 1e-3) / 1e9,
                             "frac_hbm": rq_bytes / (ms_rq * 1e-3) / 1e9 / HBM_PEAK_GBS,
                             "algorithmic_bytes": rq_bytes},
-           "gemm": {"kernel": "w4a4_gemm_kernel (INT8 weights)", **t_gemm,
+           "gemm": {"kernel": GEMM_NAMES.get(w4.w8a8_gemm_plan(M, K, N), "?") + " (INT8 weights)", **t_gemm,
                     "TOPS": ops / (ms_gemm * 1e-3) / 1e12,
                     "frac_int8": ops / (ms_gemm * 1e-3) / 1e12 / INT8_PEAK_TOPS, "ops": ops,
                     "GB_s": gemm_bytes / (ms_gemm * 1e-3) / 1e9, "algorithmic_bytes": gemm_bytes}}
@@ -833,11 +834,11 @@ def _profile_kernels():
     return [
         ("void w4a4::rq_row_kernel<2, false, false, 4, 1, 7>", "rotate_quant_row_prefill_m8192_k3840_g64",
          text(p), rq_bytes(p), None, src + "rq_row.hip"),
-        ("void w4a4::w4a4_gemm_ring3_kernel<2, false>", "gemm_ring3_prefill_m8192_k3840_n3840",
+        ("void w4a4::w4a4_gemm_pp_kernel<2>", "gemm_pingpong_prefill_m8192_k3840_n3840",
          text(p), gemm_bytes(p), 2.0 * p.M * p.N * p.K, src + "gemm.hip"),
         ("void w4a4::rq_colmajor_kernel<1, 256, false, false, 6>", "rotate_quant_colmajor_widek_m8192_k10240_g256",
          text(wk), rq_bytes(wk), None, src + "rotate_quant.hip"),
-        ("void w4a4::w4a4_gemm_ring3_kernel<1, false>", "gemm_ring3_widek_m8192_k10240_n3840",
+        ("void w4a4::w4a4_gemm_pp_kernel<1>", "gemm_pingpong_widek_m8192_k10240_n3840",
          text(wk), gemm_bytes(wk), 2.0 * wk.M * wk.N * wk.K, src + "gemm.hip"),
         ("void w4a4::rq_g256_kernel<2, true, 7>", "rotate_quant_g256_lowrank_m4096_k16384",
          text(lr), rq_bytes(lr), None, src + "rotate_quant.hip"),
@@ -963,7 +964,7 @@ def summarize_profiles(d):
         with open(os.path.join(out_dir, stem + ".md"), "w") as f:
             f.write("\n".join(lines) + "\n")
         rows_md.append((k, wtext, st))
-        if stem in ("rotate_quant_row_prefill_m8192_k3840_g64", "gemm_ring3_prefill_m8192_k3840_n3840"):
+        if stem in ("rotate_quant_row_prefill_m8192_k3840_g64", "gemm_pingpong_prefill_m8192_k3840_n3840"):
             with open(os.path.join(ROOT, srcf), "rb") as f:
                 digest = hashlib.sha256(f.read()).hexdigest()
             rec = {"kernel": _short_name(k), "workload": "prefill", "source": srcf,

@@ -638,7 +638,10 @@ __device__ __forceinline__ R3Tile r3_tile(const GemmArgs& a, int t, int ntiles, 
     const int q8 = ntiles >> 3, r8 = ntiles & 7;
     const int xcd = t & 7, loc = t >> 3;
     const int tile = xcd * q8 + min(xcd, r8) + loc;
-    constexpr int GROUP_M = 8;
+    // groups of four tile rows: an XCD's 32 concurrent tiles then span 4 row
+    // blocks and 8 column blocks, the pair that keeps the fewest operand bytes
+    // (a code row block is twice a packed weight column block) across its L2
+    constexpr int GROUP_M = 4;
     const int tiles_m = ntiles / tiles_n;
     const int per_group = GROUP_M * tiles_n;
     const int first_m = (tile / per_group) * GROUP_M;
@@ -1305,7 +1308,10 @@ __device__ __forceinline__ R3Tile b6_tile(const GemmArgs& a, int t, int ntiles, 
     const int q8 = ntiles >> 3, r8 = ntiles & 7;
     const int xcd = t & 7, loc = t >> 3;
     const int tile = xcd * q8 + min(xcd, r8) + loc;
-    constexpr int GROUP_M = 8;
+    // groups of four tile rows: an XCD's 32 concurrent tiles then span 4 row
+    // blocks and 8 column blocks, the pair that keeps the fewest operand bytes
+    // (a code row block is twice a packed weight column block) across its L2
+    constexpr int GROUP_M = 4;
     const int tiles_m = ntiles / tiles_n;
     const int per_group = GROUP_M * tiles_n;
     const int first_m = (tile / per_group) * GROUP_M;
