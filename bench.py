@@ -949,12 +949,14 @@ def summarize_profiles(d):
                   "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"):
             lines.append(f"| {c} | {sq[c]:,.0f} |")
         mfma_busy = sq["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_SIMD)
-        valu_busy = 4 * sq["SQ_INSTS_VALU"] / (cyc * N_SIMD)
+        # SQ_INSTS_VALU counts the MFMA instructions too
+        valu_busy = 4 * (sq["SQ_INSTS_VALU"] - sq["SQ_INSTS_MFMA"]) / (cyc * N_SIMD)
         lines += ["", "Derived (GRBM_GUI_ACTIVE / 8 = cycles of one XCD over the counter run's dispatch, "
                   "which the profiler serialises and can stretch; 1024 SIMDs):", "",
                   f"- cycles per XCD {cyc:,.0f}",
                   f"- MFMA busy {100 * mfma_busy:.1f}% of SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES)",
-                  f"- VALU issue {100 * valu_busy:.1f}% of SIMD cycles (4 cycles per wave64 instruction)"]
+                  f"- non-MFMA VALU issue {100 * valu_busy:.1f}% of SIMD cycles (SQ_INSTS_VALU less "
+                  f"SQ_INSTS_MFMA, 4 cycles per wave64 instruction)"]
         if avg_ns:
             lines.append(f"- algorithmic bytes / average duration: {alg / (avg_ns * 1e-9) / 1e9:,.0f} GB/s "
                          f"({100 * alg / (avg_ns * 1e-9) / 1e9 / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
