@@ -842,7 +842,7 @@ def _profile_kernels():
          text(wk), gemm_bytes(wk), 2.0 * wk.M * wk.N * wk.K, src + "gemm.hip"),
         ("void w4a4::rq_g256_kernel<2, true, 7>", "rotate_quant_g256_lowrank_m4096_k16384",
          text(lr), rq_bytes(lr), None, src + "rotate_quant.hip"),
-        ("void w4a4::w4a4_gemm_kernel<2, false, true, false>", "gemm_tile128_lowrank_m4096_k16384_n6144",
+        ("void w4a4::w4a4_gemm_kernel<2, false, true, false, false>", "gemm_tile128_lowrank_m4096_k16384_n6144",
          text(lr), gemm_bytes(lr), 2.0 * lr.M * lr.N * lr.K, src + "gemm.hip"),
         ("void w4a4::lowrank_wide_kernel<2, 32>", "lowrank_down_lowrank_m4096_k16384_r32",
          text(lr), lr.M * lr.K * 2 + lr.K * lr.rank * 2 + 4 * lr.M * lr.rank, None, src + "lowrank.hip"),
