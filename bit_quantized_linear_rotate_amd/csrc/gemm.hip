@@ -50,6 +50,7 @@
 namespace w4a4 {
 
 constexpr int BM = 128, BN = 128, BK = 64, LDR = 80;
+constexpr float kMagicF = 12582912.0f;  // C = 1.5 * 2^23: C + i is exact for |i| < 2^22
 __device__ __forceinline__ void unpack16(uint32_t p, uint32_t& lo4, uint32_t& hi4)
 {
     // p holds 8 nibbles for k0..k7 (even k in the low nibble of each byte).
@@ -96,6 +97,9 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
     __shared__ __align__(16) int8_t As[2][BM * LDR];
     __shared__ __align__(16) int8_t Bs[2][BN * LDR];
     __shared__ __align__(16) float Ss[GSW >= 0 ? 2 : 1][GSW >= 0 ? 256 : 4];
+    // (16-bit group scales on the fast path: -kMagicF * scale / 16 beside each)
+    constexpr bool MAGIC = GSW == F16 || GSW == BF16;
+    __shared__ __align__(16) float Sc[MAGIC ? 2 : 1][MAGIC ? 256 : 4];
     __shared__ __align__(16) float Sa[AG ? 2 : 1][AG ? BM : 4];
 
     const int tid = threadIdx.x;
@@ -251,6 +255,14 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
     // float, whenever scale / 16 is exact (every scale but subnormal or NaN
     // ones). It returns false if some scale was not; the workgroup then runs
     // the loop again with the shift back to s.
+    // With 16-bit scales FAST also drops the conversion: each group's MFMA
+    // starts from the bit pattern of C = 1.5 * 2^23, so the INT32 result is the
+    // pattern of the float C + 16 s (|16 s| < 2^22), and one fma
+    // (C + 16 s) * (scale / 16) + (-C * scale / 16) rounds the exact real
+    // 16 s * scale / 16 = s * scale once: the product the exact path rounds.
+    // -C * scale / 16 is exact for a 16-bit scale (at most 11 significant
+    // bits, times 3) unless it overflows; a scale whose term is not exact or
+    // not finite (Inf, NaN, huge) sends the tile to the exact path too.
     auto kloop = [&](auto fast_c) -> bool {
         constexpr bool FAST = decltype(fast_c)::value;
         bool exact = true;
@@ -279,6 +291,11 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
                 if constexpr (FAST) {
                     w = v * 0.0625f;
                     exact = exact && w * 16.0f == v;
+                    if constexpr (MAGIC) {
+                        const float c = -kMagicF * w;
+                        exact = exact && __builtin_fmaf(-kMagicF, w, -c) == 0.0f && fabsf(c) < 0x1p127f;
+                        Sc[buf][tid] = c;
+                    }
                 }
                 Ss[buf][tid] = w;
             }
@@ -339,6 +356,28 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(GemmArgs a, int64_t kc)
                             facc[mt][nt][r] = add_rn(facc[mt][nt][r], p);
                         }
                     }
+                }
+            } else if constexpr (GROUP && FAST && MAGIC) {
+                const v4f swv = *(const v4f*)(&Ss[buf][(wn * 16 + j) * 4]);
+                const v4f cv = *(const v4f*)(&Sc[buf][(wn * 16 + j) * 4]);
+                const int mg = __float_as_int(-kMagicF) & 0x7fffffff;  // pattern of C
+                const v4i c0 = (v4i){mg, mg, mg, mg};
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) {
+                        const v4i t = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mt], bf[nt], c0, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            facc[mt][nt][r] = add_rn(facc[mt][nt][r],
+                                                     __builtin_fmaf(__int_as_float(t[r]), swv[nt], cv[nt]));
+                    }
+                // one MFMA, then eight VALU instructions (an earlier result's
+                // fma and add), sixteen times
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
                 }
             } else if constexpr (GROUP) {
                 const v4f swv = *(const v4f*)(&Ss[buf][(wn * 16 + j) * 4]);

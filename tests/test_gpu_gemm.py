@@ -149,6 +149,43 @@ def test_group_scales_below_2_pow_minus_122():
     assert np.array_equal(bits(host(out)), bits(oout))
 
 
+@pytest.mark.parametrize("sw_dt", ["bf16", "f16"])
+def test_group_scales_16bit_special_values(sw_dt):
+    """16-bit group scales take the fast path that starts each group's INT32
+    sum from the pattern of 1.5 * 2^23 and folds the conversion into one fma.
+    Zero, negative and subnormal scales stay on it (the sums of zero terms
+    cannot change a sum that starts at +0); Inf, NaN and scales whose
+    1.5 * 2^23 * scale / 16 overflows send their workgroup to the exact path.
+    All of it bit-exact, with zero code rows and extreme codes mixed in."""
+    need_gpu()
+    M, K, N = 300, 1024, 384
+    codes, sa, wp, sw, _ = _operands(M, K, N, "f32", sw_dt, group=64, seed=24)
+    codes[3] = 0                 # zero rows: every group sum is 0
+    codes[4] = 7
+    codes[5] = -7
+    swf = workloads.storage_to_f32(sw, sw_dt).copy()
+    swf[:, 10] = 0.0
+    swf[:, 11] = -swf[:, 11]
+    swf[2, 12] = -0.0
+    swf[:, 13] = 2.0 ** -20 if sw_dt == "f16" else 2.0 ** -130   # subnormal in the scale's format
+    swf[0, 140] = np.inf         # (a tile of its own column block)
+    swf[1, 300] = np.nan
+    swf[7, 290] = 6.0e4 if sw_dt == "f16" else 3.0e38             # large, finite
+    sw = workloads.f32_to_storage(swf, sw_dt)
+    parts = oracle.gemm(codes, oracle.unpack(wp, K), group=64)
+    for odt, tdt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        out = w4.w4a4_gemm_from_codes(dev(codes), dev(sa), dev(wp), dev(sw, sw_dt), w_scale_group=64,
+                                      out_dtype=tdt)
+        oout = oracle.epilogue(parts, sa, sw, sw_dt, odt, group=64)
+        go = host(out)
+        # bit-exact, signed zeros included; a NaN is any NaN (the pages fix no
+        # NaN payload: the oracle stores one canonical NaN, the GPU's
+        # conversion keeps the f32 NaN's sign)
+        nan = np.isnan(oracle.decode(odt, oout))
+        assert nan[:, 300].all() and np.array_equal(np.isnan(oracle.decode(odt, go)), nan)
+        assert np.array_equal(bits(go)[~nan], bits(oout)[~nan]), (odt, sw_dt)
+
+
 def test_lowrank_down_matches_oracle():
     need_gpu()
     rng = np.random.default_rng(8)
