@@ -991,8 +991,9 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
 // the kernel above, but:
 //   * The eight waves form two groups of four, one wave of each per SIMD
 //     (group A: waves 0-3, group B: waves 4-7).  Each wave alternates a
-//     memory phase (the LDS fragment reads of one K step; group A also puts
-//     the stage two steps ahead in flight) and a compute phase (the step's 64
+//     memory phase (the LDS fragment reads of one K step, then its group's
+//     part of the stage two steps ahead: group A's waves the codes, group B's
+//     the packed weights) and a compute phase (the step's 64
 //     MFMAs, the nibble unpack of the weights interleaved with them at 1.25
 //     VALU instructions per MFMA, which the SIMD issues beside the matrix
 //     core).  Group B runs one phase behind group A, so on every SIMD one wave
@@ -1000,10 +1001,14 @@ __global__ __launch_bounds__(512) void w4a4_gemm_ring3_kernel(GemmArgs a, int ti
 //     time and does not wait for LDS.  Every phase ends at a workgroup
 //     barrier.
 //   * A stage's slot is read only in the two groups' memory phases of its
-//     step; group A puts stage s+2 in flight into the slot of stage s-1 in
-//     its memory phase of step s, after group B's memory phase of step s-1,
-//     and waits for stage s+1 at the end of its compute phase of step s: a
-//     load has four phases to land.
+//     step; each group puts its part of stage s+2 in flight into the slot of
+//     stage s-1 in its memory phase of step s (after both groups' reads of
+//     step s-1), and waits for its part of stage s+1 before the barrier that
+//     precedes group A's memory phase of step s+1: group A at the end of its
+//     compute phase of step s (its codes have four phases to land), group B
+//     at the end of its memory phase of step s (its weights, a third of the
+//     bytes, have two).  Splitting the loads shortens group A's memory
+//     phase, the longer of the two.
 //   * The MFMA takes the weights as its first operand: lane (j, q) then holds
 //     output row j and output columns 4q .. 4q+3 of every 16 x 16 tile.  The
 //     weight columns of a wave's four column tiles are interleaved (tile nt,
@@ -1046,7 +1051,9 @@ template <int ODT> __device__ __forceinline__ uint32_t pp_pack2(float lo, float 
 template <int ODT>
 __global__ __launch_bounds__(512) void w4a4_gemm_pp_kernel(GemmArgs a, int tiles_m, int tiles_n)
 {
-    constexpr int BK = R3_BK, SLOT = R3_SLOT, ASTAGE = BBM * BK, LPS = 12;
+    // loads per stage and wave: LPS for both parts (the first two stages, by
+    // group A), LPA codes (group A), LPB weights (group B)
+    constexpr int BK = R3_BK, SLOT = R3_SLOT, ASTAGE = BBM * BK, LPS = 12, LPA = 8, LPB = 4;
     constexpr int ST = pp_stores<ODT>(), ESZ = ODT == F32 ? 4 : 2;
     using lds_vptr = __attribute__((address_space(3))) void*;
     __shared__ __align__(16) int8_t smem[PP_LDS];
@@ -1078,14 +1085,17 @@ __global__ __launch_bounds__(512) void w4a4_gemm_pp_kernel(GemmArgs a, int tiles
     const int64_t wrow = K >> 1;
     const int w_vo = (int)((lw * 64 + (lane >> 2)) * wrow);
     const int w_col16 = (int)(16 * wrow);
-    auto issue = [&](int slot, const __amdgpu_buffer_rsrc_t& ra, const __amdgpu_buffer_rsrc_t& rw, int st) {
+    // part: 1 the codes, 2 the weights, 3 both
+    auto issue = [&](int slot, const __amdgpu_buffer_rsrc_t& ra, const __amdgpu_buffer_rsrc_t& rw, int st, int part) {
         int8_t* as = smem + slot * SLOT;
         int8_t* ws = as + ASTAGE;
         const int ka = st * BK, kw = st * (BK / 2);
+        if (part & 1)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)(as + (lw * 64 + i * 8) * BK), 16,
                                                      a_vo + i * a_rowl, ka, 0, 0);
+        if (part & 2)
 #pragma unroll
         for (int i = 0; i < 4; ++i)  // column lw*64 + 16 i + c has swizzle pp_wswz = entry i
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -1142,21 +1152,23 @@ __global__ __launch_bounds__(512) void w4a4_gemm_pp_kernel(GemmArgs a, int tiles
 
     // group B stages the tile's column scales, bias and row scales in LDS
     // as they are stored (DMA, no registers): wave b = wave - 4 moves bytes
-    // 256 b .. 256 b + 255 of each; the epilogue widens them to f32
+    // 256 b .. 256 b + 255 of each; the epilogue widens them to f32.  Always
+    // three loads a wave (a zero-sized resource where there is nothing to
+    // move: zeros into an unused part of the buffer), so that group B's wait
+    // counts a fixed number of operations
     const bool has_bias = a.bias != nullptr;
     const int sw_sz = a.sw_dtype == F32 ? 4 : 2, b_sz = has_bias && a.bias_dtype != F32 ? 2 : 4;
     auto scale_issue = [&](int par, int64_t m0, int64_t n0) {
         int8_t* sc = smem + 3 * SLOT + par * PP_SCL;
         const int b = wave - 4;
         const int vo = b * 256 + lane * 4;
-        if (b * 256 < BBN * sw_sz)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                make_rsrc((const int8_t*)a.sw + n0 * sw_sz, (uint64_t)(N - n0) * sw_sz),
-                (lds_vptr)(sc + b * 256), 4, vo, 0, 0, 0);
-        if (has_bias && b * 256 < BBN * b_sz)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                make_rsrc((const int8_t*)a.bias + n0 * b_sz, (uint64_t)(N - n0) * b_sz),
-                (lds_vptr)(sc + BBN * 4 + b * 256), 4, vo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            make_rsrc((const int8_t*)a.sw + n0 * sw_sz, b * 256 < BBN * sw_sz ? (uint64_t)(N - n0) * sw_sz : 0),
+            (lds_vptr)(sc + b * 256), 4, vo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            make_rsrc(has_bias ? (const int8_t*)a.bias + n0 * b_sz : (const int8_t*)a.sw,
+                      has_bias && b * 256 < BBN * b_sz ? (uint64_t)(N - n0) * b_sz : 0),
+            (lds_vptr)(sc + BBN * 4 + b * 256), 4, vo, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(a.sa + m0, (uint64_t)(M - m0) * 4),
                                                  (lds_vptr)(sc + 2 * BBN * 4 + b * 256), 4, vo, 0, 0, 0);
     };
@@ -1233,8 +1245,8 @@ __global__ __launch_bounds__(512) void w4a4_gemm_pp_kernel(GemmArgs a, int tiles
     R3Tile cur_t = r3_tile<false>(a, t, ntiles, tiles_n);
     R3Tile nxt_t = r3_tile<false>(a, t + G, ntiles, tiles_n);
     if (grp_a) {
-        issue(0, cur_t.ra, cur_t.rw, 0);
-        issue(1, cur_t.ra, cur_t.rw, 1);
+        issue(0, cur_t.ra, cur_t.rw, 0, 3);
+        issue(1, cur_t.ra, cur_t.rw, 1, 3);
         // stand-ins for a previous tile's output stores, so that the wait of
         // every tile's first compute phase counts the same operations
         const __amdgpu_buffer_rsrc_t none = make_rsrc(a.out, 0);
@@ -1252,28 +1264,23 @@ __global__ __launch_bounds__(512) void w4a4_gemm_pp_kernel(GemmArgs a, int tiles
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = (v4i){0, 0, 0, 0};
         for (int s = 0; s < nsteps; ++s) {
-            // ---- memory phase: the fragment reads first, then (group A)
-            // the DMA, whose issue takes a while, under their latency
+            // ---- memory phase: the fragment reads first, then the group's
+            // DMA, whose issue takes a while, under their latency
             const int nslot = slot == 0 ? 2 : slot - 1;  // (slot + 2) % 3
             mem(slot);
-            if (grp_a) {
+            {
                 const bool same = s + 2 < nsteps;
-                issue(nslot, same ? cur_t.ra : nxt_t.ra, same ? cur_t.rw : nxt_t.rw, same ? s + 2 : s + 2 - nsteps);
-            } else if (s == 0) {
-                scale_issue(par, cur_t.m0, cur_t.n0);
-            } else if (s == 1) {
-                __builtin_amdgcn_s_waitcnt(r3_vmcnt(0));  // the tile's scales landed
+                if (!grp_a && s == 0) scale_issue(par, cur_t.m0, cur_t.n0);
+                issue(nslot, same ? cur_t.ra : nxt_t.ra, same ? cur_t.rw : nxt_t.rw, same ? s + 2 : s + 2 - nsteps,
+                      grp_a ? 1 : 2);
             }
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): fragments (and scales) in
-            unpack0();
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- compute phase
-            comp();
-            if (grp_a) {
-                // stage s+1 landed: after it, this wave has issued stage s+2's
-                // loads and, in a tile's first step, the previous tile's
-                // output stores (or their stand-ins) before them
+            if (!grp_a) {
+                // group B: its weights of stage s+1 landed (the scales of the
+                // tile, issued before its stage-2 weights, by step 1).  After
+                // them this wave has issued this step's weights and, in a
+                // tile's first step, the previous tile's output stores and the
+                // scale loads before them (the first tile: stage 1 came from
+                // group A, so the wait has nothing to do)
                 asm volatile(
                     "s_cmp_eq_u32 %0, 0\n\t"
                     "s_cbranch_scc0 1f\n\t"
@@ -1281,7 +1288,27 @@ __global__ __launch_bounds__(512) void w4a4_gemm_pp_kernel(GemmArgs a, int tiles
                     "s_branch 2f\n"
                     "1:\n\t"
                     "s_waitcnt vmcnt(%2)\n"
-                    "2:" ::"s"(s), "n"(LPS + ST), "n"(LPS) : "memory", "scc");
+                    "2:" ::"s"(s), "n"(ST + 3 + LPB), "n"(LPB) : "memory", "scc");
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): fragments in
+            unpack0();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- compute phase
+            comp();
+            if (grp_a) {
+                // its codes of stage s+1 landed: after them this wave has
+                // issued stage s+2's codes and, in a tile's first step, the
+                // previous tile's output stores (or their stand-ins) before
+                // them
+                asm volatile(
+                    "s_cmp_eq_u32 %0, 0\n\t"
+                    "s_cbranch_scc0 1f\n\t"
+                    "s_waitcnt vmcnt(%1)\n\t"
+                    "s_branch 2f\n"
+                    "1:\n\t"
+                    "s_waitcnt vmcnt(%2)\n"
+                    "2:" ::"s"(s), "n"(LPA + ST), "n"(LPA) : "memory", "scc");
             }
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
