@@ -13,36 +13,48 @@
 //     once per workgroup; a row is up to four tiles of 16 group-rows, each
 //     rotated by eight v_mfma_f32_16x16x32 (B = the tile's x, two 16-byte
 //     loads a lane), column tile by column tile so that each R fragment is
-//     read from LDS once per row and used for every tile.
+//     read from LDS once per row and used for every tile (in registers the
+//     fragments took 32 VGPRs and a wave per SIMD).
 //   * The rotated values are rounded to T in pairs (v_cvt_pk) and kept packed:
 //     eight VGPRs a tile.  The row absmax is a packed 16-bit integer max over
 //     the sign-cleared patterns (monotone in |y|; a NaN pattern exceeds every
 //     other) and one wave reduction: no second rotation, no LDS.
 //   * As soon as a row's tiles are rotated, the next row's loads go into the
 //     freed x registers, so each wave keeps one row in flight while it
-//     quantizes the previous one; under 128 VGPRs leave room for four waves a
-//     SIMD.
-//   * Codes: with rinv = 1/s (IEEE), the integers RNE(y * rinv * (1 + 2^-21))
-//     and RNE(y * rinv * (1 - 2^-21)), each one fma against 1.5 * 2^23 (the
-//     add rounds the exact product to an integer and leaves it in the low
-//     byte), bracket the correctly rounded quotient fl(y / s): when they agree
-//     that integer IS the code (rounding is monotone).  They disagree only
-//     when y / s lies within 2^-20 of a half-integer, which for 16-bit y and a
+//     quantizes the previous one.  96 VGPRs (bf16): four workgroups of four
+//     waves per CU, so 8192 rows give every wave exactly two.
+//   * Row indices are 32-bit: every row test is a scalar compare, and the
+//     per-row buffer resources (rows past M get a zero-sized one) stay in
+//     SGPRs with no exec-masked code around the stores; the scale is stored
+//     by a buffer store whose lanes other than 0 fall past its 4-byte range.
+//   * Row scale: s = max(a / qmax, 2^-126), 1/s and the outcomes of exact
+//     ties depend only on the significand of the 16-bit absmax a, up to a
+//     power of two while every value stays normal; a compile-time table per
+//     significand (scale_table.hpp), read with scalar loads and shifted by a's
+//     exponent, replaces the per-row IEEE divisions.  Rows outside the
+//     table's range (zero, a < 2^-119, Inf, NaN) take the divisions.
+//   * Codes: with rinv = 1/s, the integers RNE(y * rinv * (1 + 2^-21)) and
+//     RNE(y * rinv * (1 - 2^-21)), each one fma against 1.5 * 2^23 (the add
+//     rounds the exact product to an integer and leaves it in the low byte),
+//     bracket the correctly rounded quotient fl(y / s): when they agree that
+//     integer IS the code (rounding is monotone).  They disagree only when
+//     y / s lies within 2^-20 of a half-integer, which for 16-bit y and a
 //     scale taken from the row's own 16-bit absmax a happens only at exact
 //     ties 7 y = (k + 1/2) a, k = 0..6.  All elements of a row that tie at
-//     the same k have the same |y|, so seven IEEE divisions per row (one per
-//     lane) decide, once, whether each k rounds away from zero; every element
-//     then takes its code from the two integers and that 7-bit table with
-//     three integer operations, with no branch and no per-element division.
-//     When 7 does not divide the integer significand of a, a tie needs
-//     7 | 2k + 1, i.e. k = 3 only: then the one multiplier that rounds that
-//     tie the quantizer's way gives every code with a single fma (most rows).
-//     Rows whose scale is Inf or NaN take the division for every element.
+//     the same k have the same |y|, so a 7-bit mask per row (bit k: the tie
+//     at k rounds away from zero) decides every tie; each element takes its
+//     code from the two integers and that mask with one bitfield extract and
+//     one bitwise select, with no branch and no per-element division.  When
+//     7 does not divide the integer significand of a, a tie needs 7 | 2k + 1,
+//     i.e. k = 3 only: then the one multiplier that rounds that tie the
+//     quantizer's way gives every code with a single fma (most rows).  Rows
+//     whose scale is Inf or NaN take the division for every element.
 //   * Each lane holds four codes of each of four column tiles; two
 //     v_permlane32_swap and two v_permlane16_swap transpose them so that every
 //     lane stores 16 consecutive codes (one 1 KB store per tile and wave).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "scale_table.hpp"
 
 namespace w4a4 {
 
@@ -121,12 +133,14 @@ __device__ __forceinline__ uint32_t tie_mask(float a, float s, bool clamped, int
 }
 
 // code byte of y from its two bracketing roundings (magic sums) and the tie
-// mask: t_dn when they agree (then t_up == t_dn), else the tie's outcome
+// mask: t_dn when they agree (then t_up == t_dn), else the tie's outcome.
+// The mask bit, sign-extended to all ones or zero, selects t_up or t_dn with
+// one bitfield insert
 __device__ __forceinline__ uint32_t tie_select(float t_up, float t_dn, uint32_t mask)
 {
     const uint32_t u = __float_as_uint(t_up), d = __float_as_uint(t_dn);
-    const uint32_t up = __builtin_amdgcn_ubfe(mask, d & 31u, 1u);
-    return d + up * (u - d);
+    const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)mask, (int)(d & 31u), 1);
+    return (sel & u) | (~sel & d);
 }
 
 // four code bytes (in the low byte of each value) in one dword
@@ -145,11 +159,25 @@ __device__ __forceinline__ int code_of_quotient(float qv)
     return (int)__builtin_amdgcn_fmed3f(rintf(qv), -(float)QMAX, (float)QMAX);
 }
 
+// per-significand row scales (exact: see scale_table.hpp), read with scalar
+// loads since the row's absmax is uniform across its wave
+__constant__ const RowScaleTable<7> kRowScaleBf16Q7 = make_row_scale_table<7, 7>();
+__constant__ const RowScaleTable<7> kRowScaleBf16Q127 = make_row_scale_table<7, 127>();
+__constant__ const RowScaleTable<10> kRowScaleF16Q7 = make_row_scale_table<10, 7>();
+__constant__ const RowScaleTable<10> kRowScaleF16Q127 = make_row_scale_table<10, 127>();
+
+template <int DT, int QMAX>
+__device__ __forceinline__ const RowScaleEntry& row_scale_entry(uint32_t idx)
+{
+    if constexpr (DT == BF16) return QMAX == 7 ? kRowScaleBf16Q7.e[idx] : kRowScaleBf16Q127.e[idx];
+    else return QMAX == 7 ? kRowScaleF16Q7.e[idx] : kRowScaleF16Q127.e[idx];
+}
+
 }  // namespace
 
 template <int DT, bool SMOOTH, bool YOUT, int TW, int PF, int QMAX>
-__global__ __launch_bounds__(256, 2) void rq_row_kernel(
-    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t sm,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void rq_row_kernel(
+    const uint16_t* __restrict__ x, int M, int64_t K, int64_t sm,
     const float* __restrict__ rot, const uint16_t* __restrict__ smooth,
     int8_t* __restrict__ codes, float* __restrict__ scales, uint16_t* __restrict__ yout)
 {
@@ -158,11 +186,14 @@ __global__ __launch_bounds__(256, 2) void rq_row_kernel(
     const int lane = threadIdx.x & 63;
     const int j = lane & 15, q = lane >> 4;
     const int gpr = (int)(K / GP);
-    const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
+    // row indices are 32-bit (the launcher requires M < 2^30) so that every
+    // row test is a scalar compare: the buffer resources built from them stay
+    // in SGPRs
+    const int nw = (int)gridDim.x * (int)(blockDim.x >> 6);
     // the wave's row is uniform: row pointers live in SGPRs and every load
     // and store is a scalar base plus a 32-bit lane offset
     const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + wid;
+    int row = (int)blockIdx.x * (int)(blockDim.x >> 6) + wid;
 
     // this lane's byte offsets in tile u (x, codes); lanes past the row's
     // last group-row get an offset past the row, so their loads read zeros
@@ -181,8 +212,9 @@ __global__ __launch_bounds__(256, 2) void rq_row_kernel(
     // memory, so the loads need no branch (and the compiler's wait counts
     // stay exact)
     v8s xf[PF][TW][NKS];
-    auto load_row = [&](v8s (&buf)[TW][NKS], int64_t r) {
-        const __amdgpu_buffer_rsrc_t rx = r < M ? row_rsrc(x + r * sm, (uint32_t)(2 * K)) : row_rsrc(x, 0u);
+    auto load_row = [&](v8s (&buf)[TW][NKS], int r) {
+        const bool live = r < M;
+        const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + (int64_t)(live ? r : 0) * sm, live ? (uint32_t)(2 * K) : 0u);
 #pragma unroll
         for (int u = 0; u < TW; ++u)
 #pragma unroll
@@ -192,20 +224,23 @@ __global__ __launch_bounds__(256, 2) void rq_row_kernel(
 #pragma unroll
     for (int p = 0; p < PF; ++p) load_row(xf[p], row + p * nw);
 
-    // R's MFMA fragments (A operand) in registers, rounded to T: fragment
-    // f = ct*2 + ks of lane (j, q) holds T(R[q*16 + ks*8 + e][ct*16 + j]),
-    // e = 0..7 (read once per wave from the fp32 matrix, after the first
-    // rows' loads are on their way)
-    v8s rf[CT * NKS];
+    // R's MFMA fragments (A operand), rounded to T: fragment f = ct*2 + ks of
+    // lane (j, q) holds T(R[q*16 + ks*8 + e][ct*16 + j]), e = 0..7.  Built
+    // once per workgroup from the fp32 matrix after the first rows' loads are
+    // on their way
+    __shared__ v8s rlds[CT * NKS][64];
+    for (int e = threadIdx.x; e < CT * NKS * 64; e += blockDim.x) {
+        const int f = e >> 6, jj = e & 15, qq = (e >> 4) & 3;
+        v8s v;
 #pragma unroll
-    for (int f = 0; f < CT * NKS; ++f)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            rf[f][e] = (short)f32_to_h<DT>(rot[(q * LPL + (f & 1) * 8 + e) * GP + (f >> 1) * 16 + j]);
+        for (int i = 0; i < 8; ++i) v[i] = (short)f32_to_h<DT>(rot[(qq * LPL + (f & 1) * 8 + i) * GP + (f >> 1) * 16 + jj]);
+        rlds[f][e & 63] = v;
+    }
+    __syncthreads();
 
     // one row: rotate, absmax, refill this buffer with the row PF*nw ahead,
     // scale, codes
-    auto process = [&](v8s (&buf)[TW][NKS], int64_t r) {
+    auto process = [&](v8s (&buf)[TW][NKS], int r) {
         if constexpr (SMOOTH) {
             // x' = T(fp32(x) / fp32(smooth)), one IEEE division per value
             // (lanes past the row keep their zeros)
@@ -225,13 +260,17 @@ __global__ __launch_bounds__(256, 2) void rq_row_kernel(
         }
         // rotate every tile, one column tile of R at a time; keep the rounded
         // values packed; packed absmax per tile
+        // the fragments are re-read from LDS for every row: an opaque lane
+        // index keeps the compiler from hoisting them into 32 live VGPRs
+        int rlane = lane;
+        asm volatile("" : "+v"(rlane));
         uint32_t yp[TW][CT][2];
         v2u16 um[TW];
 #pragma unroll
         for (int u = 0; u < TW; ++u) um[u] = (v2u16){0, 0};
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-            const v8s a0 = rf[ct * NKS + 0], a1 = rf[ct * NKS + 1];
+            const v8s a0 = rlds[ct * NKS + 0][rlane], a1 = rlds[ct * NKS + 1][rlane];
 #pragma unroll
             for (int u = 0; u < TW; ++u) {
                 v4f acc = {0.f, 0.f, 0.f, 0.f};
@@ -261,14 +300,49 @@ __global__ __launch_bounds__(256, 2) void rq_row_kernel(
         // the row PF*nw ahead goes into the x registers the rotation freed
         load_row(buf, r + PF * nw);
 
-        // row scale: IEEE a / 7, clamped up to the smallest normal
+        // row scale s = max(a / qmax, 2^-126), 1/s, the bracketing multipliers
+        // and the tie outcomes: from the significand table shifted by a's
+        // exponent (a scalar load, no division), or with IEEE divisions for
+        // the rows the table does not cover (zero, tiny, Inf, NaN)
         const uint32_t a16 = wave_max_u32(max((uint32_t)amax[0], (uint32_t)amax[1]));
-        const float a = DT == BF16 ? __uint_as_float(a16 << 16) : f16_to_f32((uint16_t)a16);
-        float s = a / (float)QMAX;
-        if (s < 0x1p-126f) s = 0x1p-126f;  // NaN compares false and stays NaN
-        if (lane == 0 && r < M) scales[r] = s;
+        uint32_t tidx;
+        int tE;
+        float s, rinv, rh, rl, r1;
+        uint32_t tmask;
+        bool one;
+        if (row_scale_key<DT == BF16>(a16, tidx, tE)) {
+            const RowScaleEntry& te = row_scale_entry<DT, QMAX>(tidx);
+            s = row_scale_shift(te.s, tE);
+            rinv = row_scale_shift(te.rinv, -tE);
+            rh = row_scale_shift(te.rh, -tE);
+            rl = row_scale_shift(te.rl, -tE);
+            r1 = row_scale_shift(te.r1, -tE);
+            tmask = te.tie;
+            one = te.one != 0u;
+        } else {
+            const float a = DT == BF16 ? __uint_as_float(a16 << 16) : f16_to_f32((uint16_t)a16);
+            s = a / (float)QMAX;
+            if (s < 0x1p-126f) s = 0x1p-126f;  // NaN compares false and stays NaN
+            const bool clamped = s == 0x1p-126f;
+            rinv = 1.0f / s;
+            rh = rinv * (1.0f + 0x1p-21f);
+            rl = rinv * (1.0f - 0x1p-21f);
+            tmask = QMAX == 7 && fabsf(s) < 3.0e38f ? tie_mask(a, s, clamped, lane) : 0u;
+            r1 = (tmask & 8u) ? rh : rl;
+            // a's integer significand: when 7 does not divide it, the only
+            // tie a 16-bit element can make is y = a / 2 (k = 3)
+            const uint32_t sig = DT == BF16 ? ((a16 >> 7) & 0xffu ? (a16 & 0x7fu) | 0x80u : a16 & 0x7fu)
+                                            : ((a16 >> 10) & 0x1fu ? (a16 & 0x3ffu) | 0x400u : a16 & 0x3ffu);
+            one = !clamped && sig % 7u != 0u;
+        }
+        const bool live = r < M;
+        const int64_t rr = live ? r : 0;
+        // lane 0 stores the scale; the other lanes' offsets fall past the
+        // 4-byte resource and are dropped (no branch)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), row_rsrc(scales + rr, live ? 4u : 0u),
+                                              lane == 0 ? 0 : 4, 0, 0);
         const bool finite = fabsf(s) < 3.0e38f;
-        const __amdgpu_buffer_rsrc_t rc = r < M ? row_rsrc(codes + r * K, (uint32_t)K) : row_rsrc(codes, 0u);
+        const __amdgpu_buffer_rsrc_t rc = row_rsrc(codes + rr * K, live ? (uint32_t)K : 0u);
 
         // transpose the codes of tile u (4 x 4 dwords across the lane groups:
         // lane group q then holds bytes q*16 .. q*16+15 of its group-row) and
@@ -282,8 +356,7 @@ __global__ __launch_bounds__(256, 2) void rq_row_kernel(
             if constexpr (YOUT) {
                 // rotated values of columns ct*16 + 4q .. +3: byte offset
                 // 2*(b*64) + 32*ct + 8q
-                const __amdgpu_buffer_rsrc_t ry =
-                    r < M ? row_rsrc(yout + r * K, (uint32_t)(2 * K)) : row_rsrc(yout, 0u);
+                const __amdgpu_buffer_rsrc_t ry = row_rsrc(yout + rr * K, live ? (uint32_t)(2 * K) : 0u);
                 const int yo = coff[u] < (int)K ? 2 * (coff[u] - q * 16) + 8 * q : (int)(2 * K);
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
@@ -292,17 +365,11 @@ __global__ __launch_bounds__(256, 2) void rq_row_kernel(
             }
         };
 
-        // a's integer significand: when 7 does not divide it, the only tie a
-        // 16-bit element can make is y = a / 2 (k = 3)
-        const uint32_t sig = DT == BF16 ? ((a16 >> 7) & 0xffu ? (a16 & 0x7fu) | 0x80u : a16 & 0x7fu)
-                                        : ((a16 >> 10) & 0x1fu ? (a16 & 0x3ffu) | 0x400u : a16 & 0x3ffu);
-        const bool clamped = s == 0x1p-126f;
         if constexpr (QMAX == 127) {
             // INT8 mode: one rounding per element (|y / s| <= 127 (1 + 2^-23),
             // so y * (1/s) is within 2^-15 of fl(y / s)); a quotient within
             // 2^-13 of a half-integer sends its group of four to the IEEE
             // division, as does a scale that is not finite
-            const float rinv = 1.0f / s;
 #pragma unroll
             for (int u = 0; u < TW; ++u) {
                 uint32_t P[CT];
@@ -327,13 +394,10 @@ __global__ __launch_bounds__(256, 2) void rq_row_kernel(
                 }
                 store_tile(u, P);
             }
-        } else if (__builtin_expect(finite && !clamped && sig % 7u != 0u, 1)) {
+        } else if (__builtin_expect(finite && one, 1)) {
             // one rounding per element: of the two bracketing multipliers,
             // the one that takes the k = 3 tie the quantizer's way gives every
             // code (the two agree on every element that is not a tie)
-            const float rinv = 1.0f / s;
-            const float rh = rinv * (1.0f + 0x1p-21f), rl = rinv * (1.0f - 0x1p-21f);
-            const float r1 = (tie_mask(a, s, false, lane) & 8u) ? rh : rl;
 #pragma unroll
             for (int u = 0; u < TW; ++u) {
                 uint32_t P[CT];
@@ -348,9 +412,6 @@ __global__ __launch_bounds__(256, 2) void rq_row_kernel(
                 store_tile(u, P);
             }
         } else if (finite) {
-            const float rinv = 1.0f / s;
-            const float rh = rinv * (1.0f + 0x1p-21f), rl = rinv * (1.0f - 0x1p-21f);
-            const uint32_t tmask = tie_mask(a, s, clamped, lane);
 #pragma unroll
             for (int u = 0; u < TW; ++u) {
                 uint32_t P[CT];
@@ -405,7 +466,7 @@ __global__ __launch_bounds__(256, 2) void rq_row_kernel(
 bool row_kernel_ok(const RQArgs& a)
 {
     const bool sixteen = a.dtype == F16 || a.dtype == BF16;
-    if (!sixteen || !a.rot || a.g != 64 || a.sk != 1 || a.M < 2048) return false;
+    if (!sixteen || !a.rot || a.g != 64 || a.sk != 1 || a.M < 2048 || a.M >= (int64_t(1) << 30)) return false;
     if ((a.K % 64) != 0) return false;
     const int64_t gpr = a.K / 64;
     if (gpr <= 16 || gpr > 64) return false;
@@ -436,10 +497,13 @@ static hipError_t launch_row_t(const RQArgs& a, hipStream_t st)
             n_cu = p.multiProcessorCount;
         }
     }
-    int64_t grid = (int64_t)per_cu * n_cu;
+    // at most four workgroups (16 waves) per CU: with 8192 rows every wave
+    // then takes exactly two (a fifth workgroup, which the registers would
+    // allow, leaves waves with one or two rows and measured slower)
+    int64_t grid = (int64_t)(per_cu < 4 ? per_cu : 4) * n_cu;
     const int64_t need = (a.M + 3) / 4;   // four waves (rows) per workgroup
     if (grid > need) grid = need;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.x, a.M, a.K,
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.x, (int)a.M, a.K,
                        a.sm, a.rot, (const uint16_t*)a.smooth, a.codes, a.scales, (uint16_t*)a.yout);
     return hipGetLastError();
 }
