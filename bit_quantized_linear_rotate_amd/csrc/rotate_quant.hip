@@ -27,6 +27,7 @@
 //     the code identical to the correctly-rounded quotient's.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "row_quant.hpp"
 
 namespace w4a4 {
 
@@ -134,6 +135,13 @@ __device__ __forceinline__ uint32_t quant4_finite(const float (&y)[4], float rin
         near |= fabsf(qv - r) > 0.5f - 0x1p-17f;
     }
     return pack4_magic(t[0], t[1], t[2], t[3]);
+}
+
+// fp32 pattern of T(|v|) for the sign-cleared fp32 pattern of v
+template <int DT>
+__device__ __forceinline__ uint32_t round_bits(uint32_t vbits)
+{
+    return __float_as_uint(h_to_f32<DT>(f32_to_h<DT>(__uint_as_float(vbits))));
 }
 
 __device__ __forceinline__ float row_scale(uint32_t absmax_bits)
@@ -624,7 +632,7 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
     __shared__ __align__(16) int8_t ctile[2][CM_ROWS * GP];
     __shared__ __align__(16) uint16_t ytile[2][YOUT ? CM_ROWS * GP : 8];
     __shared__ uint32_t rowmax[CM_ROWS];
-    __shared__ float rowsc[CM_ROWS], rowinv[CM_ROWS];
+    __shared__ RowQuant rowq[CM_ROWS];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -709,7 +717,7 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
         }
     };
 
-    float rsc[MPW], rinv[MPW];  // scale of this lane's row in each row tile (pass 2)
+    RowQuant rq[MPW];  // quantizer of this lane's row in each row tile (pass 2)
     const int nsteps = 2 * G;
     if (loader)
         for (int i = 0; i < NSTG - 1 && i < nsteps; ++i) issue(i, i % G);
@@ -789,15 +797,18 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
             }
         }
         if (!pass2) {
+            // the row absmax of the unrounded values as an integer max of the
+            // sign-cleared fp32 patterns (a NaN pattern exceeds every other);
+            // rounding to T is monotone, so rounding the maximum once per row
+            // gives the maximum of the rounded values
 #pragma unroll
             for (int mi = 0; mi < MPW; ++mi)
 #pragma unroll
-                for (int jj = 0; jj < JPW; ++jj)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const uint16_t yb = f32_to_h<DT>(acc[mi][jj][r]);
-                        rmax[mi] = max(rmax[mi], __float_as_uint(h_to_f32<DT>(yb)) & 0x7fffffffu);
-                    }
+                for (int jj = 0; jj < JPW; ++jj) {
+                    const v4f a = acc[mi][jj];
+                    rmax[mi] = max(rmax[mi], max(__float_as_uint(a[0]) & 0x7fffffffu, __float_as_uint(a[1]) & 0x7fffffffu));
+                    rmax[mi] = max(rmax[mi], max(__float_as_uint(a[2]) & 0x7fffffffu, __float_as_uint(a[3]) & 0x7fffffffu));
+                }
             if (s == G - 1) {
                 // row absmax across the four lane groups, then across waves
 #pragma unroll
@@ -809,32 +820,28 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
                 }
                 lds_barrier();
                 if (tid < CM_ROWS) {
-                    const float sc = row_scale(rowmax[tid]);
-                    rowsc[tid] = sc;
-                    rowinv[tid] = 1.0f / sc;
+                    // T(max |y|) of the row, then its quantizer parameters
+                    const RowQuant p = row_quant_thread<DT>(f32_to_h<DT>(__uint_as_float(rowmax[tid])));
+                    rowq[tid] = p;
+                    if (m0 + tid < M) scales[m0 + tid] = p.s;
                 }
-                if (st_tid >= 0 && st_tid < CM_ROWS && m0 + st_tid < M)
-                    scales[m0 + st_tid] = row_scale(rowmax[st_tid]);
                 lds_barrier();
 #pragma unroll
-                for (int mi = 0; mi < MPW; ++mi) {
-                    rsc[mi] = rowsc[(mt0 + mi) * 16 + n];
-                    rinv[mi] = rowinv[(mt0 + mi) * 16 + n];
-                }
+                for (int mi = 0; mi < MPW; ++mi) rq[mi] = rowq[(mt0 + mi) * 16 + n];
             }
             continue;
         }
         // pass 2: quantize four codes of one row at a time into this step's
         // code tile (the storers write out the previous step's tile
-        // meanwhile).  A quotient within 2^-17 of a half-integer, or a
-        // non-finite scale, sends the wave to the exact division.
+        // meanwhile): the two bracketing roundings and the row's tie mask.
+        // A non-finite scale sends the wave to the exact division.
         int8_t* ct = ctile[s & 1];
         float yv[MPW][JPW][4];
         bool near = false;
 #pragma unroll
         for (int mi = 0; mi < MPW; ++mi) {
             const int row = (mt0 + mi) * 16 + n;
-            near |= !(fabsf(rsc[mi]) < __builtin_inff());
+            near |= !(fabsf(rq[mi].s) < 3.0e38f);
 #pragma unroll
             for (int jj = 0; jj < JPW; ++jj) {
                 uint16_t yb[4];
@@ -844,7 +851,7 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
                     yv[mi][jj][r] = h_to_f32<DT>(yb[r]);
                 }
                 const int col = (jt0 + jj) * 16 + 4 * q;
-                lds_write4(ct + row * GP + col, quant4_finite(yv[mi][jj], rinv[mi], near));
+                lds_write4(ct + row * GP + col, quant4_bracket(yv[mi][jj], rq[mi]));
                 if constexpr (YOUT)
                     lds_write8(ytile[s & 1] + row * GP + col, (uint32_t)yb[0] | ((uint32_t)yb[1] << 16),
                                (uint32_t)yb[2] | ((uint32_t)yb[3] << 16));
@@ -856,7 +863,7 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
 #pragma unroll
                 for (int jj = 0; jj < JPW; ++jj)
                     lds_write4(ct + ((mt0 + mi) * 16 + n) * GP + (jt0 + jj) * 16 + 4 * q,
-                               quant4_exact(yv[mi][jj], rsc[mi]));
+                               quant4_exact(yv[mi][jj], rq[mi].s));
         }
     }
     // the last step's codes

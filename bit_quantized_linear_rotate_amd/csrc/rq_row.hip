@@ -54,7 +54,7 @@
 //     lane stores 16 consecutive codes (one 1 KB store per tile and wave).
 #include "common.hpp"
 #include "kernels.hpp"
-#include "scale_table.hpp"
+#include "row_quant.hpp"
 
 namespace w4a4 {
 
@@ -132,45 +132,12 @@ __device__ __forceinline__ uint32_t tie_mask(float a, float s, bool clamped, int
     return b | (__builtin_bitreverse32(b) << 1);
 }
 
-// code byte of y from its two bracketing roundings (magic sums) and the tie
-// mask: t_dn when they agree (then t_up == t_dn), else the tie's outcome.
-// The mask bit, sign-extended to all ones or zero, selects t_up or t_dn with
-// one bitfield insert
-__device__ __forceinline__ uint32_t tie_select(float t_up, float t_dn, uint32_t mask)
-{
-    const uint32_t u = __float_as_uint(t_up), d = __float_as_uint(t_dn);
-    const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)mask, (int)(d & 31u), 1);
-    return (sel & u) | (~sel & d);
-}
-
-// four code bytes (in the low byte of each value) in one dword
-__device__ __forceinline__ uint32_t pack_bytes(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3)
-{
-    const uint32_t lo = __builtin_amdgcn_perm(c1, c0, 0x0c0c0400u);
-    const uint32_t hi = __builtin_amdgcn_perm(c3, c2, 0x0c0c0400u);
-    return lo | (hi << 16);
-}
-
 // correctly rounded code for a finite or non-finite quotient (NaN -> 0)
 template <int QMAX>
 __device__ __forceinline__ int code_of_quotient(float qv)
 {
     if (qv != qv) return 0;
     return (int)__builtin_amdgcn_fmed3f(rintf(qv), -(float)QMAX, (float)QMAX);
-}
-
-// per-significand row scales (exact: see scale_table.hpp), read with scalar
-// loads since the row's absmax is uniform across its wave
-__constant__ const RowScaleTable<7> kRowScaleBf16Q7 = make_row_scale_table<7, 7>();
-__constant__ const RowScaleTable<7> kRowScaleBf16Q127 = make_row_scale_table<7, 127>();
-__constant__ const RowScaleTable<10> kRowScaleF16Q7 = make_row_scale_table<10, 7>();
-__constant__ const RowScaleTable<10> kRowScaleF16Q127 = make_row_scale_table<10, 127>();
-
-template <int DT, int QMAX>
-__device__ __forceinline__ const RowScaleEntry& row_scale_entry(uint32_t idx)
-{
-    if constexpr (DT == BF16) return QMAX == 7 ? kRowScaleBf16Q7.e[idx] : kRowScaleBf16Q127.e[idx];
-    else return QMAX == 7 ? kRowScaleF16Q7.e[idx] : kRowScaleF16Q127.e[idx];
 }
 
 }  // namespace
@@ -390,7 +357,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
                         for (int i = 0; i < 4; ++i)
                             c[i] = (uint32_t)code_of_quotient<127>(unpack_half<DT>(yp[u][ct][i >> 1], i & 1) / s);
                     }
-                    P[ct] = pack_bytes(c[0], c[1], c[2], c[3]);
+                    P[ct] = pack_code_bytes(c[0], c[1], c[2], c[3]);
                 }
                 store_tile(u, P);
             }
@@ -407,7 +374,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         c[i] = __float_as_uint(__builtin_fmaf(unpack_half<DT>(yp[u][ct][i >> 1], i & 1), r1, kMagic));
-                    P[ct] = pack_bytes(c[0], c[1], c[2], c[3]);
+                    P[ct] = pack_code_bytes(c[0], c[1], c[2], c[3]);
                 }
                 store_tile(u, P);
             }
@@ -423,7 +390,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
                         const float y = unpack_half<DT>(yp[u][ct][i >> 1], i & 1);
                         c[i] = tie_select(__builtin_fmaf(y, rh, kMagic), __builtin_fmaf(y, rl, kMagic), tmask);
                     }
-                    P[ct] = pack_bytes(c[0], c[1], c[2], c[3]);
+                    P[ct] = pack_code_bytes(c[0], c[1], c[2], c[3]);
                 }
                 store_tile(u, P);
             }
