@@ -694,7 +694,7 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
     // storer waves: codes (and rotated values) of step st from the LDS
     // staging tiles to global memory, 16 bytes per store
     auto store_group = [&](int st) {
-        const int bs = st - G;
+        const int bs = 2 * G - 1 - st;
         const int8_t* ct = ctile[st & 1];
 #pragma unroll
         for (int u = 0; u < NCS; ++u) {
@@ -718,12 +718,16 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
     };
 
     RowQuant rq[MPW];  // quantizer of this lane's row in each row tile (pass 2)
+    // group of step s: pass 1 walks the groups forward, pass 2 backward, so
+    // that the second pass starts on the tiles the first one read last
+    // (still in cache)
+    auto step_group = [G](int st) { return st < G ? st : 2 * G - 1 - st; };
     const int nsteps = 2 * G;
     if (loader)
-        for (int i = 0; i < NSTG - 1 && i < nsteps; ++i) issue(i, i % G);
+        for (int i = 0; i < NSTG - 1 && i < nsteps; ++i) issue(i, step_group(i));
     int cur = 0;  // ring slot of step s
     for (int s = 0; s < nsteps; ++s) {
-        const int b = s < G ? s : s - G;
+        const int b = step_group(s);
         const bool pass2 = s >= G;
         // a loader waits for its part of this step's tile; the next NSTG - 2
         // tiles' loads stay in flight (near the end, none)
@@ -733,7 +737,7 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
         }
         lds_barrier();  // also publishes the previous step's code tile
         const int nxt = cur == 0 ? NSTG - 1 : cur - 1;  // slot of step s - 1, free now
-        if (loader && s + NSTG - 1 < nsteps) issue(nxt, (s + NSTG - 1) % G);
+        if (loader && s + NSTG - 1 < nsteps) issue(nxt, step_group(s + NSTG - 1));
         if (!loader && s > G) store_group(s - 1);
         uint8_t* tile = stg[cur];
         cur = cur == NSTG - 1 ? 0 : cur + 1;
