@@ -427,6 +427,8 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_s_barrier();
 }
 
+typedef unsigned v2u32 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rq_rsrc(const void* base, uint64_t bytes)
 {
     const uint32_t n = bytes > 0x7fffffffull ? 0x7fffffffu : (uint32_t)bytes;
@@ -1390,33 +1392,41 @@ __global__ __launch_bounds__(256, TW >= 4 ? 2 : 3) void rq_wave_kernel(
 // -------------------------------------------------------------------------
 // g = 256 on contiguous rows (16-bit, K/256 <= 64 group-rows per row): the
 // rotation's 128 MFMA A fragments (R^T, rounded to T; 128 KB) live in LDS for
-// the life of a persistent workgroup, so each of its eight waves can own one
-// 16-group-row tile of one of its two current rows and apply the whole
-// rotation to it:
-// x is loaded (and smoothed) exactly once, the rotated values stay in
-// registers (two per VGPR), and only the row absmax crosses waves, through
-// LDS with one barrier per row.  The k-slots of each MFMA step are those of
-// the column-major kernel (lane group q, step ks: k = 64 q + 8 ks + e), so
-// the two give the same rotated bits.
+// the life of a persistent workgroup.  Its eight waves take 2 * RPW rows at a
+// time: wave (wr, wt) owns the wt-th 16-group-row tile of rows wr*RPW ..
+// wr*RPW + RPW - 1, and every R fragment it reads from LDS feeds one MFMA per
+// row (the LDS stream of R per row falls by RPW).  x is loaded (and smoothed)
+// exactly once, the rotated values stay in registers (two per VGPR), and only
+// the row absmax crosses waves, through LDS with one barrier per 2 * RPW
+// rows.  The k-slots of each MFMA step are those of the column-major kernel
+// (lane group q, step ks: k = 64 q + 8 ks + e), so the two give the same
+// rotated bits.  The row absmax is a packed 16-bit max of the sign-cleared
+// patterns (a NaN pattern exceeds every other).  INT4 codes come from the two
+// bracketing multipliers and the row's tie mask (row_quant.hpp); the INT8
+// mode keeps the product with a residual test and an exact division near
+// half-integers.
 // -------------------------------------------------------------------------
-template <int DT, bool SMOOTH, int QMAX = 7>
+template <int DT, bool SMOOTH, int QMAX = 7, int RPW = 1>
 __global__ __launch_bounds__(512) void rq_g256_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t sm,
     const float* __restrict__ rot, const uint16_t* __restrict__ smooth,
     int8_t* __restrict__ codes, float* __restrict__ scales, uint16_t* __restrict__ yout)
 {
     constexpr int GP = 256, CT = 16, NKS = 8, LPL = 64;
+    constexpr int RB = 2 * RPW;                      // rows per workgroup step
     __shared__ __align__(16) v8s rs[CT * NKS][64];   // fragment (ct, ks), lane-major
-    __shared__ uint32_t wmax[2][8];
+    __shared__ uint32_t wmax[2][8][RPW];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wr = wave >> 2, wt = wave & 3;     // row of the pair, tile in the row
-    const int j = lane & 15, q = lane >> 4;
+    // (the wave index is uniform: row bases and buffer resources stay scalar)
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int wr = wave >> 2, wt = wave & 3;     // row pair, tile in the row
+    const int q = lane >> 4;
     const int G = (int)(K / GP);
     const int ntile = (G + 15) >> 4;
 
     // R^T fragments: element (kk, c) of R goes to fragment (c / 16, (kk % 64) / 8),
     // lane (kk / 64) * 16 + c % 16, slot kk % 8 (coalesced reads of R)
+#pragma unroll 4
     for (int idx = tid; idx < GP * GP; idx += 512) {
         const int kk = idx >> 8, c = idx & 255;
         uint16_t* dst = (uint16_t*)&rs[(c >> 4) * NKS + ((kk & 63) >> 3)][(kk >> 6) * 16 + (c & 15)];
@@ -1424,114 +1434,156 @@ __global__ __launch_bounds__(512) void rq_g256_kernel(
     }
     __syncthreads();
 
-    const int gr = wt * 16 + j;                  // this lane's group-row in the row
+    const int gr = wt * 16 + (lane & 15);        // this lane's group-row in the row
     const bool tlive = wt < ntile && gr < G;
     const int xo = gr * GP + q * LPL;            // element offset of the lane's slice
 
+    // lanes past the row's last group-row take offsets past the row: their
+    // loads read zeros and their stores are dropped by the range check
+    const int xoff = tlive ? xo * 2 : (int)(2 * K);
+    const int coff = tlive ? gr * GP + 4 * q : (int)K;
     auto load_row = [&](int64_t row, v8s (&xf)[NKS]) {
-        if (tlive && row < M) {
-            // plain loads: each lane reads one whole 128-byte line in eight
-            // 16-byte pieces, and only a cached line serves the later seven
-            // (non-temporal loads sent every piece to L2)
-            const v4i* src = (const v4i*)(x + row * sm + xo);
+        const bool rl = row < M;
+        // plain loads: each lane reads one whole 128-byte line in eight
+        // 16-byte pieces, and only a cached line serves the later seven
+        // (non-temporal loads sent every piece to L2)
+        const __amdgpu_buffer_rsrc_t rx = rq_rsrc(x + (rl ? row : 0) * sm, rl ? (uint64_t)K * 2 : 0);
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) xf[ks] = __builtin_bit_cast(v8s, src[ks]);
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) xf[ks] = (v8s){0, 0, 0, 0, 0, 0, 0, 0};
-        }
+        for (int ks = 0; ks < NKS; ++ks)
+            xf[ks] = __builtin_bit_cast(v8s, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + 16 * ks, 0, 0));
     };
 
-    v8s xa[NKS], xb[NKS];
+    // the rows' x in registers; the next rows' loads go into them as soon as
+    // the rotation has read them, so they are in flight during the absmax
+    // exchange and the quantization
+    v8s xa[RPW][NKS];
     int par = 0;
-    const int64_t rstep = 2 * (int64_t)gridDim.x;
-    load_row(2 * (int64_t)blockIdx.x + wr, xa);
-    for (int64_t row0 = 2 * (int64_t)blockIdx.x; row0 < M; row0 += rstep, par ^= 1) {
-        const int64_t row = row0 + wr;
-        const bool live = tlive && row < M;
-        load_row(row + rstep, xb);
+    const int64_t rstep = RB * (int64_t)gridDim.x;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) load_row(RB * (int64_t)blockIdx.x + wr * RPW + i, xa[i]);
+    for (int64_t row0 = RB * (int64_t)blockIdx.x; row0 < M; row0 += rstep, par ^= 1) {
+        const int64_t rowb = row0 + wr * RPW;
         if constexpr (SMOOTH) {
-            if (live) {
+            if (tlive) {
                 const v4i* sp = (const v4i*)(smooth + xo);
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
                     const v8s sv = __builtin_bit_cast(v8s, sp[ks]);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        xa[ks][e] = (short)f32_to_h<DT>(h_to_f32<DT>((uint16_t)xa[ks][e]) /
-                                                        h_to_f32<DT>((uint16_t)sv[e]));
+                    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            xa[i][ks][e] = (short)f32_to_h<DT>(h_to_f32<DT>((uint16_t)xa[i][ks][e]) /
+                                                               h_to_f32<DT>((uint16_t)sv[e]));
                 }
             }
         }
         // rotate: lane (j, q) gets output columns 16 ct + 4 q .. + 3 of
-        // group-row j, rounded to T and packed two per register
-        uint32_t yp[CT][2];
-        uint32_t m = 0u;
+        // group-row j of each of its rows, rounded to T and packed two per
+        // register
+        typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+        uint32_t yp[RPW][CT][2];
+        v2u16 m2[RPW];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) m2[i] = (v2u16){0, 0};
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-            v4f acc = {0.f, 0.f, 0.f, 0.f};
+            v4f acc[RPW];
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) acc[i] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const v8s af = rs[ct * NKS + ks][lane];
-                if constexpr (DT == BF16)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, af),
-                                                                  __builtin_bit_cast(v8bf, xa[ks]), acc, 0, 0, 0);
-                else
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, af),
-                                                                 __builtin_bit_cast(v8h, xa[ks]), acc, 0, 0, 0);
-            }
-            uint16_t h[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                h[r] = f32_to_h<DT>(acc[r]);
-                m = max(m, __float_as_uint(h_to_f32<DT>(h[r])) & 0x7fffffffu);
-            }
-            yp[ct][0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-            yp[ct][1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-        }
-        // row absmax: a wave max, then the four waves' through LDS (two
-        // buffers by row parity, so one barrier per row suffices)
-        m = wave_max_dpp(live ? m : 0u);
-        if (lane == 0) wmax[par][wave] = m;
-        __syncthreads();
-        const uint32_t* wm = wmax[par] + 4 * wr;
-        const uint32_t v = max(max(wm[0], wm[1]), max(wm[2], wm[3]));
-        const float sv = row_scale_q<QMAX>(v);
-        const float ri = 1.0f / sv;
-        if (wt == 0 && lane == 0 && row < M) scales[row] = sv;
-        // quantize: exact division only where a quotient is near a tie or the
-        // scale is not finite (|y * ri - fl(y / s)| <= 2 QMAX 2^-24, so the
-        // band is 2^-17 for INT4 codes and 2^-13 in the INT8 mode)
-        constexpr float kBand = QMAX == 7 ? 0x1p-17f : 0x1p-13f;
-        constexpr float kQ = (float)QMAX;
-        const bool fin = fabsf(sv) < 3.0e38f;
-        int8_t* cb = codes + (live ? row : 0) * K + gr * GP;
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            float yy[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) yy[r] = h_to_f32<DT>((uint16_t)(yp[ct][r >> 1] >> (16 * (r & 1))));
-            uint32_t pk;
-            if (!fin) {
-                pk = quant4_exact<QMAX>(yy, sv);
-            } else {
-                float t[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float qv = yy[r] * ri;
-                    t[r] = __builtin_amdgcn_fmed3f(qv, -kQ, kQ) + kRoundMagic;
-                    const bool nr = fabsf(qv - (t[r] - kRoundMagic)) > 0.5f - kBand;
-                    if (__any(nr)) t[r] = __builtin_amdgcn_fmed3f(yy[r] / sv, -kQ, kQ) + kRoundMagic;
+                for (int i = 0; i < RPW; ++i) {
+                    if constexpr (DT == BF16)
+                        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, af),
+                                                                         __builtin_bit_cast(v8bf, xa[i][ks]), acc[i], 0, 0, 0);
+                    else
+                        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, af),
+                                                                        __builtin_bit_cast(v8h, xa[i][ks]), acc[i], 0, 0, 0);
                 }
-                pk = pack4_magic(t[0], t[1], t[2], t[3]);
             }
-            if (live) {
-                *(uint32_t*)(cb + ct * 16 + 4 * q) = pk;
-                if (yout) *(uint2*)(yout + row * K + gr * GP + ct * 16 + 4 * q) = make_uint2(yp[ct][0], yp[ct][1]);
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) {
+                yp[i][ct][0] = (uint32_t)f32_to_h<DT>(acc[i][0]) | ((uint32_t)f32_to_h<DT>(acc[i][1]) << 16);
+                yp[i][ct][1] = (uint32_t)f32_to_h<DT>(acc[i][2]) | ((uint32_t)f32_to_h<DT>(acc[i][3]) << 16);
+                m2[i] = __builtin_elementwise_max(m2[i], __builtin_bit_cast(v2u16, yp[i][ct][0] & 0x7fff7fffu));
+                m2[i] = __builtin_elementwise_max(m2[i], __builtin_bit_cast(v2u16, yp[i][ct][1] & 0x7fff7fffu));
             }
+            // one column tile at a time: only its fragments and results live
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) xa[ks] = xb[ks];
+        for (int i = 0; i < RPW; ++i) load_row(rowb + i + rstep, xa[i]);
+        // row absmax: a wave max, then the four waves' through LDS (two
+        // buffers by step parity, so one barrier per step suffices)
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const uint32_t mi = wave_max_dpp(tlive ? max((uint32_t)m2[i][0], (uint32_t)m2[i][1]) : 0u);
+            if (lane == 0) wmax[par][wave][i] = mi;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int64_t row = rowb + i;
+            const uint32_t* wm = &wmax[par][4 * wr][i];
+            const uint32_t a16 = max(max(wm[0], wm[RPW]), max(wm[2 * RPW], wm[3 * RPW]));
+            const bool rl = row < M;
+            const __amdgpu_buffer_rsrc_t rc = rq_rsrc(codes + (rl ? row : 0) * K, rl ? (uint64_t)K : 0);
+            const __amdgpu_buffer_rsrc_t ry =
+                rq_rsrc(yout + (rl && yout ? row : 0) * K, rl && yout ? (uint64_t)K * 2 : 0);
+            if constexpr (QMAX == 7) {
+                const RowQuant p = row_quant_thread<DT>(a16);
+                if (wt == 0 && lane == 0 && rl) scales[row] = p.s;
+                const bool fin = fabsf(p.s) < 3.0e38f;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    float yy[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) yy[r] = h_to_f32<DT>((uint16_t)(yp[i][ct][r >> 1] >> (16 * (r & 1))));
+                    const uint32_t pk = fin ? quant4_bracket(yy, p) : quant4_exact<7>(yy, p.s);
+                    __builtin_amdgcn_raw_buffer_store_b32(pk, rc, coff + ct * 16, 0, 0);
+                    if (yout)
+                        __builtin_amdgcn_raw_buffer_store_b64((v2u32){yp[i][ct][0], yp[i][ct][1]}, ry,
+                                                              2 * (coff + ct * 16), 0, 0);
+                }
+            } else {
+                const float sv = row_scale_q<QMAX>(__float_as_uint(h_to_f32<DT>((uint16_t)a16)));
+                const float ri = 1.0f / sv;
+                if (wt == 0 && lane == 0 && rl) scales[row] = sv;
+                // exact division only where a quotient is near a tie or the
+                // scale is not finite (|y * ri - fl(y / s)| <= 2 QMAX 2^-24,
+                // so the band is 2^-13 in the INT8 mode)
+                constexpr float kBand = 0x1p-13f;
+                constexpr float kQ = (float)QMAX;
+                const bool fin = fabsf(sv) < 3.0e38f;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    float yy[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) yy[r] = h_to_f32<DT>((uint16_t)(yp[i][ct][r >> 1] >> (16 * (r & 1))));
+                    uint32_t pk;
+                    if (!fin) {
+                        pk = quant4_exact<QMAX>(yy, sv);
+                    } else {
+                        float t[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float qv = yy[r] * ri;
+                            t[r] = __builtin_amdgcn_fmed3f(qv, -kQ, kQ) + kRoundMagic;
+                            const bool nr = fabsf(qv - (t[r] - kRoundMagic)) > 0.5f - kBand;
+                            if (__any(nr)) t[r] = __builtin_amdgcn_fmed3f(yy[r] / sv, -kQ, kQ) + kRoundMagic;
+                        }
+                        pk = pack4_magic(t[0], t[1], t[2], t[3]);
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b32(pk, rc, coff + ct * 16, 0, 0);
+                    if (yout)
+                        __builtin_amdgcn_raw_buffer_store_b64((v2u32){yp[i][ct][0], yp[i][ct][1]}, ry,
+                                                              2 * (coff + ct * 16), 0, 0);
+                }
+            }
+        }
     }
 }
 
@@ -1547,14 +1599,19 @@ static hipError_t launch_g256_dt(const RQArgs& a, hipStream_t st)
         else
             n_cu = 256;
     }
-    const int64_t pairs = (a.M + 1) / 2;
-    const int64_t grid = pairs < n_cu ? pairs : n_cu;   // one workgroup per CU (128 KB of LDS)
+    // one row per wave: with two (every R fragment read feeding two MFMAs)
+    // the registers spilled and the kernel measured no faster
+    constexpr int RPW = 1;
+    const int64_t blocks = (a.M + 2 * RPW - 1) / (2 * RPW);
+    const int64_t grid = blocks < n_cu ? blocks : n_cu;   // one workgroup per CU (128 KB of LDS)
     if (a.smooth)
-        hipLaunchKernelGGL((rq_g256_kernel<DT, true, QMAX>), dim3((unsigned)grid), dim3(512), 0, st, (const uint16_t*)a.x,
-                           a.M, a.K, a.sm, a.rot, (const uint16_t*)a.smooth, a.codes, a.scales, (uint16_t*)a.yout);
+        hipLaunchKernelGGL((rq_g256_kernel<DT, true, QMAX, RPW>), dim3((unsigned)grid), dim3(512), 0, st,
+                           (const uint16_t*)a.x, a.M, a.K, a.sm, a.rot, (const uint16_t*)a.smooth, a.codes, a.scales,
+                           (uint16_t*)a.yout);
     else
-        hipLaunchKernelGGL((rq_g256_kernel<DT, false, QMAX>), dim3((unsigned)grid), dim3(512), 0, st, (const uint16_t*)a.x,
-                           a.M, a.K, a.sm, a.rot, (const uint16_t*)a.smooth, a.codes, a.scales, (uint16_t*)a.yout);
+        hipLaunchKernelGGL((rq_g256_kernel<DT, false, QMAX, RPW>), dim3((unsigned)grid), dim3(512), 0, st,
+                           (const uint16_t*)a.x, a.M, a.K, a.sm, a.rot, (const uint16_t*)a.smooth, a.codes, a.scales,
+                           (uint16_t*)a.yout);
     return hipGetLastError();
 }
 
