@@ -840,7 +840,7 @@ def _profile_kernels():
          text(wk), rq_bytes(wk), None, src + "rotate_quant.hip"),
         ("void w4a4::w4a4_gemm_pp_kernel<1>", "gemm_pingpong_widek_m8192_k10240_n3840",
          text(wk), gemm_bytes(wk), 2.0 * wk.M * wk.N * wk.K, src + "gemm.hip"),
-        ("void w4a4::rq_g256_kernel<2, true, 7>", "rotate_quant_g256_lowrank_m4096_k16384",
+        ("void w4a4::rq_g256_kernel<2, true, 7, 1>", "rotate_quant_g256_lowrank_m4096_k16384",
          text(lr), rq_bytes(lr), None, src + "rotate_quant.hip"),
         ("void w4a4::w4a4_gemm_kernel<2, false, true, false, false>", "gemm_tile128_lowrank_m4096_k16384_n6144",
          text(lr), gemm_bytes(lr), 2.0 * lr.M * lr.N * lr.K, src + "gemm.hip"),
