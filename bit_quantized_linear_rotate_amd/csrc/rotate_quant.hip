@@ -1542,7 +1542,7 @@ __global__ __launch_bounds__(512) void rq_g256_kernel(
                     float yy[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) yy[r] = h_to_f32<DT>((uint16_t)(yp[i][ct][r >> 1] >> (16 * (r & 1))));
-                    const uint32_t pk = fin ? quant4_bracket(yy, p) : quant4_exact<7>(yy, p.s);
+                    const uint32_t pk = !fin ? quant4_exact<7>(yy, p.s) : p.one ? quant4_one(yy, p) : quant4_bracket(yy, p);
                     __builtin_amdgcn_raw_buffer_store_b32(pk, rc, coff + ct * 16, 0, 0);
                     if (yout)
                         __builtin_amdgcn_raw_buffer_store_b64((v2u32){yp[i][ct][0], yp[i][ct][1]}, ry,

@@ -37,7 +37,9 @@ __device__ __forceinline__ const RowScaleEntry& row_scale_entry(uint32_t idx)
 struct RowQuant {
     float s;       // the row's scale
     float rh, rl;  // rinv * (1 + 2^-21), rinv * (1 - 2^-21)
+    float r1;      // the bracketing multiplier that rounds the k = 3 tie the quantizer's way
     uint32_t tie;  // tie mask, bit k and its mirror bit 32 - k (see tie_select)
+    bool one;      // 7 does not divide a's significand: r1 alone gives every code
 };
 
 // Parameters of one row from its 16-bit absmax pattern a16, computed by one
@@ -55,7 +57,9 @@ __device__ __forceinline__ RowQuant row_quant_thread(uint32_t a16)
         p.s = row_scale_shift(e.s, E);
         p.rh = row_scale_shift(e.rh, -E);
         p.rl = row_scale_shift(e.rl, -E);
+        p.r1 = row_scale_shift(e.r1, -E);
         p.tie = e.tie;
+        p.one = e.one != 0u;
         return p;
     }
     const float a = h_to_f32<DT>((uint16_t)a16);
@@ -79,6 +83,12 @@ __device__ __forceinline__ RowQuant row_quant_thread(uint32_t a16)
         }
     }
     p.tie = b | (__builtin_bitreverse32(b) << 1);
+    p.r1 = (b & 8u) ? p.rh : p.rl;
+    // a's integer significand: when 7 does not divide it, the only tie a
+    // 16-bit element can make is y = a / 2 (k = 3)
+    const uint32_t sig = DT == BF16 ? ((a16 >> 7) & 0xffu ? (a16 & 0x7fu) | 0x80u : a16 & 0x7fu)
+                                    : ((a16 >> 10) & 0x1fu ? (a16 & 0x3ffu) | 0x400u : a16 & 0x3ffu);
+    p.one = s != 0x1p-126f && sig % 7u != 0u;
     return p;
 }
 
@@ -98,6 +108,16 @@ __device__ __forceinline__ uint32_t pack_code_bytes(uint32_t c0, uint32_t c1, ui
     const uint32_t lo = __builtin_amdgcn_perm(c1, c0, 0x0c0c0400u);
     const uint32_t hi = __builtin_amdgcn_perm(c3, c2, 0x0c0c0400u);
     return lo | (hi << 16);
+}
+
+// codes of four finite-scale values of a row whose tie can only be k = 3
+// (p.one): one fma each
+__device__ __forceinline__ uint32_t quant4_one(const float (&y)[4], const RowQuant& p)
+{
+    uint32_t c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = __float_as_uint(__builtin_fmaf(y[i], p.r1, kBracketMagic));
+    return pack_code_bytes(c[0], c[1], c[2], c[3]);
 }
 
 // codes of four finite-scale values of one row

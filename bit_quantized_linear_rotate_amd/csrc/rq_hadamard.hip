@@ -59,6 +59,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "row_quant.hpp"
 
 namespace w4a4 {
 namespace {
@@ -215,7 +216,8 @@ __global__ __launch_bounds__(1024) void rq_hadamard_kernel(
     auto process = [&](int64_t row, const v8s (&xin)[P]) {
         if (row >= M) return;
         uint32_t yp[P][4];                         // packed T values: [h * 2 + r / 2]
-        uint32_t m16 = 0u;                         // max sign-cleared 16-bit pattern
+        typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+        v2u16 m2 = {0, 0};                         // max sign-cleared 16-bit patterns, packed
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             const int p = chunk_of(i);
@@ -262,23 +264,36 @@ __global__ __launch_bounds__(1024) void rq_hadamard_kernel(
                     if constexpr (LA >= 2) v = __builtin_fmaf(bs2, v, partner<2>(v));
                     if constexpr (LA >= 3) v = __builtin_fmaf(bs4, v, partner<4>(v));
                     hv[r] = f32_to_h<DT>(v);
-                    m16 = max(m16, (uint32_t)(hv[r] & 0x7fffu));
                 }
                 yp[i][2 * h] = ((uint32_t)hv[0] | ((uint32_t)hv[1] << 16)) ^ omask[2 * h];
                 yp[i][2 * h + 1] = ((uint32_t)hv[2] | ((uint32_t)hv[3] << 16)) ^ omask[2 * h + 1];
+                m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(v2u16, yp[i][2 * h] & 0x7fff7fffu));
+                m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(v2u16, yp[i][2 * h + 1] & 0x7fff7fffu));
             }
         }
         // lanes past K hold zeros (zero inputs, zero outputs): they do not
         // raise the max
-        const uint32_t wm = wave_max_u32(m16);
+        const uint32_t wm = wave_max_u32(max((uint32_t)m2[0], (uint32_t)m2[1]));
         if (lane == 0) wmax[par][wave] = wm;
         __syncthreads();
         uint32_t mm = wmax[par][0];
         for (int w = 1; w < nw; ++w) mm = max(mm, wmax[par][w]);
         par ^= 1;
-        const float amax = h_to_f32<DT>((uint16_t)mm);
-        float sv = amax / (float)QMAX;
-        if (sv < 0x1p-126f) sv = 0x1p-126f;        // NaN stays NaN
+        // INT4 codes: the row's quantizer from the significand table (or
+        // divisions outside its range), codes from one fma per value (or the
+        // two bracketing fmas and the tie mask when 7 divides the absmax's
+        // significand); the INT8 mode: product, residual test, exact division
+        // near half-integers
+        RowQuant rq;
+        float sv;
+        if constexpr (QMAX == 7) {
+            rq = row_quant_thread<DT>(mm);
+            sv = rq.s;
+        } else {
+            const float amax = h_to_f32<DT>((uint16_t)mm);
+            sv = amax / (float)QMAX;
+            if (sv < 0x1p-126f) sv = 0x1p-126f;        // NaN stays NaN
+        }
         // lane 0 of wave 0 writes the scale (the other lanes' offsets are
         // out of range and dropped)
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), rsc,
@@ -301,6 +316,8 @@ __global__ __launch_bounds__(1024) void rq_hadamard_kernel(
                 uint32_t pk;
                 if (!fin) {
                     pk = codes_exact4<QMAX>(yy, sv);
+                } else if constexpr (QMAX == 7) {
+                    pk = rq.one ? quant4_one(yy, rq) : quant4_bracket(yy, rq);
                 } else {
                     float t[4];
                     bool nr = false;
