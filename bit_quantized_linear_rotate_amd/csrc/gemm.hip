@@ -1086,10 +1086,15 @@ __global__ __launch_bounds__(512) void w4a4_gemm_pp_kernel(GemmArgs a, int tiles
     const int w_vo = (int)((lw * 64 + (lane >> 2)) * wrow);
     const int w_col16 = (int)(16 * wrow);
     // part: 1 the codes, 2 the weights, 3 both
-    auto issue = [&](int slot, const __amdgpu_buffer_rsrc_t& ra, const __amdgpu_buffer_rsrc_t& rw, int st, int part) {
+    auto issue = [&](int slot, const __amdgpu_buffer_rsrc_t& ra, const __amdgpu_buffer_rsrc_t& rw, int st, int part,
+                     bool rev) {
         int8_t* as = smem + slot * SLOT;
         int8_t* ws = as + ASTAGE;
-        const int ka = st * BK, kw = st * (BK / 2);
+        // tiles of odd rounds walk K backward: their first steps read the
+        // code slices the previous round read last, still in L2 (the integer
+        // sum does not depend on the order)
+        const int kst = rev ? nsteps - 1 - st : st;
+        const int ka = kst * BK, kw = kst * (BK / 2);
         if (part & 1)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -1245,8 +1250,8 @@ __global__ __launch_bounds__(512) void w4a4_gemm_pp_kernel(GemmArgs a, int tiles
     R3Tile cur_t = r3_tile<false>(a, t, ntiles, tiles_n);
     R3Tile nxt_t = r3_tile<false>(a, t + G, ntiles, tiles_n);
     if (grp_a) {
-        issue(0, cur_t.ra, cur_t.rw, 0, 3);
-        issue(1, cur_t.ra, cur_t.rw, 1, 3);
+        issue(0, cur_t.ra, cur_t.rw, 0, 3, (t / G) & 1);
+        issue(1, cur_t.ra, cur_t.rw, 1, 3, (t / G) & 1);
         // stand-ins for a previous tile's output stores, so that the wait of
         // every tile's first compute phase counts the same operations
         const __amdgpu_buffer_rsrc_t none = make_rsrc(a.out, 0);
@@ -1272,7 +1277,7 @@ __global__ __launch_bounds__(512) void w4a4_gemm_pp_kernel(GemmArgs a, int tiles
                 const bool same = s + 2 < nsteps;
                 if (!grp_a && s == 0) scale_issue(par, cur_t.m0, cur_t.n0);
                 issue(nslot, same ? cur_t.ra : nxt_t.ra, same ? cur_t.rw : nxt_t.rw, same ? s + 2 : s + 2 - nsteps,
-                      grp_a ? 1 : 2);
+                      grp_a ? 1 : 2, ((same ? t : t + G) / G) & 1);
             }
             if (!grp_a) {
                 // group B: its weights of stage s+1 landed (the scales of the
