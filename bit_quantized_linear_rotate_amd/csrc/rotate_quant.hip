@@ -840,14 +840,15 @@ __global__ __launch_bounds__(512) void rq_colmajor_kernel(
         // pass 2: quantize four codes of one row at a time into this step's
         // code tile (the storers write out the previous step's tile
         // meanwhile): the two bracketing roundings and the row's tie mask.
-        // A non-finite scale sends the wave to the exact division.
+        // A non-finite scale, or a row outside the scale table's range, sends
+        // the wave to the exact division.
         int8_t* ct = ctile[s & 1];
         float yv[MPW][JPW][4];
         bool near = false;
 #pragma unroll
         for (int mi = 0; mi < MPW; ++mi) {
             const int row = (mt0 + mi) * 16 + n;
-            near |= !(fabsf(rq[mi].s) < 3.0e38f);
+            near |= !(fabsf(rq[mi].s) < 3.0e38f) || rq[mi].exact;
 #pragma unroll
             for (int jj = 0; jj < JPW; ++jj) {
                 uint16_t yb[4];
@@ -1542,7 +1543,8 @@ __global__ __launch_bounds__(512) void rq_g256_kernel(
                     float yy[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) yy[r] = h_to_f32<DT>((uint16_t)(yp[i][ct][r >> 1] >> (16 * (r & 1))));
-                    const uint32_t pk = !fin ? quant4_exact<7>(yy, p.s) : p.one ? quant4_one(yy, p) : quant4_bracket(yy, p);
+                    const uint32_t pk = (!fin || p.exact) ? quant4_exact<7>(yy, p.s)
+                                        : p.one ? quant4_one(yy, p) : quant4_bracket(yy, p);
                     __builtin_amdgcn_raw_buffer_store_b32(pk, rc, coff + ct * 16, 0, 0);
                     if (yout)
                         __builtin_amdgcn_raw_buffer_store_b64((v2u32){yp[i][ct][0], yp[i][ct][1]}, ry,

@@ -40,12 +40,14 @@ struct RowQuant {
     float r1;      // the bracketing multiplier that rounds the k = 3 tie the quantizer's way
     uint32_t tie;  // tie mask, bit k and its mirror bit 32 - k (see tie_select)
     bool one;      // 7 does not divide a's significand: r1 alone gives every code
+    bool exact;    // outside the table's range: every code by IEEE division
 };
 
 // Parameters of one row from its 16-bit absmax pattern a16, computed by one
-// thread: the significand table shifted by a's exponent, or IEEE divisions
-// for the patterns the table does not cover (zero, tiny, Inf, NaN; the tie
-// mask is then evaluated directly, as in the table's construction).
+// thread: the significand table shifted by a's exponent.  For the patterns
+// the table does not cover (zero, a < 2^-119, Inf, NaN) only the scale is
+// computed (one IEEE division) and `exact` sends the row's codes to the IEEE
+// division of every element, the quantizer's own formula.
 template <int DT>
 __device__ __forceinline__ RowQuant row_quant_thread(uint32_t a16)
 {
@@ -60,35 +62,17 @@ __device__ __forceinline__ RowQuant row_quant_thread(uint32_t a16)
         p.r1 = row_scale_shift(e.r1, -E);
         p.tie = e.tie;
         p.one = e.one != 0u;
+        p.exact = false;
         return p;
     }
     const float a = h_to_f32<DT>((uint16_t)a16);
     float s = a / 7.0f;
     if (s < 0x1p-126f) s = 0x1p-126f;  // NaN compares false and stays NaN
     p.s = s;
-    const float rinv = 1.0f / s;
-    p.rh = rinv * (1.0f + 0x1p-21f);
-    p.rl = rinv * (1.0f - 0x1p-21f);
-    uint32_t b = 0;
-    if (s == 0x1p-126f) {
-        b = 0x2au;  // y / s = y * 2^126 exactly: a tie rounds to even
-    } else if (fabsf(s) < 3.0e38f) {
-        const bool big = a > 0x1p64f;
-        const float ah = big ? a * 0x1p-64f : a;
-        for (int k = 0; k < 7; ++k) {
-            const float h = (float)k + 0.5f;
-            float yh = (h * ah) / 7.0f;
-            if (big) yh *= 0x1p64f;
-            if (rintf(yh / s) > h) b |= 1u << k;
-        }
-    }
-    p.tie = b | (__builtin_bitreverse32(b) << 1);
-    p.r1 = (b & 8u) ? p.rh : p.rl;
-    // a's integer significand: when 7 does not divide it, the only tie a
-    // 16-bit element can make is y = a / 2 (k = 3)
-    const uint32_t sig = DT == BF16 ? ((a16 >> 7) & 0xffu ? (a16 & 0x7fu) | 0x80u : a16 & 0x7fu)
-                                    : ((a16 >> 10) & 0x1fu ? (a16 & 0x3ffu) | 0x400u : a16 & 0x3ffu);
-    p.one = s != 0x1p-126f && sig % 7u != 0u;
+    p.rh = p.rl = p.r1 = 0.0f;
+    p.tie = 0u;
+    p.one = false;
+    p.exact = true;
     return p;
 }
 

@@ -317,7 +317,7 @@ __global__ __launch_bounds__(1024) void rq_hadamard_kernel(
                 if (!fin) {
                     pk = codes_exact4<QMAX>(yy, sv);
                 } else if constexpr (QMAX == 7) {
-                    pk = rq.one ? quant4_one(yy, rq) : quant4_bracket(yy, rq);
+                    pk = rq.exact ? codes_exact4<7>(yy, sv) : rq.one ? quant4_one(yy, rq) : quant4_bracket(yy, rq);
                 } else {
                     float t[4];
                     bool nr = false;

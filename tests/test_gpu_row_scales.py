@@ -1,9 +1,12 @@
-"""Every row-absmax significand through the prefill row kernel.
+"""Every row-absmax significand through the rotate-quant kernels that take
+their row scales from the significand table.
 
-The row kernel takes a row's scale s = max(a / qmax, 2^-126), its reciprocal,
-the bracketing multipliers and the outcomes of exact ties from a table indexed
-by the significand of the 16-bit absmax a, shifted by a's exponent; rows the
-table does not cover (zero, a < 2^-119, Inf, NaN) use divisions.  The per-row
+The prefill row kernel (and, for INT4 codes, the g = 256 and column-major
+kernels, one thread per row) takes a row's scale s = max(a / qmax, 2^-126),
+its reciprocal, the bracketing multipliers and the outcomes of exact ties from
+a table indexed by the significand of the 16-bit absmax a, shifted by a's
+exponent; rows the table does not cover (zero, a < 2^-119, Inf, NaN) use
+divisions.  The per-row
 absmax scale and the round-half-even codes follow "[Feat][Ascend] Consolidate
 INT8, RotateQuant, RoPE and ConvRot W4A4 backends", section "W4A4 correctness
 and performance scope" (qmax = 7) and "[Feat][Ascend] Add fused RotateQuant
@@ -105,3 +108,43 @@ def test_row_kernel_every_significand(dt, qmax):
     ties = int((np.abs(workloads.storage_to_f32(x, dt).astype(np.float64) * qmax /
                        np.abs(workloads.storage_to_f32(x, dt)).max(axis=1, keepdims=True)) % 1 == 0.5).sum())
     print(f"{dt} qmax={qmax}: {M} rows, {1 << FB[dt]} significands, {ties} tie elements, codes and scales bit-exact")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("qmax", [7, 127])
+def test_g256_kernel_every_significand(dt, qmax):
+    # contiguous rows, g = 256: the low-rank layer's kernel, whose INT4 codes
+    # take the same table through one thread per row
+    need_gpu()
+    M, K, g = 2048, 2048, 256
+    x = rows_every_significand(dt, M, K, qmax, seed=29 + qmax)
+    xd = dev(x, dt)
+    rot = torch.eye(g, dtype=torch.float32, device="cuda")
+    if qmax == 7:
+        assert w4.w4a4_rotate_quant_plan(xd, rot, g) == "g256"
+        c, s = w4.w4a4_rotate_quant_rowwise(xd, rot, g)
+    else:
+        assert w4.w8a8_rotate_quant_plan(xd, rot, g) == "g256"
+        c, s = w4.w8a8_rotate_quant_rowwise(xd, rot, g)
+    c, s = host(c), host(s)
+    oc, os_ = oracle.quantize(x, dt, qmax=qmax)
+    bad = np.flatnonzero((c != oc).any(axis=1) | (bits(s) != bits(os_)))
+    assert bad.size == 0, f"{bad.size} rows differ, first row {bad[0]}: scale {s[bad[0]]!r} vs {os_[bad[0]]!r}"
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_colmajor_kernel_every_significand(dt):
+    # a transposed view, g = 256: the wide-K kernel, whose second pass takes
+    # every code from the row's table entry (one thread per row)
+    need_gpu()
+    M, K, g = 2048, 2048, 256
+    x = rows_every_significand(dt, M, K, 7, seed=31)
+    xt = np.ascontiguousarray(x.T)
+    xd = dev(xt, dt).t()
+    rot = torch.eye(g, dtype=torch.float32, device="cuda")
+    assert w4.w4a4_rotate_quant_plan(xd, rot, g) == "colmajor"
+    c, s = w4.w4a4_rotate_quant_rowwise(xd, rot, g)
+    c, s = host(c), host(s)
+    oc, os_ = oracle.quantize(x, dt)
+    bad = np.flatnonzero((c != oc).any(axis=1) | (bits(s) != bits(os_)))
+    assert bad.size == 0, f"{bad.size} rows differ, first row {bad[0]}: scale {s[bad[0]]!r} vs {os_[bad[0]]!r}"
