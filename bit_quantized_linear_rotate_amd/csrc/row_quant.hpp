@@ -45,9 +45,11 @@ struct RowQuant {
 
 // Parameters of one row from its 16-bit absmax pattern a16, computed by one
 // thread: the significand table shifted by a's exponent.  For the patterns
-// the table does not cover (zero, a < 2^-119, Inf, NaN) only the scale is
-// computed (one IEEE division) and `exact` sends the row's codes to the IEEE
-// division of every element, the quantizer's own formula.
+// the table does not cover (zero, a < 2^-119, Inf, NaN) the scale is one IEEE
+// division; a row whose scale is the smallest one (2^-126: zero and tiny rows)
+// keeps the bracketed codes, exact at that scale, and every other such row
+// (Inf, NaN, absmax in [7 * 2^-126, 2^-119)) sets `exact`, which sends its
+// codes to the IEEE division of every element, the quantizer's own formula.
 template <int DT>
 __device__ __forceinline__ RowQuant row_quant_thread(uint32_t a16)
 {
@@ -69,10 +71,21 @@ __device__ __forceinline__ RowQuant row_quant_thread(uint32_t a16)
     float s = a / 7.0f;
     if (s < 0x1p-126f) s = 0x1p-126f;  // NaN compares false and stays NaN
     p.s = s;
-    p.rh = p.rl = p.r1 = 0.0f;
-    p.tie = 0u;
     p.one = false;
-    p.exact = true;
+    if (s == 0x1p-126f) {
+        // the smallest scale (zero and tiny rows): y / s = y * 2^126 exactly,
+        // so the bracketing multipliers are exact scalings and a tie rounds
+        // to even (k odd rounds up)
+        p.rh = 0x1p126f * (1.0f + 0x1p-21f);
+        p.rl = 0x1p126f * (1.0f - 0x1p-21f);
+        p.r1 = p.rh;
+        p.tie = 0x2au | (__builtin_bitreverse32(0x2au) << 1);
+        p.exact = false;
+    } else {
+        p.rh = p.rl = p.r1 = 0.0f;
+        p.tie = 0u;
+        p.exact = true;
+    }
     return p;
 }
 
