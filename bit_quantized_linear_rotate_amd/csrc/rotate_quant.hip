@@ -123,20 +123,6 @@ __device__ __forceinline__ uint32_t pack4_magic(float t0, float t1, float t2, fl
     return lo | (hi << 16);
 }
 
-__device__ __forceinline__ uint32_t quant4_finite(const float (&y)[4], float rinv, bool& near)
-{
-    float t[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float qv = y[i] * rinv;
-        const float c = __builtin_amdgcn_fmed3f(qv, -7.0f, 7.0f);
-        t[i] = c + kRoundMagic;
-        const float r = t[i] - kRoundMagic;
-        near |= fabsf(qv - r) > 0.5f - 0x1p-17f;
-    }
-    return pack4_magic(t[0], t[1], t[2], t[3]);
-}
-
 // fp32 pattern of T(|v|) for the sign-cleared fp32 pattern of v
 template <int DT>
 __device__ __forceinline__ uint32_t round_bits(uint32_t vbits)
