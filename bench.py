@@ -409,7 +409,8 @@ def _bf6_leg(w, sets, outs, qbufs, steps, warmup, torch, np, w4, ops):
 def _hadamard_leg(w, sets, outs, wss, qbufs, steps, warmup, torch, np, w4, b, stream, rq_bytes, qmax):
     """The same workload with the rotation given by its structure (the
     normalized Hadamard the workload uses): rotate-quant alone through
-    w4a4_rotate_quant_hadamard (fast Walsh-Hadamard kernel), and for INT4
+    w4a4_rotate_quant_hadamard (fast Walsh-Hadamard kernel; the row-streaming
+    kernel at g = 64 on many contiguous rows), and for INT4
     codes the whole layer through w4a4_linear_hadamard."""
     lib = w4.lib()
     M, K, g = w.M, w.K, w.g
@@ -429,7 +430,10 @@ def _hadamard_leg(w, sets, outs, wss, qbufs, steps, warmup, torch, np, w4, b, st
     for i in range(warmup):
         rq(i)
     t = _time_each(rq, nk, torch, np)
-    out = {"kernel": "rq_hadamard_kernel (fast Walsh-Hadamard, qmax %d)" % qmax, **t,
+    plan = w4.w4a4_rotate_quant_hadamard_plan(sets[0]["x"], g, qmax, smooth=sets[0].get("smooth"))
+    name = {"row": "rq_row_kernel (R built from the signs, qmax %d)",
+            "hadamard": "rq_hadamard_kernel (fast Walsh-Hadamard, qmax %d)"}[plan] % qmax
+    out = {"kernel": name, **t,
            "GB_s": rq_bytes / (t["ms_median"] * 1e-3) / 1e9,
            "frac_hbm": rq_bytes / (t["ms_median"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
     if qmax == 7:

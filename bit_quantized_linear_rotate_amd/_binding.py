@@ -635,8 +635,10 @@ def w4a4_rotate_quant_hadamard(x: torch.Tensor, h: Hadamard, qmax: int = 7,
 def w4a4_rotate_quant_hadamard_plan(x: torch.Tensor, g: int, qmax: int = 7,
                                     smooth: Optional[torch.Tensor] = None,
                                     return_rotated: bool = False) -> str:
-    """"hadamard" when w4a4_rotate_quant_hadamard serves these arguments;
-    raises W4A4Error (unsupported) otherwise.  Host-only."""
+    """"hadamard" (fast Walsh-Hadamard kernel) or "row" (the one-wave-per-row
+    kernel with R built from the signs, g = 64 on many contiguous rows) for
+    the kernel w4a4_rotate_quant_hadamard takes; raises W4A4Error
+    (unsupported) when none does.  Host-only."""
     x2 = _as_2d(x)
     M, K = x2.shape
     k = ctypes.c_int(-1)
@@ -644,7 +646,7 @@ def w4a4_rotate_quant_hadamard_plan(x: torch.Tensor, g: int, qmax: int = 7,
         _ptr(x2), _dt(x2), M, K, x2.stride(0), x2.stride(1), g, _ptr(smooth), qmax, _ALIGNED,
         _ALIGNED if return_rotated else None, ctypes.byref(k))
     _check(rc, "w4a4_rotate_quant_hadamard_plan")
-    return {7: "hadamard"}.get(k.value, "none")
+    return {6: "row", 7: "hadamard"}.get(k.value, "none")
 
 
 def w4a4_linear_hadamard(x: torch.Tensor, h: Hadamard, w_packed: torch.Tensor,

@@ -1944,8 +1944,10 @@ static bool colmajor_ok(const RQArgs& a)
 // when none does (a row too long for the generic kernel's LDS buffer).
 int rotate_quant_path(const RQArgs& a)
 {
-    // structured (Hadamard) rotation: the fast Walsh-Hadamard kernel only
-    if (a.hadamard) return hadamard_kernel_ok(a) ? 7 : -1;
+    // structured (Hadamard) rotation: at g = 64 on many contiguous rows the
+    // row-streaming kernel (it builds R's fragments from the signs; faster
+    // than the transform at this width), else the fast Walsh-Hadamard kernel
+    if (a.hadamard) return row_kernel_ok(a) ? 6 : hadamard_kernel_ok(a) ? 7 : -1;
     // INT8 mode: the row-streaming and g = 256 kernels, else the generic one
     if (a.qmax == 127) {
         if (g256_ok(a)) return 5;

@@ -146,7 +146,8 @@ template <int DT, bool SMOOTH, bool YOUT, int TW, int PF, int QMAX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void rq_row_kernel(
     const uint16_t* __restrict__ x, int M, int64_t K, int64_t sm,
     const float* __restrict__ rot, const uint16_t* __restrict__ smooth,
-    int8_t* __restrict__ codes, float* __restrict__ scales, uint16_t* __restrict__ yout)
+    int8_t* __restrict__ codes, float* __restrict__ scales, uint16_t* __restrict__ yout,
+    int had, const int8_t* __restrict__ sign_in, const int8_t* __restrict__ sign_out)
 {
     constexpr int GP = 64, CT = 4, NKS = 2, LPL = 16;
     constexpr int kNT = 2;  // cache policy of the output stores: non-temporal
@@ -200,7 +201,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
         const int f = e >> 6, jj = e & 15, qq = (e >> 4) & 3;
         v8s v;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (short)f32_to_h<DT>(rot[(qq * LPL + (f & 1) * 8 + i) * GP + (f >> 1) * 16 + jj]);
+        for (int i = 0; i < 8; ++i) {
+            const int kk = qq * LPL + (f & 1) * 8 + i, cc = (f >> 1) * 16 + jj;
+            float rv;
+            if (had) {
+                // R = diag(sign_in) H_64 diag(sign_out) / 8, H_64 the Sylvester
+                // matrix: entry (k, c) is (-1)^popcount(k & c) / 8, exact in T
+                const int neg = (__builtin_popcount(kk & cc) ^ (sign_in && sign_in[kk] < 0) ^
+                                 (sign_out && sign_out[cc] < 0)) & 1;
+                rv = neg ? -0.125f : 0.125f;
+            } else {
+                rv = rot[kk * GP + cc];
+            }
+            v[i] = (short)f32_to_h<DT>(rv);
+        }
         rlds[f][e & 63] = v;
     }
     __syncthreads();
@@ -429,11 +443,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void r
 
 // Contiguous 16-bit rows, g = 64, 32 < K/64 <= 64 group-rows (four tiles) or
 // 16 < K/64 <= 32 (two tiles), 16-byte aligned rows, codes and smoothing
-// factors, 8-byte aligned rotated export, enough rows to fill the GPU.
+// factors, 8-byte aligned rotated export, enough rows to fill the GPU.  A
+// dense R, or the structured one (signed Sylvester-Hadamard), whose
+// fragments the kernel builds itself.
 bool row_kernel_ok(const RQArgs& a)
 {
     const bool sixteen = a.dtype == F16 || a.dtype == BF16;
-    if (!sixteen || !a.rot || a.g != 64 || a.sk != 1 || a.M < 2048 || a.M >= (int64_t(1) << 30)) return false;
+    if (!sixteen || !(a.rot || a.hadamard) || a.g != 64 || a.sk != 1 || a.M < 2048 || a.M >= (int64_t(1) << 30))
+        return false;
     if ((a.K % 64) != 0) return false;
     const int64_t gpr = a.K / 64;
     if (gpr <= 16 || gpr > 64) return false;
@@ -471,7 +488,8 @@ static hipError_t launch_row_t(const RQArgs& a, hipStream_t st)
     const int64_t need = (a.M + 3) / 4;   // four waves (rows) per workgroup
     if (grid > need) grid = need;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.x, (int)a.M, a.K,
-                       a.sm, a.rot, (const uint16_t*)a.smooth, a.codes, a.scales, (uint16_t*)a.yout);
+                       a.sm, a.rot, (const uint16_t*)a.smooth, a.codes, a.scales, (uint16_t*)a.yout,
+                       a.hadamard ? 1 : 0, a.sign_in, a.sign_out);
     return hipGetLastError();
 }
 

@@ -199,7 +199,9 @@ int w8a8_gemm_plan(const int8_t* codes, int64_t M, int64_t K, const int8_t* w, i
  * rotations; "[Feat][Ascend] Consolidate INT8, RotateQuant, RoPE and ConvRot
  * W4A4 backends", "W4A4 correctness and performance scope"); the result equals
  * the dense call's with this R up to the order of the fp32 sum of the same
- * exact products.
+ * exact products.  At g = 64 on shapes the dense one-wave-per-row kernel takes
+ * (16 < K/64 <= 64, M >= 2048) that kernel runs, with R's entries (+-1/8)
+ * built from the signs: then the result is the dense call's, bit for bit.
  *   g:        16, 32, 64, 128 or 256; K a multiple of g, K <= 16384.
  *   sign_in, sign_out: device int8 arrays of g entries, 8-byte aligned (a
  *             negative entry is -1, any other +1), or NULL for all +1.  Read
@@ -215,8 +217,9 @@ int w4a4_rotate_quant_hadamard(const void* x, int x_dtype, int64_t M, int64_t K,
                                int64_t stride_k, int32_t g, const int8_t* sign_in,
                                const int8_t* sign_out, const void* smooth, int32_t qmax,
                                int8_t* codes, float* scales, void* rotated_out, void* stream);
-/* host-only: 7 when w4a4_rotate_quant_hadamard takes its kernel for these
- * arguments, W4A4_UNSUPPORTED otherwise */
+/* host-only: which kernel w4a4_rotate_quant_hadamard takes for these
+ * arguments (7 the fast Walsh-Hadamard transform, 6 the one-wave-per-row
+ * kernel at g = 64), W4A4_UNSUPPORTED when none does */
 int w4a4_rotate_quant_hadamard_plan(const void* x, int x_dtype, int64_t M, int64_t K,
                                     int64_t stride_m, int64_t stride_k, int32_t g,
                                     const void* smooth, int32_t qmax, const int8_t* codes,
@@ -372,7 +375,8 @@ int w4a4_int32_guard(int64_t K, int64_t* k_chunk);
  *   3 one wave per row block (many contiguous rows, g <= 64)
  *   4 column-major (unit row stride, i.e. a transposed view; M % 8 == 0)
  *   5 g = 256 on contiguous rows
- *   6 one wave per contiguous row, g = 64, 16 < K/64 <= 64 (many rows)
+ *   6 one wave per contiguous row, g = 64, 16 < K/64 <= 64 (many rows; also
+ *     w4a4_rotate_quant_hadamard_plan at g = 64)
  *   7 fast Walsh-Hadamard transform (w4a4_rotate_quant_hadamard_plan only)
  * w4a4_gemm_plan, *kernel (has_lowrank: a low-rank term will be added):
  *   0 128 x 128 tiles          1 128 x 128 tiles over K chunks (int64 combine)

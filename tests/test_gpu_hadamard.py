@@ -1,5 +1,6 @@
-"""GPU parity of the structured-rotation path (fast Walsh-Hadamard transform)
-against the oracle with the same rotation written out as a dense R.
+"""GPU parity of the structured-rotation path (fast Walsh-Hadamard transform;
+at g = 64 on many contiguous rows, the row-streaming kernel with R built
+in-kernel) against the oracle with the same rotation written out as a dense R.
 
 The rotation is R = diag(sign_in) . H_g . diag(sign_out) / sqrt(g) (group
 sizes and asymmetric rotations of "[Feat][Ascend] Add fused RotateQuant
@@ -56,14 +57,14 @@ def _hadamard(g, si, so):
                        None if so is None else torch.from_numpy(so).cuda())
 
 
-def _rq_case(dt, x, g, si, so, qmax, smooth=None, x_dev=None):
+def _rq_case(dt, x, g, si, so, qmax, smooth=None, x_dev=None, plan="hadamard"):
     h = _hadamard(g, si, so)
     R = _dense(g, si, so)
     # the binding's dense form is the same matrix
     assert np.array_equal(h.dense().cpu().numpy(), R.astype(np.float32))
     xd = dev(x, dt) if x_dev is None else x_dev
     sm = dev(smooth, dt) if smooth is not None else None
-    assert w4.w4a4_rotate_quant_hadamard_plan(xd, g, qmax, smooth=sm, return_rotated=True) == "hadamard"
+    assert w4.w4a4_rotate_quant_hadamard_plan(xd, g, qmax, smooth=sm, return_rotated=True) == plan
     c, s, yg = w4.w4a4_rotate_quant_hadamard(xd, h, qmax, smooth=sm, return_rotated=True)
     c2, s2 = w4.w4a4_rotate_quant_hadamard(xd, h, qmax, smooth=sm)
     c, s, yg, c2, s2 = host(c), host(s), host(yg), host(c2), host(s2)
@@ -79,7 +80,7 @@ def _rq_case(dt, x, g, si, so, qmax, smooth=None, x_dev=None):
     same = np.array([scales_equal(s[i:i + 1], rs[i:i + 1]) for i in range(M)])
     dc = np.abs(c.astype(np.int32) - rc)
     assert dc.max(initial=0) <= 1
-    print(f"hadamard g={g} {dt} qmax={qmax} M={M} K={x.shape[1]} signs={si is not None}: "
+    print(f"{plan} g={g} {dt} qmax={qmax} M={M} K={x.shape[1]} signs={si is not None}: "
           f"{frac:.2e} rotated values differ ({beyond} beyond 1 ulp), {(~same).sum()} rows with "
           f"another scale, {(dc > 0).sum()} code flips")
     return c, s
@@ -125,6 +126,37 @@ def test_hadamard_smoothing_and_strided_rows(dt):
     si, so = _signs(g, 7)
     _rq_case(dt, x, g, si, so, 7, smooth=sm, x_dev=xd)
     _rq_case(dt, x, g, si, so, 127, smooth=sm, x_dev=xd)
+
+
+@pytest.mark.parametrize("dt,K", [("bf16", 4096), ("f16", 1152)])
+@pytest.mark.parametrize("qmax", [7, 127])
+@pytest.mark.parametrize("signs", [None, 11])
+def test_hadamard_g64_row_kernel(dt, K, qmax, signs):
+    # g = 64 on many contiguous rows: the row-streaming kernel, which builds
+    # the fragments of diag(sign_in) H_64 diag(sign_out) / 8 itself.  The
+    # oracle's checks, and bit-identity with the same kernel given that R as
+    # a dense matrix (the same fp32 products, summed in the same order)
+    need_gpu()
+    g, M = 64, 2048
+    x, where = build_matrix(dt, M, K, g, seed=65 + K + qmax)
+    si, so = _signs(g, signs)
+    sm = None
+    if signs is not None:
+        sm = workloads.f32_to_storage(np.random.default_rng(66).uniform(0.5, 2.0, size=K).astype(np.float32), dt)
+    c, s = _rq_case(dt, x, g, si, so, qmax, smooth=sm, plan="row")
+    xd = dev(x, dt)
+    smd = dev(sm, dt) if sm is not None else None
+    R = torch.from_numpy(_dense(g, si, so).astype(np.float32)).cuda()
+    c1, s1, y1 = w4.w4a4_rotate_quant_hadamard(xd, _hadamard(g, si, so), qmax, smooth=smd, return_rotated=True)
+    if qmax == 7:
+        assert w4.w4a4_rotate_quant_plan(xd, R, g, smooth=smd) == "row"
+        c2, s2, y2 = w4.w4a4_rotate_quant_rowwise(xd, R, g, smooth=smd, return_rotated=True)
+    else:
+        c2, s2, y2 = w4.w8a8_rotate_quant_rowwise(xd, R, g, smooth=smd, return_rotated=True)
+    assert torch.equal(c1, c2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert (c[where["zero"]] == 0).all() and s[where["zero"]] == np.float32(2.0 ** -126)
+    assert np.isnan(s[where["nan"]]) and (c[where["nan"]] == 0).all()
 
 
 def test_hadamard_unsupported_layouts_are_refused():
